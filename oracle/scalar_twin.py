@@ -1,0 +1,112 @@
+"""Scalar-loop twin of the oracle -- TEST INFRASTRUCTURE ONLY.
+
+A second, deliberately naive CPU implementation of the same layer used to pin
+the vectorised oracle on tiny shapes.  It shares no code with
+``moe_oracle.py``: fp16 is decoded with Python's ``struct`` half-precision
+codec, the Q4_K scale/min fields are cut from one Python integer holding the
+96-bit stream, and every product is an explicit loop over Python floats.
+Meant for hidden sizes of a few hundred and a handful of experts.
+"""
+
+from __future__ import annotations
+
+import math
+import struct
+
+
+def _f16(lo: int, hi: int) -> float:
+    return struct.unpack("<e", bytes([lo, hi]))[0]
+
+
+def weight_q8_0(buf, rows: int, cols: int, r: int, c: int) -> float:
+    nb = cols // 32
+    b = c // 32
+    so = 2 * (r * nb + b)
+    d = _f16(int(buf[so]), int(buf[so + 1]))
+    qo = -(-2 * rows * nb // 256) * 256
+    q = int(buf[qo + r * cols + c])
+    if q >= 128:
+        q -= 256
+    return d * q
+
+
+def weight_q4_k(buf, rows: int, cols: int, r: int, c: int) -> float:
+    ns = cols // 256
+    rec = r * ns + c // 256
+    within = c % 256
+    s, i = within // 32, within % 32
+    h = [int(v) for v in buf[16 * rec: 16 * rec + 16]]
+    d = _f16(h[0], h[1])
+    dmin = _f16(h[2], h[3])
+    stream = int.from_bytes(bytes(h[4:16]), "little")
+    sc = (stream >> (6 * s)) & 0x3F
+    mn = (stream >> (48 + 6 * s)) & 0x3F
+    qbyte = int(buf[16 * rows * ns + 128 * rec + 16 * s + i // 2])
+    q = (qbyte >> 4) if (i % 2) else (qbyte & 0xF)
+    return d * sc * q - dmin * mn
+
+
+def weight(dtype: str, buf, rows: int, cols: int, r: int, c: int) -> float:
+    return (weight_q8_0 if dtype == "q8_0" else weight_q4_k)(buf, rows, cols, r, c)
+
+
+def _matvec(dtype, buf, rows, cols, row0, nrows, v):
+    out = []
+    for r in range(row0, row0 + nrows):
+        acc = 0.0
+        for c in range(cols):
+            acc += weight(dtype, buf, rows, cols, r, c) * v[c]
+        out.append(acc)
+    return out
+
+
+def _ffn(dtype, g_buf, u_buf, d_buf, rows_gu, rows_d, g_row0, d_row0, F, H, x):
+    g = _matvec(dtype, g_buf, rows_gu, H, g_row0, F, x)
+    u = _matvec(dtype, u_buf, rows_gu, H, g_row0, F, x)
+    h = [gi / (1.0 + math.exp(-gi)) * ui for gi, ui in zip(g, u)]
+    return _matvec(dtype, d_buf, rows_d, F, d_row0, H, h)
+
+
+def moe_layer(x, router, gate, up, down, *, top_k, ffn, expert_type,
+              shared=None, shared_ffn=0, shared_type="q8_0"):
+    """Returns (y, ids, w) with y a list of lists of floats."""
+    E = len(router)
+    H = len(router[0])
+    F = ffn
+    ys, all_ids, all_w = [], [], []
+    for xt in x:
+        xt = [float(v) for v in xt]
+        logits = []
+        for e in range(E):
+            acc = 0.0
+            for h in range(H):
+                acc += float(router[e][h]) * xt[h]
+            logits.append(acc)
+        # selection sort on (-logit, index)
+        chosen = []
+        for _ in range(top_k):
+            best = None
+            for e in range(E):
+                if e in chosen:
+                    continue
+                if best is None or logits[e] > logits[best]:
+                    best = e
+            chosen.append(best)
+        mx = max(logits)
+        p = [math.exp(v - mx) for v in logits]
+        tot = sum(p)
+        p = [v / tot for v in p]
+        ssum = sum(p[e] for e in chosen)
+        w = [p[e] / ssum for e in chosen]
+        y = [0.0] * H
+        if shared is not None and shared_ffn > 0:
+            s = _ffn(shared_type, shared[0], shared[1], shared[2], shared_ffn, H,
+                     0, 0, shared_ffn, H, xt)
+            y = [a + b for a, b in zip(y, s)]
+        for j, e in enumerate(chosen):
+            o = _ffn(expert_type, gate, up, down, E * F, E * H, e * F, e * H, F, H, xt)
+            y = [a + w[j] * b for a, b in zip(y, o)]
+        ys.append(y)
+        all_ids.append(chosen)
+        all_w.append(w)
+    return ys, all_ids, all_w

@@ -1,0 +1,22 @@
+"""Seeded synthetic inputs for the routed-MoE verify layer.
+
+This package draws router weights, activations and block-quantised expert
+tensors from fixed seeds and packs them into the byte layouts that
+``include/moe_layer.h`` documents.  It holds none of the layer's arithmetic
+(no routing, no dequantisation, no matrix products); the CPU oracle and the
+HIP library both read the bytes it writes.
+"""
+
+from .layers import (  # noqa: F401
+    CONFIGS,
+    LayerConfig,
+    LayerInputs,
+    draw_layer,
+    draw_tokens,
+    q4_k_bytes,
+    q4_k_header_bytes,
+    q8_0_bytes,
+    q8_0_quant_offset,
+    quantize_q8_0,
+    tensor_bytes,
+)

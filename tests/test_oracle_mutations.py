@@ -1,0 +1,146 @@
+"""Planted mistakes in the oracle must be caught by its pins (CPU only).
+
+Each case patches one oracle function with a plausible slip (a wrong bias, a
+swapped nibble, a flipped sign, a wrong tie-break, a dropped term) and runs
+the pin tests of ``test_oracle_pins``; at least one pin must fail.
+"""
+
+import contextlib
+
+import numpy as np
+import pytest
+
+from oracle import moe_oracle as om
+import test_oracle_pins as P
+
+_orig = {name: getattr(om, name) for name in dir(om) if callable(getattr(om, name))}
+
+
+def _pins():
+    yield P.test_f16_decode_all_bit_patterns_match_numpy
+    for fx, dt in [("q8_0_planar.txt", "q8_0"), ("q4_k_planar.txt", "q4_k")]:
+        yield lambda fx=fx, dt=dt: P.test_dequant_matches_hand_derived_fixture(fx, dt)
+    yield P.test_dequant_fixture_twin_agrees
+    yield P.test_q8_0_requantise_roundtrip_is_byte_exact
+    for s in (0, 3, 7):
+        yield lambda s=s: P.test_q4_k_single_field_positions(s)
+    yield P.test_q4_k_multi_row_record_order
+    yield P.test_router_logits_unit_vectors_pick_columns
+    yield P.test_select_ties_go_to_lower_index
+    yield P.test_select_matches_brute_force_sort
+    yield P.test_routing_weights_sum_to_one_and_k1_is_one
+    yield P.test_k_equals_E_is_the_textbook_softmax
+    yield P.test_renormalised_weights_equal_softmax_over_selected
+    yield P.test_bucket_matches_brute_force
+    yield P.test_silu_is_g_times_logistic
+    for args in [("q8_0", 256, 128, 0, 8), ("q8_0", 256, 64, 96, 4)]:
+        yield lambda a=args: P.test_oracle_matches_scalar_twin(*a)
+    yield P.test_one_expert_top1_layer_is_dense_swiglu_ffn
+    for et in ("q8_0", "q4_k"):
+        yield lambda et=et: P.test_doubling_down_scales_doubles_routed_part_exactly(et)
+    yield P.test_rows_are_independent_of_batch
+
+
+# --- the planted mistakes -------------------------------------------------
+
+def _f16_bias(bits):
+    return _orig["f16_to_f64"](bits) * 2.0
+
+
+def _f16_no_subnormal(bits):
+    b = np.asarray(bits).astype(np.int64) & 0xFFFF
+    v = _orig["f16_to_f64"](bits)
+    return np.where(((b >> 10) & 31) == 0, 0.0, v)
+
+
+def _q4k_fields_swapped_nibbles(*a, **k):
+    d, dmin, sc, m, q = _orig["q4_k_fields"](*a, **k)
+    q2 = q.copy()
+    q2[:, :, 0::2], q2[:, :, 1::2] = q[:, :, 1::2], q[:, :, 0::2]
+    return d, dmin, sc, m, q2
+
+
+def _q4k_field_shifted(sbytes, bit):
+    return _orig["_q4_k_field"](sbytes, bit - 6 if bit >= 48 else bit)
+
+
+def _q4k_plus_min(buf, rows, cols, row_start=0, row_count=None):
+    r0, n = om._rows(rows, row_start, row_count)
+    d, dmin, sc, m, q = om.q4_k_fields(buf, rows, cols, r0, n)
+    w = d[:, None, None] * sc[:, :, None] * q + dmin[:, None, None] * m[:, :, None]
+    return w.reshape(n, cols)
+
+
+def _q8_offset_unpadded(rows, cols):
+    return 2 * rows * (cols // 32)
+
+
+def _select_high_tie(logits, k):
+    L = np.atleast_2d(np.asarray(logits, dtype=np.float64))
+    E = L.shape[1]
+    ids = np.empty((L.shape[0], k), dtype=np.int64)
+    for t in range(L.shape[0]):
+        ids[t] = np.lexsort((-np.arange(E), -L[t]))[:k]
+    return ids
+
+
+def _weights_unnormalised(logits, ids):
+    return np.take_along_axis(om.softmax(logits), np.asarray(ids), axis=1)
+
+
+def _sigmoid_only(g):
+    g = np.asarray(g, dtype=np.float64)
+    return 1.0 / (1.0 + np.exp(-g))
+
+
+def _bucket_unstable(ids, n_experts):
+    counts, offsets, slots, active = _orig["bucket"](ids, n_experts)
+    return counts, offsets, np.argsort(np.asarray(ids).reshape(-1)[::-1], kind="stable")[::-1].copy(), active
+
+
+def _ffn_no_up(Wg, Wu, Wd, xs):
+    xs = np.atleast_2d(np.asarray(xs, dtype=np.float64))
+    return om.silu(xs @ Wg.T) @ Wd.T
+
+
+MUTATIONS = {
+    "f16_scale": ("f16_to_f64", _f16_bias),
+    "f16_subnormal_flush": ("f16_to_f64", _f16_no_subnormal),
+    "q4k_nibble_order": ("q4_k_fields", _q4k_fields_swapped_nibbles),
+    "q4k_min_offset": ("_q4_k_field", _q4k_field_shifted),
+    "q4k_min_sign": ("dequant_q4_k", _q4k_plus_min),
+    "q8_plane_offset": ("q8_0_quant_offset", _q8_offset_unpadded),
+    "tie_to_higher": ("select_experts", _select_high_tie),
+    "no_renormalise": ("routing_weights", _weights_unnormalised),
+    "silu_is_sigmoid": ("silu", _sigmoid_only),
+    "bucket_order": ("bucket", _bucket_unstable),
+    "ffn_drops_up": ("swiglu_ffn", _ffn_no_up),
+}
+
+
+@contextlib.contextmanager
+def _patched(name, fn):
+    setattr(om, name, fn)
+    try:
+        yield
+    finally:
+        setattr(om, name, _orig[name])
+
+
+@pytest.mark.parametrize("case", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(case):
+    name, fn = MUTATIONS[case]
+    caught = []
+    with _patched(name, fn):
+        for pin in _pins():
+            try:
+                with np.errstate(all="ignore"):
+                    pin()
+            except (AssertionError, ValueError, IndexError):
+                caught.append(getattr(pin, "__name__", "pin"))
+    assert caught, f"no pin caught the planted mistake {case!r}"
+
+
+def test_unpatched_pins_pass():
+    for pin in _pins():
+        pin()
