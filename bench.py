@@ -1,0 +1,235 @@
+"""Benchmark: routed-MoE layer tokens/s and achieved HBM GB/s on one MI355X.
+
+A step is one moe_layer_forward call (router, top-k, bucketing, shared and
+routed gate/up + SwiGLU, shared and routed down, combine) on one batch of
+synthetic tokens already resident in HBM.  The default workload is the
+Step-3.5-Flash-shaped layer on the MTP verify batch: 4 tokens (the last
+accepted token and 3 drafts), hidden 4096, 288 routed experts, top-8, FFN
+1280, routed gate/up/down in Q4_K, a Q8_0 shared expert (FFN 1280), F32
+router.  Calls rotate over R independent layer instances so that no call
+finds its weights in the 256 MB Infinity Cache left by the previous one.
+
+Prints one JSON line.  `roofline` reports the dominant kernel (routed
+gate/up) against the 8 TB/s HBM peak, timed with HIP events recorded by
+the library on the launch stream; `cpu_baseline` times the CPU oracle on a
+bounded sample (one layer call) on the host.
+
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--instances 4]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+DEFAULT_WORKLOAD = "step35_verify_m4"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "routed_gateup_traffic.json")
+DOMINANT = "routed_gateup"
+
+
+def _bytes_per_row(dtype: str, cols: int) -> float:
+    return cols // 32 * 34 if dtype == "q8_0" else cols // 256 * 144
+
+
+def layer_bytes(cfg, distinct: int) -> dict:
+    """Algorithmic HBM bytes of one call: router, distinct experts, shared expert, x, y."""
+    H, F, Fs, M, k = cfg.hidden, cfg.ffn, cfg.shared_ffn, cfg.n_tokens, cfg.top_k
+    expert = 2 * F * _bytes_per_row(cfg.expert_type, H) + H * _bytes_per_row(cfg.expert_type, F)
+    shared = 0
+    if Fs:
+        shared = 2 * Fs * _bytes_per_row(cfg.shared_type, H) + H * _bytes_per_row(cfg.shared_type, Fs)
+    router = cfg.n_experts * H * 4
+    xy = 2 * M * H * 4
+    gateup = distinct * 2 * F * _bytes_per_row(cfg.expert_type, H) + M * H * 4 + M * k * F * 4
+    return dict(total=router + distinct * expert + shared + xy, gateup=gateup)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "speculative_verify_router_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(workload: str):
+    """HBM bytes per launch of the dominant kernel from committed counter runs,
+    or None if they were taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != source_hash() or t.get("workload") != workload:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, inp, x) -> dict:
+    """The oracle as it stands, one layer call of the workload, BLAS on one thread."""
+    from oracle import moe_oracle as om
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(1)
+    except Exception:  # pragma: no cover
+        limiter = None
+    kw = dict(top_k=cfg.top_k, ffn=cfg.ffn, expert_type=cfg.expert_type)
+    if cfg.shared_ffn:
+        kw.update(shared=(inp.shared_gate, inp.shared_up, inp.shared_down),
+                  shared_ffn=cfg.shared_ffn, shared_type=cfg.shared_type)
+    t0 = time.perf_counter()
+    om.moe_layer(x, inp.router, inp.gate, inp.up, inp.down, **kw)
+    dt = time.perf_counter() - t0
+    if limiter is not None:
+        limiter.unregister()
+    return {"value": cfg.n_tokens / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"one layer call of {cfg.name} ({cfg.n_tokens} tokens), float64 NumPy, "
+                      f"{dt:.1f} s"}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--instances", type=int, default=4, help="layer instances rotated over")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the layer is built and timed on a single MI355X; "
+              "runs on more than one GPU are not supported.", file=sys.stderr)
+        return 2
+
+    import torch
+    import speculative_verify_router_amd as svr
+    import synth
+
+    cfg = synth.CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    desc = svr.LayerDesc(cfg.hidden, cfg.n_experts, cfg.top_k, cfg.ffn, cfg.shared_ffn,
+                         cfg.expert_type, cfg.shared_type)
+    M, k = cfg.n_tokens, cfg.top_k
+    R = max(1, args.instances)
+
+    t_gen = time.perf_counter()
+    layers, xs, host0 = [], [], None
+    for i in range(R):
+        inp = synth.draw_layer(cfg, instance=i)
+        x, _ = synth.draw_tokens(cfg, instance=i)
+        up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+        w = svr.LayerWeights(up(inp.router), up(inp.gate), up(inp.up), up(inp.down))
+        if cfg.shared_ffn:
+            w.shared_gate, w.shared_up, w.shared_down = (up(inp.shared_gate), up(inp.shared_up),
+                                                         up(inp.shared_down))
+        layers.append(w)
+        xs.append(up(x))
+        if i == 0:
+            host0 = (inp, x)
+        print(f"# instance {i} resident ({time.perf_counter() - t_gen:.1f} s)", file=sys.stderr,
+              flush=True)
+    ws = svr.workspace(desc, M, dev)
+    y = torch.empty((M, cfg.hidden), dtype=torch.float32, device=dev)
+    ids = [torch.empty((M, k), dtype=torch.int32, device=dev) for _ in range(R)]
+    tw = [torch.empty((M, k), dtype=torch.float32, device=dev) for _ in range(R)]
+    stream = torch.cuda.current_stream()
+
+    for s in range(args.warmup):
+        i = s % R
+        svr.moe_layer_forward(desc, layers[i], xs[i], y, ids[i], tw[i], ws, stream)
+    torch.cuda.synchronize()
+    distinct = [len(np.unique(t.cpu().numpy())) for t in ids] if args.warmup else None
+    if distinct is None:
+        for i in range(R):
+            svr.moe_layer_forward(desc, layers[i], xs[i], y, ids[i], tw[i], ws, stream)
+        torch.cuda.synchronize()
+        distinct = [len(np.unique(t.cpu().numpy())) for t in ids]
+
+    nst = svr.moe_stage_count()
+    names = [svr.moe_stage_name(j) for j in range(nst)]
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(K)]
+    for row in evs:  # create the underlying HIP events before the timed region
+        for e in row:
+            e.record(stream)
+    torch.cuda.synchronize()
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        i = s % R
+        svr.moe_layer_forward_timed(desc, layers[i], xs[i], y, [e.cuda_event for e in evs[s]],
+                                    ids[i], tw[i], ws, stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    stage_ms = np.zeros(nst)
+    dom = names.index(DOMINANT)
+    dom_ms, dom_bytes = 0.0, 0.0
+    lay_bytes = 0.0
+    for s in range(K):
+        i = s % R
+        d = [evs[s][j].elapsed_time(evs[s][j + 1]) for j in range(nst)]
+        stage_ms += d
+        b = layer_bytes(cfg, distinct[i])
+        dom_ms += d[dom]
+        dom_bytes += b["gateup"]
+        lay_bytes += b["total"]
+    ev_ms = evs[0][0].elapsed_time(evs[K - 1][nst]) / K if K else 0.0
+
+    ms_per_step = elapsed * 1e3 / K
+    value = M * K / elapsed
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    traffic = traffic_for(cfg.name)
+
+    out = {
+        "metric": "MoE layer tokens/s + achieved HBM GB/s at verify batch M=4 (Q4_K), 1 MI355X",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": cfg.name, "tokens": M, "hidden": cfg.hidden, "experts": cfg.n_experts,
+            "top_k": k, "ffn": cfg.ffn, "shared_ffn": cfg.shared_ffn,
+            "routed": cfg.expert_type, "shared": cfg.shared_type, "router": "f32",
+            "instances_rotated": R, "distinct_experts": distinct,
+        },
+        "hbm_gbps": round(lay_bytes / K / (ms_per_step * 1e-3) / 1e9, 1),
+        "layer_bytes": int(round(lay_bytes / K)),
+        "event_ms_per_step": round(ev_ms, 5),
+        "stage_us": {n: round(v * 1e3 / K, 2) for n, v in zip(names, stage_ms)},
+        "roofline": {
+            "kernel": DOMINANT, "bound": "hbm", "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic, "bytes_per_launch": int(round(dom_bytes / K)),
+            "avg_launch_us": round(dom_ms * 1e3 / K, 3),
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, *host0)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

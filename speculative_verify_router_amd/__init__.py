@@ -1,0 +1,28 @@
+"""Routed mixture-of-experts verify layer for AMD Instinct MI355X (gfx950).
+
+One routed-MoE FFN block (F32 softmax top-k router, Q4_K / Q8_0 experts,
+SwiGLU, a shared expert and a weighted combine) applied to the verify batch
+of MTP speculative decoding, implemented as hand-written HIP kernels behind
+the C ABI of ``include/moe_layer.h``.  This package is the thin Python
+binding of that ABI (``_binding``) and the build helper (``build``).
+"""
+
+from ._binding import (  # noqa: F401
+    C_SYMBOLS,
+    LIB_PATH,
+    LayerDesc,
+    LayerWeights,
+    MoeError,
+    lib,
+    moe_dequant_rows,
+    moe_layer_forward,
+    moe_layer_forward_timed,
+    moe_route,
+    moe_stage_count,
+    moe_stage_name,
+    moe_strerror,
+    moe_tensor_bytes,
+    moe_version,
+    moe_workspace_bytes,
+    workspace,
+)

@@ -1,0 +1,68 @@
+// Weighted combine of expert outputs, and the block-decoder test hook.
+#pragma once
+
+#include "common.h"
+
+namespace svr {
+
+// y[t][h] = s[t][h] + sum_{j=0..k-1} w[t][j] * o[t*k + j][h], in slot order.
+// One thread per 4 consecutive outputs (float4 loads/stores).
+__global__ __launch_bounds__(kBlock) void k_combine(const float* __restrict__ o,
+                                                    const float* __restrict__ s,
+                                                    const float* __restrict__ w,
+                                                    float* __restrict__ y, int M, int H, int k) {
+  const int64_t i4 = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  const int H4 = H >> 2;
+  if (i4 >= (int64_t)M * H4) return;
+  const int t = (int)(i4 / H4);
+  const int c = (int)(i4 - (int64_t)t * H4);
+  float4 acc = s ? ldf4(s + (int64_t)t * H + 4 * c) : make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < k; ++j) {
+    const float wj = w[(int64_t)t * k + j];
+    const float4 v = ldf4(o + ((int64_t)t * k + j) * H + 4 * c);
+    acc.x = fmaf(wj, v.x, acc.x);
+    acc.y = fmaf(wj, v.y, acc.y);
+    acc.z = fmaf(wj, v.z, acc.z);
+    acc.w = fmaf(wj, v.w, acc.w);
+  }
+  *reinterpret_cast<float4*>(y + (int64_t)t * H + 4 * c) = acc;
+}
+
+// Dequantise rows [r0, r0 + n) of a planar tensor into out[n][cols].
+// Q8_0: d*q.  Q4_K: fma(d*sc, q, -(dmin*m)); d*sc and dmin*m are exact in
+// fp32, so the result is the correctly rounded block value.
+__global__ __launch_bounds__(kBlock) void k_dequant(int fmt, const uint8_t* __restrict__ base,
+                                                    int64_t rows, int cols, int64_t r0, int64_t n,
+                                                    float* __restrict__ out) {
+  const int64_t total = n * cols;
+  for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * kBlock) {
+    const int64_t r = r0 + i / cols;
+    const int c = (int)(i % cols);
+    float v;
+    if (fmt == MOE_Q8_0) {
+      const int64_t nb = cols >> 5;
+      const int64_t qoff = ((2 * rows * nb) + 255) & ~(int64_t)255;
+      const float d = f16_to_f32(*reinterpret_cast<const uint16_t*>(base + 2 * (r * nb + (c >> 5))));
+      const int q = (int)(int8_t)base[qoff + r * cols + c];
+      v = d * (float)q;
+    } else {
+      const int64_t ns = cols >> 8;
+      const int64_t rec = r * ns + (c >> 8);
+      const uint8_t* h = base + 16 * rec;
+      const float d = f16_to_f32((uint32_t)h[0] | ((uint32_t)h[1] << 8));
+      const float dmin = f16_to_f32((uint32_t)h[2] | ((uint32_t)h[3] << 8));
+      const int s = (c >> 5) & 7;
+      const int wi = c & 31;
+      const int sb = 6 * s, mb = 48 + 6 * s;  // bit offsets in the 96-bit stream
+      const uint32_t sc = (((uint32_t)h[4 + (sb >> 3)] | ((uint32_t)h[4 + min((sb >> 3) + 1, 11)] << 8)) >> (sb & 7)) & 63u;
+      const uint32_t m = (((uint32_t)h[4 + (mb >> 3)] | ((uint32_t)h[4 + min((mb >> 3) + 1, 11)] << 8)) >> (mb & 7)) & 63u;
+      const uint8_t qb = base[16 * rows * ns + 128 * rec + 16 * s + (wi >> 1)];
+      const float q = (float)((wi & 1) ? (qb >> 4) : (qb & 15));
+      v = fmaf(d * (float)sc, q, -(dmin * (float)m));
+    }
+    out[i] = v;
+  }
+}
+
+}  // namespace svr

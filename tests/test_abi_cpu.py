@@ -1,0 +1,163 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry
+point the header declares, sizes its tensors and workspace, and rejects bad
+arguments with the documented status before enqueueing anything."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import speculative_verify_router_amd as svr
+from speculative_verify_router_amd import _binding as B
+import synth
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "moe_layer.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_symbols():
+    assert _declared() == sorted(B.C_SYMBOLS)
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = svr.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+    assert svr.moe_version() >= 100
+    assert svr.moe_strerror(0) == "ok"
+    assert svr.moe_strerror(12345) == "unknown status"
+    names = [svr.moe_stage_name(i) for i in range(svr.moe_stage_count())]
+    assert "routed_gateup" in names and "routed_down" in names
+    assert svr.moe_stage_name(-1) is None and svr.moe_stage_name(len(names)) is None
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(B, "LIB_PATH", "/nonexistent/libsvr_moe.so")
+    monkeypatch.setattr(B, "_lib", None)
+    with pytest.raises(RuntimeError, match="not found"):
+        B.lib()
+
+
+@pytest.mark.parametrize("dtype,rows,cols", [("q8_0", 1, 32), ("q8_0", 1280, 4096), ("q8_0", 7, 96),
+                                             ("q4_k", 5, 256), ("q4_k", 352 * 1536, 4096),
+                                             ("f32", 3, 5)])
+def test_tensor_bytes_match_the_generator(dtype, rows, cols):
+    assert svr.moe_tensor_bytes(dtype, rows, cols) == synth.tensor_bytes(dtype, rows, cols)
+
+
+def test_tensor_bytes_rejects_bad_shapes():
+    with pytest.raises(svr.MoeError) as e:
+        svr.moe_tensor_bytes("q4_k", 4, 100)
+    assert e.value.status == B.ERR_SHAPE
+    out = ctypes.c_int64()
+    assert svr.lib().moe_tensor_bytes(9, 1, 32, ctypes.byref(out)) == B.ERR_DTYPE
+    assert svr.lib().moe_tensor_bytes(1, 1, 32, None) == B.ERR_NULL
+
+
+def _desc(**kw):
+    base = dict(hidden=4096, n_experts=288, top_k=8, ffn=1280, shared_ffn=1280,
+                expert_type="q4_k", shared_type="q8_0")
+    base.update(kw)
+    return svr.LayerDesc(**base)
+
+
+def test_workspace_grows_with_tokens():
+    a = svr.moe_workspace_bytes(_desc(), 1)
+    b = svr.moe_workspace_bytes(_desc(), 4)
+    c = svr.moe_workspace_bytes(_desc(), 512)
+    assert 0 < a < b < c
+    assert a % 256 == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hidden=4000), B.ERR_SHAPE),            # not a multiple of 256 for Q4_K
+    (dict(ffn=1000), B.ERR_SHAPE),
+    (dict(shared_ffn=100), B.ERR_SHAPE),
+    (dict(n_experts=0), B.ERR_SHAPE),
+    (dict(n_experts=2000), B.ERR_SHAPE),
+    (dict(top_k=0), B.ERR_SHAPE),
+    (dict(top_k=300), B.ERR_SHAPE),
+    (dict(top_k=65, n_experts=100), B.ERR_SHAPE),
+    (dict(hidden=288, expert_type="q8_0", shared_type="q8_0"), B.ERR_SHAPE),  # 18 chunks
+    (dict(expert_type="f32"), B.ERR_DTYPE),
+    (dict(shared_type="f32"), B.ERR_DTYPE),
+])
+def test_bad_descriptors_are_rejected(kw, status):
+    d = _desc(**kw).c()
+    out = ctypes.c_size_t()
+    assert svr.lib().moe_workspace_bytes(ctypes.byref(d), 4, ctypes.byref(out)) == status
+
+
+def test_shared_type_ignored_without_shared_expert():
+    d = _desc(shared_ffn=0, shared_type="f32").c()
+    out = ctypes.c_size_t()
+    assert svr.lib().moe_workspace_bytes(ctypes.byref(d), 4, ctypes.byref(out)) == B.OK
+
+
+FAKE = 1 << 20  # never dereferenced: every call below fails validation first
+
+
+def _fake_weights(**kw):
+    w = B._Weights(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    for k, v in kw.items():
+        setattr(w, k, v)
+    return w
+
+
+def _forward(desc=None, weights=None, x=FAKE, M=4, y=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    L = svr.lib()
+    d = desc if desc is not None else _desc().c()
+    w = weights if weights is not None else _fake_weights()
+    return L.moe_layer_forward(ctypes.byref(d) if d else None, ctypes.byref(w) if w else None,
+                               x, M, y, None, None, ws, ws_bytes, None)
+
+
+def test_forward_error_paths():
+    need = svr.moe_workspace_bytes(_desc(), 4)
+    assert _forward(ws_bytes=need - 1) == B.ERR_WORKSPACE
+    assert _forward(x=None) == B.ERR_NULL
+    assert _forward(y=None) == B.ERR_NULL
+    assert _forward(ws=None) == B.ERR_NULL
+    assert _forward(weights=_fake_weights(gate=None)) == B.ERR_NULL
+    assert _forward(weights=_fake_weights(shared_down=None)) == B.ERR_NULL
+    assert _forward(M=-1) == B.ERR_NULL
+    assert _forward(desc=_desc(ffn=100).c()) == B.ERR_SHAPE
+    assert _forward(x=FAKE + 4) == B.ERR_ARG          # misaligned activations
+    assert _forward(ws=FAKE + 16) == B.ERR_ARG        # misaligned workspace
+    L = svr.lib()
+    assert L.moe_layer_forward(None, None, FAKE, 4, FAKE, None, None, FAKE, 1 << 40, None) == B.ERR_NULL
+
+
+def test_forward_timed_checks_the_event_count():
+    L = svr.lib()
+    d, w = _desc().c(), _fake_weights()
+    evs = (ctypes.c_void_p * 3)(1, 2, 3)
+    st = L.moe_layer_forward_timed(ctypes.byref(d), ctypes.byref(w), FAKE, 4, FAKE, None, None,
+                                   FAKE, 1 << 40, None, evs, 3)
+    assert st == B.ERR_ARG
+    st = L.moe_layer_forward_timed(ctypes.byref(d), ctypes.byref(w), FAKE, 4, FAKE, None, None,
+                                   FAKE, 1 << 40, None, None, 0)
+    assert st == B.ERR_NULL
+
+
+def test_route_and_dequant_error_paths():
+    L = svr.lib()
+    d = _desc().c()
+    st = L.moe_route(ctypes.byref(d), FAKE, FAKE, 4, None, FAKE, None, None, None, None, None,
+                     FAKE, 1 << 40, None)
+    assert st == B.ERR_NULL
+    st = L.moe_route(ctypes.byref(d), FAKE, FAKE, 4, FAKE, FAKE, None, None, None, None, None,
+                     FAKE, 10, None)
+    assert st == B.ERR_WORKSPACE
+    assert L.moe_dequant_rows(7, FAKE, 10, 256, 0, 10, FAKE, None) == B.ERR_DTYPE
+    assert L.moe_dequant_rows(2, FAKE, 10, 100, 0, 10, FAKE, None) == B.ERR_SHAPE
+    assert L.moe_dequant_rows(1, FAKE, 10, 64, 5, 6, FAKE, None) == B.ERR_SHAPE
+    assert L.moe_dequant_rows(1, None, 10, 64, 0, 5, FAKE, None) == B.ERR_NULL
+    assert L.moe_dequant_rows(1, None, 10, 64, 0, 0, None, None) == B.OK    # empty range

@@ -1,0 +1,51 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times (same shapes, same token counts, one moe_layer_forward).
+
+Step-3.5-Flash-shaped decode (M=1, Q8_0), the same layer as the 4-token
+verify batch (Q4_K routed), the Step-5-shaped verify batch with the four
+tokens on disjoint experts, and the 512-token prefill micro-batch, whose
+FFN outputs the oracle computes for a sample of tokens.
+"""
+
+import gc
+
+import numpy as np
+import pytest
+
+import synth
+from _support import conditioned_tokens, run_oracle
+from gpu_common import check_routing, check_y, dev, gpu_forward, gpu_route, log, upload
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+SAMPLE_TOKENS = [0, 1, 2, 255, 256, 400, 510, 511]
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["step35_decode_m1", "step35_verify_m4", "step5_verify_m4",
+                                  "step5_prefill_m512"])
+def test_full_config(name):
+    cfg = synth.CONFIGS[name]
+    log(f"[{name}] drawing layer")
+    inp = synth.draw_layer(cfg)
+    x, attempts = conditioned_tokens(inp)
+    log(f"[{name}] tokens drawn, redraws = {sum(attempts)}")
+    w = upload(inp)
+    y, ids, tw = gpu_forward(cfg, w, x)
+    log(f"[{name}] GPU done")
+    tokens = None if cfg.n_tokens <= 4 else SAMPLE_TOKENS
+    ref = run_oracle(inp, x, tokens=tokens)
+    log(f"[{name}] oracle done, distinct experts = {len(ref['active'])}")
+    check_routing(ids, tw, ref)
+    rows = ref["tokens"]
+    check_y(y[rows], ref["y"], name)
+    if name == "step5_verify_m4":
+        assert len(ref["active"]) == 32
+    # Routing lists of the whole batch, exactly.
+    r = gpu_route(cfg, w.router, x)
+    assert np.array_equal(r["counts"], ref["counts"])
+    assert np.array_equal(r["offsets"], ref["offsets"])
+    assert np.array_equal(r["slots"], ref["slots"])
+    assert int(r["n_active"][0]) == len(ref["active"])
+    del w, inp
+    gc.collect()

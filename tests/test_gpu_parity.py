@@ -1,0 +1,221 @@
+"""GPU parity on small and edge-case layers: HIP library vs the CPU oracle.
+
+Every call goes through the C ABI.  Expert ids, their order and the bucket
+lists must match exactly; routing weights within 1e-6; outputs within
+2e-3 x RMS of the oracle's output.  Block decoding must be bit-exact.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as om
+import synth
+from _support import (conditioned_tokens, copy_expert_rows, read_fixture, run_oracle,
+                      scale_fields, small_config)
+from gpu_common import (check_routing, check_y, desc_of, dev, gpu_forward, gpu_route, log,
+                        upload)
+import speculative_verify_router_amd as svr
+
+pytestmark = pytest.mark.gpu
+
+
+def _layer_case(cfg, x=None, inp=None):
+    log(f"case {cfg.name}: H={cfg.hidden} E={cfg.n_experts} k={cfg.top_k} F={cfg.ffn} "
+        f"Fs={cfg.shared_ffn} {cfg.expert_type}/{cfg.shared_type} M={cfg.n_tokens}")
+    inp = inp or synth.draw_layer(cfg)
+    if x is None:
+        x, _ = conditioned_tokens(inp)
+    ref = run_oracle(inp, x)
+    y, ids, w = gpu_forward(cfg, upload(inp), x)
+    check_routing(ids, w, ref)
+    check_y(y, ref["y"], cfg.name)
+    return inp, x, y, ref
+
+
+# ----------------------------------------------------------------------------- dequant
+
+@pytest.mark.parametrize("fixture,dtype", [("q8_0_planar.txt", "q8_0"), ("q4_k_planar.txt", "q4_k")])
+def test_dequant_fixture_bit_exact(fixture, dtype):
+    rows, cols, buf, _ = read_fixture(fixture)
+    ref = om.dequant(dtype, buf, rows, cols).astype(np.float32)
+    out = torch.empty((rows, cols), dtype=torch.float32, device="cuda")
+    svr.moe_dequant_rows(dtype, dev(buf), rows, cols, 0, rows, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("dtype,cols", [("q8_0", 4096), ("q8_0", 1280), ("q4_k", 4096), ("q4_k", 1536)])
+def test_dequant_random_bit_exact(dtype, cols):
+    cfg = small_config(hidden=cols, ffn=256, n_experts=3, expert_type=dtype, seed_index=300)
+    inp = synth.draw_layer(cfg)
+    rows = 3 * 256
+    buf = inp.gate.copy()
+    # a few subnormal and zero scales
+    f = scale_fields(dtype, buf, rows, cols)     # a view into buf
+    f[:7] = np.array([0, 1, 2, 0x3FF, 0x200, 0x8001, 0], dtype=np.uint16).reshape(
+        (7,) + (1,) * (f.ndim - 1))
+    ref = om.dequant(dtype, buf, rows, cols, 5, 300).astype(np.float32)
+    out = torch.empty((300, cols), dtype=torch.float32, device="cuda")
+    svr.moe_dequant_rows(dtype, dev(buf), rows, cols, 5, 300, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+# ----------------------------------------------------------------------------- routing
+
+@pytest.mark.parametrize("E,k,M", [(8, 2, 1), (8, 8, 3), (8, 1, 5), (288, 8, 4), (352, 8, 64),
+                                   (1024, 64, 7), (1, 1, 2), (100, 3, 300)])
+def test_route_exact(E, k, M):
+    cfg = small_config(n_experts=E, top_k=k, n_tokens=M, hidden=512, router_std=0.3,
+                       seed_index=400 + E + k)
+    rng = np.random.default_rng(E * 1000 + k)
+    router = (rng.standard_normal((E, 512)) * 0.3).astype(np.float32)
+    inp = synth.LayerInputs(cfg, router, None, None, None)
+    x, _ = conditioned_tokens(inp)
+    ref = om.route(router, x, k)
+    got = gpu_route(cfg, dev(router), x)
+    check_routing(got["ids"], got["w"], ref)
+    assert np.array_equal(got["counts"], ref["counts"])
+    assert np.array_equal(got["offsets"], ref["offsets"])
+    assert np.array_equal(got["slots"][:M * k], ref["slots"])
+    na = int(got["n_active"][0])
+    assert na == len(ref["active"])
+    assert np.array_equal(got["active"][:na], ref["active"])
+    assert np.all(got["active"][na:] == -1)
+
+
+def test_route_ties_go_to_lower_index():
+    # Router rows 0..7 identical: every token sees 8 exactly equal logits.
+    cfg = small_config(n_experts=8, top_k=3, n_tokens=2, hidden=256)
+    router = np.tile(np.random.default_rng(5).standard_normal(256).astype(np.float32), (8, 1))
+    x = np.random.default_rng(6).standard_normal((2, 256)).astype(np.float32)
+    got = gpu_route(cfg, dev(router), x)
+    assert got["ids"].tolist() == [[0, 1, 2], [0, 1, 2]]
+    assert np.allclose(got["w"], 1.0 / 3.0, atol=1e-7)
+
+
+# ----------------------------------------------------------------------------- layer
+
+def test_tiny_config():
+    _layer_case(synth.CONFIGS["tiny"])
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 9])
+def test_small_q4_k_with_shared(M):
+    cfg = small_config(hidden=512, n_experts=16, top_k=4, ffn=256, shared_ffn=128,
+                       expert_type="q4_k", n_tokens=M, router_std=0.2, seed_index=500 + M)
+    _layer_case(cfg)
+
+
+@pytest.mark.parametrize("M", [1, 4, 6])
+def test_small_q8_0_with_shared(M):
+    cfg = small_config(hidden=1024, n_experts=12, top_k=3, ffn=320, shared_ffn=192,
+                       expert_type="q8_0", n_tokens=M, router_std=0.1, seed_index=520 + M)
+    _layer_case(cfg)
+
+
+def test_shared_expert_in_q4_k():
+    cfg = small_config(hidden=512, n_experts=8, top_k=2, ffn=512, shared_ffn=256,
+                       expert_type="q4_k", shared_type="q4_k", n_tokens=3, router_std=0.2,
+                       seed_index=540)
+    _layer_case(cfg)
+
+
+def test_k_equals_one():
+    _layer_case(small_config(n_experts=8, top_k=1, n_tokens=4, seed_index=550))
+
+
+def test_k_equals_n_experts():
+    _layer_case(small_config(n_experts=6, top_k=6, n_tokens=3, shared_ffn=64, seed_index=551))
+
+
+def test_single_expert_layer():
+    _layer_case(small_config(n_experts=1, top_k=1, n_tokens=3, ffn=96, seed_index=552))
+
+
+def test_ragged_rows_and_lanes():
+    # F = 96 (3 Q8_0 blocks: 6 chunks per down row) and H = 640 (20 blocks):
+    # row tiles and lane groups both end part-way.
+    _layer_case(small_config(hidden=640, n_experts=5, top_k=2, ffn=96, shared_ffn=160,
+                             n_tokens=5, router_std=0.2, seed_index=553))
+
+
+def test_all_tokens_on_the_same_experts():
+    cfg = small_config(hidden=512, n_experts=16, top_k=4, ffn=256, shared_ffn=128,
+                       expert_type="q4_k", n_tokens=8, router_std=0.2, seed_index=554)
+    inp = synth.draw_layer(cfg)
+    x1, _ = conditioned_tokens(inp, n_tokens=1)
+    x = np.repeat(x1, 8, axis=0)
+    _, _, y, ref = _layer_case(cfg, x=x, inp=inp)
+    assert len(ref["active"]) == 4
+    assert np.array_equal(y, np.repeat(y[:1], 8, axis=0))
+
+
+def test_zero_and_subnormal_scales():
+    for etype in ("q8_0", "q4_k"):
+        F = 256
+        cfg = small_config(hidden=512, n_experts=4, top_k=2, ffn=F, shared_ffn=64,
+                           expert_type=etype, n_tokens=3, router_std=0.2, seed_index=555)
+        inp = synth.draw_layer(cfg)
+        for name, rows, cols in (("gate", 4 * F, 512), ("up", 4 * F, 512), ("down", 4 * 512, F)):
+            buf = getattr(inp, name).copy()
+            f = scale_fields(etype, buf, rows, cols)     # a view into buf
+            f[::5] = 0                                   # zero blocks
+            f[1::7] = f[1::7] & 0x83FF                   # subnormal (exponent field 0)
+            setattr(inp, name, buf)
+        _layer_case(cfg, inp=inp)
+
+
+def test_identical_experts_match_across_routing():
+    cfg = small_config(hidden=512, n_experts=6, top_k=3, ffn=256, expert_type="q4_k",
+                       n_tokens=4, router_std=0.2, seed_index=556)
+    inp = synth.draw_layer(cfg)
+    inp.gate = copy_expert_rows("q4_k", inp.gate, 256, 512, 6)
+    inp.up = copy_expert_rows("q4_k", inp.up, 256, 512, 6)
+    inp.down = copy_expert_rows("q4_k", inp.down, 512, 256, 6)
+    _layer_case(cfg, inp=inp)
+
+
+def test_rows_equal_single_token_calls_bitwise():
+    # Each token's result does not depend on the other tokens of the batch.
+    cfg = small_config(hidden=1024, n_experts=32, top_k=4, ffn=512, shared_ffn=256,
+                       expert_type="q4_k", n_tokens=4, router_std=0.1, seed_index=557)
+    inp, x, y, _ = _layer_case(cfg)
+    w = upload(inp)
+    for t in range(4):
+        y1, _, _ = gpu_forward(cfg, w, x[t:t + 1])
+        assert np.array_equal(y1[0].view(np.uint32), y[t].view(np.uint32)), t
+
+
+def test_zero_tokens_is_a_no_op():
+    cfg = small_config()
+    inp = synth.draw_layer(cfg)
+    x = torch.empty((0, cfg.hidden), dtype=torch.float32, device="cuda")
+    y = torch.empty((0, cfg.hidden), dtype=torch.float32, device="cuda")
+    svr.moe_layer_forward(desc_of(cfg), upload(inp), x, y, ws=torch.empty(256, dtype=torch.uint8,
+                                                                            device="cuda"))
+    torch.cuda.synchronize()
+
+
+def test_timed_forward_matches_and_records_events():
+    cfg = small_config(hidden=512, n_experts=16, top_k=4, ffn=256, shared_ffn=128,
+                       expert_type="q4_k", n_tokens=4, router_std=0.2, seed_index=558)
+    inp = synth.draw_layer(cfg)
+    x, _ = conditioned_tokens(inp)
+    w = upload(inp)
+    y0, _, _ = gpu_forward(cfg, w, x)
+    n = svr.moe_stage_count() + 1
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for e in evs:
+        e.record()
+    torch.cuda.synchronize()
+    y = torch.empty((4, 512), dtype=torch.float32, device="cuda")
+    svr.moe_layer_forward_timed(desc_of(cfg), w, dev(x), y, [e.cuda_event for e in evs])
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy(), y0)
+    ms = [evs[i].elapsed_time(evs[i + 1]) for i in range(n - 1)]
+    assert all(m >= 0 for m in ms)
+    with pytest.raises(svr.MoeError):
+        svr.moe_layer_forward_timed(desc_of(cfg), w, dev(x), y, [e.cuda_event for e in evs[:-1]])
