@@ -33,8 +33,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "step35_verify_m4"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "routed_gateup_traffic.json")
-DOMINANT = "routed_gateup"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gateup_traffic.json")
+DOMINANT = "gateup"
 
 
 def _bytes_per_row(dtype: str, cols: int) -> float:
@@ -50,7 +50,10 @@ def layer_bytes(cfg, distinct: int) -> dict:
         shared = 2 * Fs * _bytes_per_row(cfg.shared_type, H) + H * _bytes_per_row(cfg.shared_type, Fs)
     router = cfg.n_experts * H * 4
     xy = 2 * M * H * 4
+    # Stage "gateup": routed gate/up (x in, h out) and shared down (hs in, s out).
     gateup = distinct * 2 * F * _bytes_per_row(cfg.expert_type, H) + M * H * 4 + M * k * F * 4
+    if Fs:
+        gateup += H * _bytes_per_row(cfg.shared_type, Fs) + M * Fs * 4 + M * H * 4
     return dict(total=router + distinct * expert + shared + xy, gateup=gateup)
 
 
@@ -106,6 +109,10 @@ def main(argv=None) -> int:
     ap.add_argument("--instances", type=int, default=4, help="layer instances rotated over")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--events", choices=["dominant", "all"], default="dominant",
+                    help="HIP events per step: around the dominant stage only, or every stage")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the same steps replayed from a captured HIP graph")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -147,16 +154,16 @@ def main(argv=None) -> int:
     tw = [torch.empty((M, k), dtype=torch.float32, device=dev) for _ in range(R)]
     stream = torch.cuda.current_stream()
 
+    calls = [svr.PreparedForward(desc, layers[i], xs[i], y, ids[i], tw[i], ws, stream)
+             for i in range(R)]
     for s in range(args.warmup):
-        i = s % R
-        svr.moe_layer_forward(desc, layers[i], xs[i], y, ids[i], tw[i], ws, stream)
+        calls[s % R]()
     torch.cuda.synchronize()
-    distinct = [len(np.unique(t.cpu().numpy())) for t in ids] if args.warmup else None
-    if distinct is None:
+    if args.warmup < R:
         for i in range(R):
-            svr.moe_layer_forward(desc, layers[i], xs[i], y, ids[i], tw[i], ws, stream)
+            calls[i]()
         torch.cuda.synchronize()
-        distinct = [len(np.unique(t.cpu().numpy())) for t in ids]
+    distinct = [len(np.unique(t.cpu().numpy())) for t in ids]
 
     nst = svr.moe_stage_count()
     names = [svr.moe_stage_name(j) for j in range(nst)]
@@ -165,30 +172,62 @@ def main(argv=None) -> int:
     for row in evs:  # create the underlying HIP events before the timed region
         for e in row:
             e.record(stream)
+    import ctypes
+    dom = names.index(DOMINANT)
+    if args.events == "all":
+        ev_arrays = [(ctypes.c_void_p * (nst + 1))(*[e.cuda_event for e in row]) for row in evs]
+    else:
+        # Only the dominant stage's boundaries carry real events; the others
+        # are NULL entries, which the library skips.
+        ev_arrays = [(ctypes.c_void_p * (nst + 1))(
+            *[row[j].cuda_event if j in (dom, dom + 1) else None for j in range(nst + 1)])
+            for row in evs]
     torch.cuda.synchronize()
 
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(K):
-        i = s % R
-        svr.moe_layer_forward_timed(desc, layers[i], xs[i], y, [e.cuda_event for e in evs[s]],
-                                    ids[i], tw[i], ws, stream)
+        calls[s % R](ev_arrays[s])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
     stage_ms = np.zeros(nst)
-    dom = names.index(DOMINANT)
     dom_ms, dom_bytes = 0.0, 0.0
     lay_bytes = 0.0
     for s in range(K):
         i = s % R
-        d = [evs[s][j].elapsed_time(evs[s][j + 1]) for j in range(nst)]
-        stage_ms += d
+        if args.events == "all":
+            stage_ms += [evs[s][j].elapsed_time(evs[s][j + 1]) for j in range(nst)]
+        dom_ms += evs[s][dom].elapsed_time(evs[s][dom + 1])
         b = layer_bytes(cfg, distinct[i])
-        dom_ms += d[dom]
         dom_bytes += b["gateup"]
         lay_bytes += b["total"]
-    ev_ms = evs[0][0].elapsed_time(evs[K - 1][nst]) / K if K else 0.0
+
+    graph_ms = None
+    if args.graph:
+        # One captured graph holds one call per instance; replays keep the
+        # same rotation.  The workspace counters return to zero every call.
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        gcalls = [svr.PreparedForward(desc, layers[i], xs[i], y, ids[i], tw[i], ws, side)
+                  for i in range(R)]
+        with torch.cuda.stream(side):
+            for c in gcalls:
+                c()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=side):
+            for c in gcalls:
+                c()
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        reps = max(1, K // R)
+        t1 = time.perf_counter()
+        for _ in range(reps):
+            g.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t1) * 1e3 / (reps * R)
 
     ms_per_step = elapsed * 1e3 / K
     value = M * K / elapsed
@@ -216,8 +255,7 @@ def main(argv=None) -> int:
         },
         "hbm_gbps": round(lay_bytes / K / (ms_per_step * 1e-3) / 1e9, 1),
         "layer_bytes": int(round(lay_bytes / K)),
-        "event_ms_per_step": round(ev_ms, 5),
-        "stage_us": {n: round(v * 1e3 / K, 2) for n, v in zip(names, stage_ms)},
+        "events": args.events,
         "roofline": {
             "kernel": DOMINANT, "bound": "hbm", "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -225,6 +263,11 @@ def main(argv=None) -> int:
             "avg_launch_us": round(dom_ms * 1e3 / K, 3),
         },
     }
+    if args.events == "all":
+        out["stage_us"] = {n: round(v * 1e3 / K, 2) for n, v in zip(names, stage_ms)}
+    if graph_ms is not None:
+        out["graph_replay"] = {"ms_per_step": round(graph_ms, 5),
+                               "tokens_per_s": round(M / (graph_ms * 1e-3), 1)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, *host0)
     print(json.dumps(out), flush=True)

@@ -127,8 +127,12 @@ const char* moe_strerror(int32_t status);
 int32_t moe_tensor_bytes(int32_t dtype, int64_t rows, int64_t cols, int64_t* bytes);
 
 /* Device workspace, in *bytes, that moe_layer_forward and moe_route need for
- * up to max_tokens tokens: router logits, routing lists, the SwiGLU
- * activations of every (token, slot) pair and the per-pair expert outputs. */
+ * up to max_tokens tokens: a 4 KiB page of hand-off counters, router logits,
+ * routing lists, the SwiGLU activations of every (token, slot) pair and the
+ * per-pair expert outputs.  The counter page (the first 4096 bytes) must be
+ * zero before the first call that uses the workspace; every call leaves it
+ * zero again, so zero-fill a workspace once when it is allocated.  Calls that
+ * share a workspace must not overlap in time. */
 int32_t moe_workspace_bytes(const moe_layer_desc* desc, int32_t max_tokens, size_t* bytes);
 
 /* Routing only (steps: router GEMV, top-k with renormalised softmax weights,
@@ -149,7 +153,9 @@ int32_t moe_route(const moe_layer_desc* desc, const float* router, const float* 
 
 /* The whole layer: y [M][H] float from x [M][H] float.  topk_ids [M][k] and
  * topk_w [M][k] receive the routing if non-NULL.  workspace must hold
- * moe_workspace_bytes(desc, n_tokens) bytes (device, 256-byte aligned). */
+ * moe_workspace_bytes(desc, n_tokens) bytes (device, 256-byte aligned,
+ * counter page zero as described above).  The stages are listed by
+ * moe_stage_count / moe_stage_name. */
 int32_t moe_layer_forward(const moe_layer_desc* desc, const moe_layer_weights* weights,
                           const float* x, int32_t n_tokens, float* y,
                           int32_t* topk_ids, float* topk_w,
@@ -162,7 +168,8 @@ const char* moe_stage_name(int32_t i);
 
 /* moe_layer_forward that also records events[i] (hipEvent_t, created by the
  * caller) on hip_stream before stage i and events[moe_stage_count()] after
- * the last stage, so that the caller can time each stage.  n_events must be
+ * the last stage, so that the caller can time each stage.  A NULL entry is
+ * skipped (no event recorded at that boundary).  n_events must be
  * moe_stage_count() + 1, else MOE_ERR_ARG. */
 int32_t moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_weights* weights,
                                 const float* x, int32_t n_tokens, float* y,

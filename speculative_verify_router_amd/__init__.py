@@ -13,6 +13,7 @@ from ._binding import (  # noqa: F401
     LayerDesc,
     LayerWeights,
     MoeError,
+    PreparedForward,
     lib,
     moe_dequant_rows,
     moe_layer_forward,

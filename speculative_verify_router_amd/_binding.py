@@ -174,9 +174,10 @@ def moe_stage_name(i: int) -> Optional[str]:
 
 
 def workspace(desc: LayerDesc, max_tokens: int, device="cuda") -> torch.Tensor:
-    """A device workspace tensor of moe_workspace_bytes(desc, max_tokens) bytes."""
-    n = max(moe_workspace_bytes(desc, max_tokens), 256)
-    return torch.empty(n, dtype=torch.uint8, device=device)
+    """A zero-filled device workspace of moe_workspace_bytes(desc, max_tokens)
+    bytes (its counter page must start at zero; calls keep it so)."""
+    n = max(moe_workspace_bytes(desc, max_tokens), 4096)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
 def moe_route(desc: LayerDesc, router: torch.Tensor, x: torch.Tensor, topk_ids: torch.Tensor,
@@ -222,6 +223,41 @@ def moe_layer_forward_timed(desc: LayerDesc, weights: LayerWeights, x: torch.Ten
                                        _ptr(topk_w, torch.float32), _ptr(ws, torch.uint8),
                                        ws.numel(), _stream(stream), arr, len(events))
     _check(st, "moe_layer_forward_timed")
+
+
+class PreparedForward:
+    """A moe_layer_forward call with its arguments marshalled once.
+
+    The tensors are captured by reference (their device pointers are fixed);
+    calling the object enqueues the layer again on the captured stream.
+    ``events`` (raw hipEvent_t handles), if given per call, selects
+    moe_layer_forward_timed.
+    """
+
+    def __init__(self, desc: LayerDesc, weights: LayerWeights, x: torch.Tensor, y: torch.Tensor,
+                 topk_ids=None, topk_w=None, ws: torch.Tensor = None, stream=None):
+        self._keep = (weights, x, y, topk_ids, topk_w)
+        if ws is None:
+            ws = workspace(desc, x.shape[0], x.device)
+        self._ws = ws
+        self._d = desc.c()
+        self._w = weights.c()
+        vp = ctypes.c_void_p
+        self._args = (ctypes.byref(self._d), ctypes.byref(self._w), vp(_ptr(x, torch.float32)),
+                      ctypes.c_int32(x.shape[0]), vp(_ptr(y, torch.float32)),
+                      vp(_ptr(topk_ids, torch.int32)), vp(_ptr(topk_w, torch.float32)),
+                      vp(_ptr(ws, torch.uint8)), ctypes.c_size_t(ws.numel()),
+                      vp(_stream(stream)))
+        self._f = lib().moe_layer_forward
+        self._ft = lib().moe_layer_forward_timed
+
+    def __call__(self, events=None):
+        if events is None:
+            st = self._f(*self._args)
+        else:
+            st = self._ft(*self._args, events, len(events))
+        if st != OK:
+            raise MoeError(st, "moe_layer_forward")
 
 
 def moe_dequant_rows(dtype: str, tensor: torch.Tensor, rows: int, cols: int, row_start: int,

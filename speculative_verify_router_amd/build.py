@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libsvr_moe.so")
 SOURCES = [os.path.join(CSRC, "moe_layer.hip")]
-HEADERS = [os.path.join(CSRC, f) for f in ("common.h", "route.h", "ffn.h", "misc.h")] + [
+HEADERS = [os.path.join(CSRC, f) for f in ("common.h", "quant.h", "route.h", "ffn.h", "phases.h", "misc.h")] + [
     os.path.join(ROOT, "include", "moe_layer.h")]
 
 ARCH = "gfx950"

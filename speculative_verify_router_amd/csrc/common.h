@@ -10,23 +10,89 @@ namespace svr {
 
 constexpr int kWave = 64;          // CDNA wavefront width
 constexpr int kBlock = 256;        // threads per workgroup (4 waves)
+constexpr int kWavesPerBlock = kBlock / kWave;
 constexpr int kMaxExperts = 1024;  // experts per layer
 constexpr int kMaxTopK = 64;       // selected experts per token
 constexpr int kMaxChunksPerLane = 8;
 
-// fp16 bit pattern -> float (v_cvt_f32_f16; subnormals kept).
+// fp16 bit pattern -> float (v_cvt_f32_f16; subnormals kept: the kernels run
+// with fp16/fp64 denormals enabled).
 __device__ __forceinline__ float f16_to_f32(uint32_t bits) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits & 0xFFFFu));
 }
+__device__ __forceinline__ float f16_lo(uint32_t v) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xFFFFu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t v) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
+}
 
-// Sum over an aligned group of `lpr` consecutive lanes (lpr a power of two
-// <= 64); every lane of the group receives the total.
-__device__ __forceinline__ float group_sum(float v, int lpr) {
-  for (int off = lpr >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+// DPP lane moves.  update_dpp(old, src, ...) returns `old` in lanes whose
+// source is outside the row (row_shr) or whose row is masked off.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp(float old, float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old),
+                                                               __builtin_bit_cast(int, v), CTRL,
+                                                               ROW_MASK, 0xF, false));
+}
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t old, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+constexpr int kDppShr1 = 0x111, kDppShr2 = 0x112, kDppShr4 = 0x114, kDppShr8 = 0x118;
+constexpr int kDppBcast15 = 0x142, kDppBcast31 = 0x143;
+
+// Sum over each aligned group of `lpr` lanes (lpr a power of two <= 64),
+// delivered in the group's LAST lane (other lanes hold partial sums).  Only
+// DPP moves: an inclusive scan inside 16-lane rows, then row broadcasts.
+__device__ __forceinline__ float group_sum_last(float v, int lpr) {
+  if (lpr >= 2) v += dpp<kDppShr1>(0.f, v);
+  if (lpr >= 4) v += dpp<kDppShr2>(0.f, v);
+  if (lpr >= 8) v += dpp<kDppShr4>(0.f, v);
+  if (lpr >= 16) v += dpp<kDppShr8>(0.f, v);
+  if (lpr >= 32) v += dpp<kDppBcast15, 0xA>(0.f, v);
+  if (lpr >= 64) v += dpp<kDppBcast31, 0xC>(0.f, v);
   return v;
 }
 
-__device__ __forceinline__ float wave_sum(float v) { return group_sum(v, kWave); }
+// Sum over the whole wave, returned to every lane.
+__device__ __forceinline__ float wave_sum(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, group_sum_last(v, kWave)), kWave - 1));
+}
+
+// Maximum / minimum of a u32 over the wave, returned to every lane.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u<kDppShr1>(v, v));
+  v = max(v, dpp_u<kDppShr2>(v, v));
+  v = max(v, dpp_u<kDppShr4>(v, v));
+  v = max(v, dpp_u<kDppShr8>(v, v));
+  v = max(v, dpp_u<kDppBcast15, 0xA>(v, v));
+  v = max(v, dpp_u<kDppBcast31, 0xC>(v, v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, kWave - 1);
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, dpp_u<kDppShr1>(v, v));
+  v = min(v, dpp_u<kDppShr2>(v, v));
+  v = min(v, dpp_u<kDppShr4>(v, v));
+  v = min(v, dpp_u<kDppShr8>(v, v));
+  v = min(v, dpp_u<kDppBcast15, 0xA>(v, v));
+  v = min(v, dpp_u<kDppBcast31, 0xC>(v, v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, kWave - 1);
+}
+
+// Hand-off stores and loads for data that another workgroup, possibly on
+// another XCD, reads in the same launch: agent-scope relaxed atomics write
+// through and read past the per-XCD L2, so no cache-wide release or
+// acquire fence is needed.
+template <typename T>
+__device__ __forceinline__ void store_shared(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T load_shared(const T* p) {
+  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 __device__ __forceinline__ uint4 ld16(const uint8_t* p) {
   return *reinterpret_cast<const uint4*>(p);
@@ -42,6 +108,40 @@ __device__ __forceinline__ float ubyte_f(uint32_t v) {
   return (float)((v >> (8 * B)) & 0xFFu);
 }
 
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+// silu(g) = g / (1 + e^-g) with the hardware reciprocal (1 ulp); e^-g
+// overflowing to inf gives -0 for very negative g, as the limit requires.
+__device__ __forceinline__ float silu(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+}
+
+// Buffer resource over [base, base + bytes): 16-byte loads with 32-bit
+// offsets; reads past `bytes` return zero.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t bload2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+// 16-byte load that reads past the per-XCD L2 (sc1), for data another
+// workgroup of the same launch wrote with store_shared.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+constexpr int kCpolSc1 = 16;
+__device__ __forceinline__ f32x4 bload16_shared(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpolSc1);
+}
+
+// "Last workgroup done" hand-off.  Every wave of the workgroup must have
+// waited for its hand-off stores (store_shared) to complete -- wait_stores()
+// -- before the barrier that precedes this call by one thread.  Returns the
+// counter's previous value.
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0); }
+__device__ __forceinline__ unsigned arrive(unsigned* ctr) {
+  return __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 }  // namespace svr

@@ -5,43 +5,29 @@
 // Precision distribution table).  At a verify batch of four tokens with 8
 // of 288-352 experts each, an expert serves about one token, so this is an
 // HBM-bound matrix-vector product: each selected expert's quant blocks are
-// streamed exactly once, for all of that expert's tokens together.
+// streamed once for all of that expert's tokens.
 //
 // Mapping.  A 16-byte chunk of the quant plane is the unit of loading:
 // 16 weights for Q8_0, one 32-weight sub-block for Q4_K.  A row of K
-// columns has C = K/16 (Q8_0) or K/32 (Q4_K) chunks, covered by a group of
-// `lpr` consecutive lanes (lpr | 64), lane j of the group taking chunks
-// j, j+lpr, ..., j+(CPL-1)*lpr.  A wave therefore works on 64/lpr rows at
-// once and every wave load instruction reads whole 128-byte lines.  Each
-// lane keeps its K-slice of the activations in VGPRs for the whole pass, so
-// activations are read from L2 once per wave, not once per row.
+// columns has K / kWpc chunks, covered by a group of `lpr` consecutive
+// lanes (lpr | 64), lane j of the group taking chunks j, j+lpr, ...,
+// j+(CPL-1)*lpr.  A wave works on 64/lpr rows at once and every wave load
+// instruction reads whole 128-byte lines.  Each lane keeps its K-slice of
+// the activations in VGPRs for the whole pass, so activations are read once
+// per wave, not once per row.  Row loads go through a ring of NST register
+// stages: while one step's chunks are multiplied, the next NST-1 steps'
+// chunks are in flight.  Loads use per-expert buffer resources, so rows
+// past the expert's end read as zero and need no clamping.
 //
-// Arithmetic (fp32 FMA throughout, no packed-fp32 forms):
-//  * Q8_0: bytes are flipped to q+128 with one XOR per dword so that
-//    v_cvt_f32_ubyte converts them; sum((q+128) x) - 128 sum(x) = sum(q x).
-//  * Q4_K: a dword of quants masked with 0x0F0F0F0F gives the even weights
-//    and with 0xF0F0F0F0 gives 16x the odd weights; the odd activations are
-//    stored pre-scaled by 1/16 (exact), so one accumulator serves both.
-//    w = d*sc*q - dmin*m folds to d*sc*sum(q x) - dmin*m*sum(x) per
-//    sub-block, with sum(x) precomputed per lane.
+// Work split.  Routed experts: the four waves of a workgroup take
+// different rows (tokens in passes of TP).  The shared expert serves every
+// token, so there the waves take different tokens over the same rows and
+// the rows are fetched from HBM once.
 #pragma once
 
-#include "common.h"
+#include "quant.h"
 
 namespace svr {
-
-enum QFmt { kQ8_0 = 1, kQ4_K = 2 };
-
-template <int FMT>
-struct QTraits;
-template <>
-struct QTraits<kQ8_0> {
-  static constexpr int kWpc = 16;  // weights per 16-byte chunk
-};
-template <>
-struct QTraits<kQ4_K> {
-  static constexpr int kWpc = 32;
-};
 
 struct FfnArgs {
   const uint8_t* w0;        // gate (gate/up role) or down: planar tensor base
@@ -59,254 +45,191 @@ struct FfnArgs {
   int act_by_pair;          // activation row = pair (1) or token (0)
   float* out;               // output rows of width rows_per_expert
   int lpr;                  // lanes per row (power of two dividing 64)
-  int units_per_block;      // output rows per workgroup (multiple of 4*64/lpr)
+  int units_per_block;      // output rows per workgroup
+  int split_tokens;         // 1: waves take tokens, 0: waves take rows
+  int coherent_out;         // 1: outputs are read by other workgroups of this launch
+  const int32_t* pair_expert;  // pair slots: slot p is pair p, expert pair_expert[p]
+  int n_pairs;                 // number of pair slots (pair_expert != NULL)
 };
 
-// Per-lane view of one 16-byte chunk of a row: its quants and its scale data.
-template <int FMT>
-struct Chunk;
-template <>
-struct Chunk<kQ8_0> {
-  uint4 q;
-  uint32_t d;  // fp16 bits
-};
-template <>
-struct Chunk<kQ4_K> {
-  uint4 q;
-  uint4 h;  // super-block header
-};
-
-template <int FMT>
-__device__ __forceinline__ void load_chunk(Chunk<FMT>& ch, const uint8_t* base, int64_t total_rows,
-                                           int K, int64_t row, int c);
-
-template <>
-__device__ __forceinline__ void load_chunk<kQ8_0>(Chunk<kQ8_0>& ch, const uint8_t* base,
-                                                  int64_t total_rows, int K, int64_t row, int c) {
-  const int64_t nb = K >> 5;
-  const int64_t qoff = ((2 * total_rows * nb) + 255) & ~(int64_t)255;
-  ch.q = ld16(base + qoff + row * K + 16 * c);
-  ch.d = *reinterpret_cast<const uint16_t*>(base + 2 * (row * nb + (c >> 1)));
+// Tokens per pass: keep the per-lane activation slice within 64 floats.
+constexpr int tp_for(int fmt, int cpl) {
+  return (cpl * (fmt == kQ8_0 ? 16 : 32) <= 16) ? 4 : (cpl * (fmt == kQ8_0 ? 16 : 32) <= 32) ? 2 : 1;
 }
 
-template <>
-__device__ __forceinline__ void load_chunk<kQ4_K>(Chunk<kQ4_K>& ch, const uint8_t* base,
-                                                  int64_t total_rows, int K, int64_t row, int c) {
-  const int64_t ns = K >> 8;
-  const int64_t hb = 16 * total_rows * ns;
-  ch.q = ld16(base + hb + row * (K >> 1) + 16 * c);
-  ch.h = ld16(base + 16 * (row * ns + (c >> 3)));
+// Ring depth: three stages while the in-flight chunks of the ring stay
+// within about 100 VGPRs, else two.
+constexpr int nst_for(int fmt, int cpl, bool gateup) {
+  return (cpl * (gateup ? 2 : 1) * (fmt == kQ8_0 ? 5 : 8) * 3 <= 100) ? 3 : 2;
 }
 
-// Activation slice of one token for one chunk position.
-template <int FMT>
-struct XSlice {
-  float v[QTraits<FMT>::kWpc];
-  float sum;  // Q8_0: 128 * sum(x); Q4_K: sum(x)
+template <int FMT, int CPL, bool GATEUP>
+struct Stage {
+  Chunk<FMT> c0[CPL];
+  Chunk<FMT> c1[GATEUP ? CPL : 1];
 };
 
-template <int FMT>
-__device__ __forceinline__ void load_x(XSlice<FMT>& xs, const float* row, int c) {
-  constexpr int W = QTraits<FMT>::kWpc;
-  const float* p = row + W * c;
-  float s = 0.f;
+template <int FMT, int CPL, bool GATEUP>
+__device__ __forceinline__ void load_stage(Stage<FMT, CPL, GATEUP>& s, const QPlanes& p0,
+                                           const QPlanes& p1, uint32_t row, int j, int lpr) {
+  const uint32_t qo = row * p0.qrow, so = row * p0.srow;
 #pragma unroll
-  for (int i = 0; i < W / 4; ++i) {
-    const float4 a = ldf4(p + 4 * i);
-    s += (a.x + a.y) + (a.z + a.w);
-    if (FMT == kQ4_K) {
-      xs.v[4 * i + 0] = a.x;
-      xs.v[4 * i + 1] = a.y * 0.0625f;
-      xs.v[4 * i + 2] = a.z;
-      xs.v[4 * i + 3] = a.w * 0.0625f;
-    } else {
-      xs.v[4 * i + 0] = a.x;
-      xs.v[4 * i + 1] = a.y;
-      xs.v[4 * i + 2] = a.z;
-      xs.v[4 * i + 3] = a.w;
+  for (int ci = 0; ci < CPL; ++ci) {
+    load_chunk(s.c0[ci], p0, qo, so, j + lpr * ci);
+    if (GATEUP) load_chunk(s.c1[ci], p1, qo, so, j + lpr * ci);
+  }
+}
+
+template <int FMT, int CPL, int NT, bool GATEUP>
+__device__ __forceinline__ void compute_stage(const Stage<FMT, CPL, GATEUP>& s,
+                                              const XSlice<FMT> (&xs)[NT][CPL], const FfnArgs& a,
+                                              int j, int lpr, int u, bool ok,
+                                              const int (&out_row)[NT]) {
+  float acc0[NT], acc1[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc0[t] = acc1[t] = 0.f;
+#pragma unroll
+  for (int ci = 0; ci < CPL; ++ci) {
+    const int sub = (j + lpr * ci) & 7;  // Q4_K sub-block of this chunk
+    const ChunkScale k0 = decode_scale(s.c0[ci], sub);
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      acc0[t] = fmaf(k0.a, chunk_dot(s.c0[ci], xs[t][ci]), fmaf(-k0.b, xs[t][ci].sum, acc0[t]));
+    if (GATEUP) {
+      const ChunkScale k1 = decode_scale(s.c1[ci], sub);
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        acc1[t] = fmaf(k1.a, chunk_dot(s.c1[ci], xs[t][ci]), fmaf(-k1.b, xs[t][ci].sum, acc1[t]));
     }
   }
-  xs.sum = (FMT == kQ8_0) ? 128.f * s : s;
-}
-
-template <int FMT>
-__device__ __forceinline__ void zero_x(XSlice<FMT>& xs) {
 #pragma unroll
-  for (int i = 0; i < QTraits<FMT>::kWpc; ++i) xs.v[i] = 0.f;
-  xs.sum = 0.f;
-}
-
-// Scale data of a chunk, decoded once and applied to every token.
-struct ChunkScale {
-  float a;  // multiplies sum(q x)
-  float b;  // multiplies the precomputed activation sum (subtracted)
-};
-
-__device__ __forceinline__ ChunkScale decode_scale(const Chunk<kQ8_0>& ch, int /*sub*/) {
-  const float d = f16_to_f32(ch.d);
-  return {d, d};
-}
-
-__device__ __forceinline__ ChunkScale decode_scale(const Chunk<kQ4_K>& ch, int sub) {
-  const float d = f16_to_f32(ch.h.x);
-  const float dmin = f16_to_f32(ch.h.x >> 16);
-  const uint64_t lo = (uint64_t)ch.h.y | ((uint64_t)ch.h.z << 32);  // stream bits 0..63
-  const uint64_t hi = (uint64_t)ch.h.z | ((uint64_t)ch.h.w << 32);  // stream bits 32..95
-  const uint32_t sc = (uint32_t)(lo >> (6 * sub)) & 63u;
-  const uint32_t m = (uint32_t)(hi >> (16 + 6 * sub)) & 63u;
-  return {d * (float)sc, dmin * (float)m};
-}
-
-// sum over the chunk of q'_i * x_i, with q' as described above.
-__device__ __forceinline__ float chunk_dot(const Chunk<kQ8_0>& ch, const XSlice<kQ8_0>& xs) {
-  const uint32_t w[4] = {ch.q.x ^ 0x80808080u, ch.q.y ^ 0x80808080u, ch.q.z ^ 0x80808080u,
-                         ch.q.w ^ 0x80808080u};
-  float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    s0 = fmaf(ubyte_f<0>(w[k]), xs.v[4 * k + 0], s0);
-    s1 = fmaf(ubyte_f<1>(w[k]), xs.v[4 * k + 1], s1);
-    s0 = fmaf(ubyte_f<2>(w[k]), xs.v[4 * k + 2], s0);
-    s1 = fmaf(ubyte_f<3>(w[k]), xs.v[4 * k + 3], s1);
+  for (int t = 0; t < NT; ++t) {
+    const float v0 = group_sum_last(acc0[t], lpr);
+    float v = v0;
+    if (GATEUP) v = silu(v0) * group_sum_last(acc1[t], lpr);
+    if (ok && j == lpr - 1) {
+      float* dst = a.out + (int64_t)out_row[t] * a.rows_per_expert + u;
+      if (a.coherent_out)
+        store_shared(dst, v);
+      else
+        *dst = v;
+    }
   }
-  return s0 + s1;
 }
 
-__device__ __forceinline__ float chunk_dot(const Chunk<kQ4_K>& ch, const XSlice<kQ4_K>& xs) {
-  const uint32_t w[4] = {ch.q.x, ch.q.y, ch.q.z, ch.q.w};
-  float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const uint32_t lo = w[k] & 0x0F0F0F0Fu;
-    const uint32_t hi = w[k] & 0xF0F0F0F0u;
-    s0 = fmaf(ubyte_f<0>(lo), xs.v[8 * k + 0], s0);
-    s1 = fmaf(ubyte_f<0>(hi), xs.v[8 * k + 1], s1);
-    s0 = fmaf(ubyte_f<1>(lo), xs.v[8 * k + 2], s0);
-    s1 = fmaf(ubyte_f<1>(hi), xs.v[8 * k + 3], s1);
-    s0 = fmaf(ubyte_f<2>(lo), xs.v[8 * k + 4], s0);
-    s1 = fmaf(ubyte_f<2>(hi), xs.v[8 * k + 5], s1);
-    s0 = fmaf(ubyte_f<3>(lo), xs.v[8 * k + 6], s0);
-    s1 = fmaf(ubyte_f<3>(hi), xs.v[8 * k + 7], s1);
-  }
-  return s0 + s1;
-}
-
-// One pass over the workgroup's rows for NT tokens (NT <= TP).
+// One pass of a wave over rows first, first+step, ... < ue of `expert`, for
+// the NT tokens whose pair ids are given.
 template <int FMT, int CPL, int NT, bool GATEUP>
 __device__ __forceinline__ void ffn_pass(const FfnArgs& a, int expert, const int* pair_ids,
-                                         int ub, int ue) {
-  constexpr int UNR = (CPL <= 4) ? 2 : 1;  // rows in flight per wave step
+                                         int first, int step, int ue) {
+  constexpr int NST = nst_for(FMT, CPL, GATEUP);
   const int lane = threadIdx.x & (kWave - 1);
-  const int wv = threadIdx.x >> 6;
   const int lpr = a.lpr;
-  const int G = kWave / lpr;
   const int g = lane / lpr;
   const int j = lane - g * lpr;
+  if (first >= ue) return;  // wave-uniform
 
-  // Activation slices of the NT tokens.
+  const int64_t row0 = (int64_t)expert * a.rows_per_expert;
+  const QPlanes p0 = expert_planes<FMT>(a.w0, a.total_rows, a.K, row0, a.rows_per_expert);
+  const QPlanes p1 =
+      expert_planes<FMT>(GATEUP ? a.w1 : a.w0, a.total_rows, a.K, row0, a.rows_per_expert);
+
   XSlice<FMT> xs[NT][CPL];
   int out_row[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const int p = pair_ids[t];
-    const int arow = a.act_by_pair ? p : p / a.top_k;
     out_row[t] = p;
-    const float* xr = a.act + (int64_t)arow * a.K;
+    const float* xr = a.act + (int64_t)(a.act_by_pair ? p : p / a.top_k) * a.K;
 #pragma unroll
     for (int ci = 0; ci < CPL; ++ci) load_x<FMT>(xs[t][ci], xr, j + lpr * ci);
   }
 
-  const int64_t rbase = (int64_t)expert * a.rows_per_expert;
-  const int stride = 4 * G;  // rows covered by the workgroup per step
-  // The loop bound is wave-uniform (base), so every lane takes part in the
-  // group reductions; lanes whose row lies past `ue` load a valid row and
-  // skip the store.
-  for (int base = ub + wv * G; base < ue; base += stride * UNR) {
-    Chunk<FMT> c0[UNR][CPL];
-    Chunk<FMT> c1[UNR][GATEUP ? CPL : 1];
-    int urow[UNR];
+  // Row of lane group g at step base: base + g.  Bounds are wave-uniform;
+  // rows at or past `ue` are loaded (zeros past the expert) but not stored.
+  Stage<FMT, CPL, GATEUP> S[NST];
 #pragma unroll
-    for (int r = 0; r < UNR; ++r) {
-      const int u = base + g + r * stride;
-      urow[r] = u;
-      const int ul = min(u, ue - 1);  // keep loads in bounds for idle lanes
-      const int64_t row = rbase + ul;
+  for (int s = 0; s < NST - 1; ++s)
+    if (first + s * step < ue) load_stage(S[s], p0, p1, (uint32_t)(first + s * step + g), j, lpr);
+  for (int base = first; base < ue; base += NST * step) {
 #pragma unroll
-      for (int ci = 0; ci < CPL; ++ci) {
-        load_chunk<FMT>(c0[r][ci], a.w0, a.total_rows, a.K, row, j + lpr * ci);
-        if (GATEUP) load_chunk<FMT>(c1[r][ci], a.w1, a.total_rows, a.K, row, j + lpr * ci);
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < UNR; ++r) {
-      float acc0[NT], acc1[NT];
-#pragma unroll
-      for (int t = 0; t < NT; ++t) acc0[t] = acc1[t] = 0.f;
-#pragma unroll
-      for (int ci = 0; ci < CPL; ++ci) {
-        const int s = (j + lpr * ci) & 7;  // Q4_K sub-block of this chunk
-        const ChunkScale k0 = decode_scale(c0[r][ci], s);
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          const float dsum = chunk_dot(c0[r][ci], xs[t][ci]);
-          acc0[t] = fmaf(k0.a, dsum, fmaf(-k0.b, xs[t][ci].sum, acc0[t]));
-        }
-        if (GATEUP) {
-          const ChunkScale k1 = decode_scale(c1[r][ci], s);
-#pragma unroll
-          for (int t = 0; t < NT; ++t) {
-            const float dsum = chunk_dot(c1[r][ci], xs[t][ci]);
-            acc1[t] = fmaf(k1.a, dsum, fmaf(-k1.b, xs[t][ci].sum, acc1[t]));
-          }
-        }
-      }
-      const bool ok = urow[r] < ue;
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const float v0 = group_sum(acc0[t], lpr);
-        if (GATEUP) {
-          const float v1 = group_sum(acc1[t], lpr);
-          if (ok && j == 0)
-            a.out[(int64_t)out_row[t] * a.rows_per_expert + urow[r]] = silu(v0) * v1;
-        } else {
-          if (ok && j == 0) a.out[(int64_t)out_row[t] * a.rows_per_expert + urow[r]] = v0;
-        }
-      }
+    for (int s = 0; s < NST; ++s) {
+      const int cur = base + s * step;
+      if (cur >= ue) break;
+      const int pre = cur + (NST - 1) * step;
+      if (pre < ue) load_stage(S[(s + NST - 1) % NST], p0, p1, (uint32_t)(pre + g), j, lpr);
+      compute_stage<FMT, CPL, NT, GATEUP>(S[s], xs, a, j, lpr, cur + g, cur + g < ue, out_row);
     }
   }
 }
 
-// Grid: (row tiles, expert slots).  A workgroup serves rows
-// [blockIdx.x * units_per_block, ...) of the expert in slot blockIdx.y for
-// every token routed to it, TP tokens per pass.
 template <int FMT, int CPL, int TP, bool GATEUP>
-__global__ __launch_bounds__(kBlock) void k_ffn(FfnArgs a) {
-  const int slot = blockIdx.y;
+__device__ __forceinline__ void ffn_pass_nt(const FfnArgs& a, int expert, const int* ids, int nt,
+                                            int first, int step, int ue) {
+  if (nt >= TP) {
+    ffn_pass<FMT, CPL, TP, GATEUP>(a, expert, ids, first, step, ue);
+  } else if (TP > 1 && nt == 1) {
+    ffn_pass<FMT, CPL, 1, GATEUP>(a, expert, ids, first, step, ue);
+  } else if (TP > 2 && nt == 2) {
+    ffn_pass<FMT, CPL, (TP > 2 ? 2 : 1), GATEUP>(a, expert, ids, first, step, ue);
+  } else if (TP > 3 && nt == 3) {
+    ffn_pass<FMT, CPL, (TP > 3 ? 3 : 1), GATEUP>(a, expert, ids, first, step, ue);
+  }
+}
+
+// Work of workgroup (tile, slot): rows [tile * units_per_block, ...) of the
+// expert in `slot`, for every token routed to it.
+template <int FMT, int CPL, bool GATEUP>
+__device__ __forceinline__ void ffn_tile(const FfnArgs& a, int slot, int tile) {
+  constexpr int TP = tp_for(FMT, CPL);
+  const int ub = tile * a.units_per_block;
+  if (a.pair_expert) {
+    // One (token, slot) pair per slot: every workgroup does the same work.
+    if (slot >= a.n_pairs) return;
+    const int ue = min(ub + a.units_per_block, a.rows_per_expert);
+    if (ub >= ue) return;
+    const int G = kWave / a.lpr;
+    const int ids1[1] = {slot};
+    ffn_pass<FMT, CPL, 1, GATEUP>(a, a.pair_expert[slot], ids1, ub + (threadIdx.x >> 6) * G,
+                                  kWavesPerBlock * G, ue);
+    return;
+  }
   if (a.n_active && slot >= *a.n_active) return;
   const int expert = a.active ? a.active[slot] : 0;
   const int begin = a.offsets ? a.offsets[expert] : 0;
   const int count = a.offsets ? a.offsets[expert + 1] - begin : a.n_tokens;
-  const int ub = blockIdx.x * a.units_per_block;
   const int ue = min(ub + a.units_per_block, a.rows_per_expert);
-  if (ub >= ue) return;
-  for (int p0 = 0; p0 < count; p0 += TP) {
-    int ids[TP];
+  if (ub >= ue || count <= 0) return;
+  const int wv = threadIdx.x >> 6;
+  const int G = kWave / a.lpr;
+  int ids[TP];
+  if (a.split_tokens) {
+    // Wave wv takes passes wv, wv + 4, ... over all rows of the tile.
+    for (int p0 = wv * TP; p0 < count; p0 += kWavesPerBlock * TP) {
 #pragma unroll
-    for (int t = 0; t < TP; ++t) {
-      const int q = min(p0 + t, count - 1);
-      ids[t] = a.slots ? a.slots[begin + q] : q;
+      for (int t = 0; t < TP; ++t) {
+        const int q = min(p0 + t, count - 1);
+        ids[t] = a.slots ? a.slots[begin + q] : q;
+      }
+      ffn_pass_nt<FMT, CPL, TP, GATEUP>(a, expert, ids, min(TP, count - p0), ub, G, ue);
     }
-    const int nt = min(TP, count - p0);
-    if (nt >= TP) {
-      ffn_pass<FMT, CPL, TP, GATEUP>(a, expert, ids, ub, ue);
-    } else if (TP > 1 && nt == 1) {
-      ffn_pass<FMT, CPL, 1, GATEUP>(a, expert, ids, ub, ue);
-    } else if (TP > 2 && nt == 2) {
-      ffn_pass<FMT, CPL, (TP > 2 ? 2 : 1), GATEUP>(a, expert, ids, ub, ue);
-    } else if (TP > 3 && nt == 3) {
-      ffn_pass<FMT, CPL, (TP > 3 ? 3 : 1), GATEUP>(a, expert, ids, ub, ue);
+  } else {
+    for (int p0 = 0; p0 < count; p0 += TP) {
+#pragma unroll
+      for (int t = 0; t < TP; ++t) {
+        const int q = min(p0 + t, count - 1);
+        ids[t] = a.slots ? a.slots[begin + q] : q;
+      }
+      ffn_pass_nt<FMT, CPL, TP, GATEUP>(a, expert, ids, min(TP, count - p0), ub + wv * G,
+                                        kWavesPerBlock * G, ue);
     }
   }
+}
+
+// Grid: (row tiles, expert slots).
+template <int FMT, int CPL, bool GATEUP>
+__global__ __launch_bounds__(kBlock) void k_ffn(FfnArgs a) {
+  ffn_tile<FMT, CPL, GATEUP>(a, blockIdx.y, blockIdx.x);
 }
 
 }  // namespace svr

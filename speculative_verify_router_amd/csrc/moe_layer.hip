@@ -1,41 +1,41 @@
 // C-ABI entry points of the routed-MoE verify layer (declared in
 // include/moe_layer.h): argument validation, workspace layout, kernel
 // selection and the launch sequence on the caller's HIP stream.
+//
+// Launch sequence (three stages, each one launch on the fast path):
+//   1 route_shared_gateup  router GEMV + shared gate/up; last router
+//                          workgroup: top-k, weights, bucketing
+//   2 gateup               routed gate/up + SwiGLU, shared down
+//   3 down_combine         routed down; last workgroup per row tile combines
+// Shapes outside the fused instantiations, and batches above 16 tokens,
+// take the same steps as separate launches.
 #include <hip/hip_runtime.h>
-
-#include <cstring>
 
 #include "common.h"
 #include "ffn.h"
 #include "misc.h"
+#include "phases.h"
 #include "route.h"
 
 using namespace svr;
 
 namespace {
 
-constexpr int kVersion = 100;  // 0.1.0
+constexpr int kVersion = 200;  // 0.2.0
+constexpr int kFusedMaxTokens = 16;
+// Batches up to this size give every (token, slot) pair its own workgroups
+// (equal work per workgroup); larger ones go by expert with token passes.
+constexpr int kPairSlotTokens = 4;
 
-enum Stage {
-  kStRouter = 0,
-  kStTopk,
-  kStBucket,
-  kStSharedGateUp,
-  kStRoutedGateUp,
-  kStSharedDown,
-  kStRoutedDown,
-  kStCombine,
-  kNumStages
-};
-const char* const kStageNames[kNumStages] = {"router_logits", "topk",        "bucket",
-                                             "shared_gateup", "routed_gateup", "shared_down",
-                                             "routed_down",   "combine"};
+enum Stage { kStPhase1 = 0, kStPhase2, kStPhase3, kNumStages };
+const char* const kStageNames[kNumStages] = {"route_shared_gateup", "gateup", "down_combine"};
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 int wpc_of(int dtype) { return dtype == MOE_Q8_0 ? 16 : 32; }
 int blk_of(int dtype) { return dtype == MOE_Q8_0 ? 32 : 256; }
 bool quant_type(int dtype) { return dtype == MOE_Q8_0 || dtype == MOE_Q4_K; }
+int qfmt(int dtype) { return dtype == MOE_Q8_0 ? kQ8_0 : kQ4_K; }
 
 // Lanes per row and 16-byte chunks per lane for a row of K columns.
 struct FfnShape {
@@ -54,16 +54,9 @@ bool ffn_shape(int dtype, int K, FfnShape* s) {
   return false;
 }
 
-// Tokens per pass: as many as keep the per-lane activation slice within 64
-// floats (at a verify batch an expert serves about one token, so VGPRs go
-// to loads in flight rather than to idle token slots).
-constexpr int tp_for(int fmt, int cpl) {
-  return (cpl * (fmt == kQ8_0 ? 16 : 32) <= 16) ? 4 : (cpl * (fmt == kQ8_0 ? 16 : 32) <= 32) ? 2 : 1;
-}
-
 struct Plan {
   int H, E, k, F, Fs, et, st, M;
-  size_t logits, ids, w, counts, offsets, slots, active, nactive, h, hs, o, s, total;
+  size_t ctr, logits, ids, w, counts, offsets, slots, active, nactive, h, hs, o, s, total;
 };
 
 int check_desc(const moe_layer_desc* d) {
@@ -102,6 +95,7 @@ int make_plan(const moe_layer_desc* d, int M, Plan* p) {
     off = align256(off + bytes);
     return o;
   };
+  p->ctr = take(sizeof(Counters));
   p->logits = take(Mz * p->E * 4);
   p->ids = take(P * 4);
   p->w = take(P * 4);
@@ -118,44 +112,190 @@ int make_plan(const moe_layer_desc* d, int M, Plan* p) {
   return MOE_OK;
 }
 
-template <int FMT, int CPL, bool GU>
-void launch_ffn_t(dim3 grid, hipStream_t st, const FfnArgs& a) {
-  hipLaunchKernelGGL((k_ffn<FMT, CPL, tp_for(FMT, CPL), GU>), grid, dim3(kBlock), 0, st, a);
+// --------------------------------------------------------------------------
+// Work split.  Every launch is sized to about one round of resident
+// workgroups (CUs x workgroups per CU for that kernel), since a partial
+// second round costs a whole extra pass of latency.  A role's rows are cut
+// into tiles of a whole number of wave steps.
+// --------------------------------------------------------------------------
+int device_cus() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (!cache[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
 }
 
+template <typename K>
+int resident_blocks(K kernel) {
+  static int per_cu = 0;  // one value per kernel instantiation
+  if (!per_cu) {
+    int v = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, kernel, kBlock, 0) != hipSuccess || v < 1)
+      v = 1;
+    per_cu = v;
+  }
+  return per_cu * device_cus();
+}
+
+// Rows per workgroup for `blocks` workgroups over `slots` experts.
+void size_role(FfnArgs& a, int dtype, int slots, int64_t blocks) {
+  FfnShape s;
+  ffn_shape(dtype, a.K, &s);
+  a.lpr = s.lpr;
+  const int G = kWave / s.lpr;  // rows per wave step
+  const int unit_step = a.split_tokens ? G : kWavesPerBlock * G;
+  int64_t tiles = blocks / (slots > 0 ? slots : 1);
+  // Workgroups go to the 8 XCDs round-robin by linear index (tile fastest):
+  // with a multiple of 8 tiles, every slot's tile t runs on XCD t % 8, so
+  // slots that stream the same expert share that XCD's L2.  Rounded down
+  // only where that leaves at most 1/8 of the round idle.
+  if (tiles >= 8 && tiles % 8 <= tiles / 8) tiles -= tiles % 8;
+  if (tiles < 1) tiles = 1;
+  int64_t upb = (a.rows_per_expert + tiles - 1) / tiles;
+  upb = (upb + unit_step - 1) / unit_step * unit_step;
+  a.units_per_block = (int)upb;
+}
+
+int tiles_of(const FfnArgs& a) {
+  return (a.rows_per_expert + a.units_per_block - 1) / a.units_per_block;
+}
+
+// Bytes per weight row of K columns.
+double row_bytes(int dtype, int K) { return dtype == MOE_Q8_0 ? K / 32 * 34.0 : K / 256 * 144.0; }
+
+// Single-role launches, every (format, chunks-per-lane) pair.
 template <int FMT, bool GU>
-bool launch_ffn_c(int cpl, dim3 grid, hipStream_t st, const FfnArgs& a) {
+bool launch_ffn_c(int cpl, FfnArgs a, int dtype, int slots, hipStream_t st) {
   switch (cpl) {
-    case 1: launch_ffn_t<FMT, 1, GU>(grid, st, a); return true;
-    case 2: launch_ffn_t<FMT, 2, GU>(grid, st, a); return true;
-    case 3: launch_ffn_t<FMT, 3, GU>(grid, st, a); return true;
-    case 4: launch_ffn_t<FMT, 4, GU>(grid, st, a); return true;
-    case 5: launch_ffn_t<FMT, 5, GU>(grid, st, a); return true;
-    case 6: launch_ffn_t<FMT, 6, GU>(grid, st, a); return true;
-    case 7: launch_ffn_t<FMT, 7, GU>(grid, st, a); return true;
-    case 8: launch_ffn_t<FMT, 8, GU>(grid, st, a); return true;
+#define SVR_CASE(C)                                                                   \
+  case C: {                                                                           \
+    auto k = k_ffn<FMT, C, GU>;                                                       \
+    size_role(a, dtype, slots, resident_blocks(k));                                   \
+    hipLaunchKernelGGL(k, dim3(tiles_of(a), slots), dim3(kBlock), 0, st, a);          \
+    return true;                                                                      \
+  }
+    SVR_CASE(1) SVR_CASE(2) SVR_CASE(3) SVR_CASE(4) SVR_CASE(5) SVR_CASE(6) SVR_CASE(7) SVR_CASE(8)
+#undef SVR_CASE
     default: return false;
   }
 }
 
-// Launches one FFN role over `slots_max` expert slots.
 bool launch_ffn(int dtype, bool gateup, FfnArgs a, int slots_max, hipStream_t st) {
   FfnShape s;
-  if (!ffn_shape(dtype, a.K, &s)) return false;
-  a.lpr = s.lpr;
-  const int G = kWave / s.lpr;
-  const int unit_step = 4 * G;  // rows a workgroup covers per step
-  const int64_t total_units = (int64_t)a.rows_per_expert * slots_max;
-  const int64_t target_blocks = 1024;
-  int64_t steps = (total_units + unit_step * target_blocks - 1) / (unit_step * target_blocks);
-  steps = steps < 4 ? 4 : (steps > 16 ? 16 : steps);
-  a.units_per_block = (int)(unit_step * steps);
-  dim3 grid((a.rows_per_expert + a.units_per_block - 1) / a.units_per_block, slots_max);
+  ffn_shape(dtype, a.K, &s);
   if (dtype == MOE_Q8_0)
-    return gateup ? launch_ffn_c<kQ8_0, true>(s.cpl, grid, st, a)
-                  : launch_ffn_c<kQ8_0, false>(s.cpl, grid, st, a);
-  return gateup ? launch_ffn_c<kQ4_K, true>(s.cpl, grid, st, a)
-                : launch_ffn_c<kQ4_K, false>(s.cpl, grid, st, a);
+    return gateup ? launch_ffn_c<kQ8_0, true>(s.cpl, a, dtype, slots_max, st)
+                  : launch_ffn_c<kQ8_0, false>(s.cpl, a, dtype, slots_max, st);
+  return gateup ? launch_ffn_c<kQ4_K, true>(s.cpl, a, dtype, slots_max, st)
+                : launch_ffn_c<kQ4_K, false>(s.cpl, a, dtype, slots_max, st);
+}
+
+// Fused instantiations.  A key packs (format, chunks per lane).
+constexpr int key(int fmt, int cpl) { return fmt * 16 + cpl; }
+
+// Phase 1: router rows (NC float4 per lane) + shared gate/up.  The shared
+// tiles get the residency the E router workgroups leave free (at least half).
+template <int NC>
+bool launch_phase1_nc(int skey, hipStream_t st, const RouteArgs& r, FfnArgs s, int sdtype) {
+  switch (skey) {
+#define SVR_P1(F, C)                                                                     \
+  case key(F, C): {                                                                      \
+    auto k = k_phase1<NC, F, C>;                                                         \
+    const int64_t cap = resident_blocks(k);                                              \
+    size_role(s, sdtype, 1, cap - r.n_router_blocks > cap / 2 ? cap - r.n_router_blocks : cap / 2); \
+    hipLaunchKernelGGL(k, dim3(r.n_router_blocks + tiles_of(s)), dim3(kBlock), 0, st, r, s); \
+    return true;                                                                         \
+  }
+    case 0:
+      hipLaunchKernelGGL((k_phase1<NC, 0, 1>), dim3(r.n_router_blocks), dim3(kBlock), 0, st, r, s);
+      return true;
+    SVR_P1(kQ8_0, 1) SVR_P1(kQ8_0, 2) SVR_P1(kQ8_0, 4) SVR_P1(kQ4_K, 1) SVR_P1(kQ4_K, 2)
+#undef SVR_P1
+    default: return false;
+  }
+}
+
+// NC: float4 chunks per lane in a quarter row (H/16 chunks per quarter).
+bool launch_phase1(int H, int skey, hipStream_t st, const RouteArgs& r, const FfnArgs& s,
+                   int sdtype) {
+  if (H <= 1024) return launch_phase1_nc<1>(skey, st, r, s, sdtype);
+  if (H <= 2048) return launch_phase1_nc<2>(skey, st, r, s, sdtype);
+  if (H <= 4096) return launch_phase1_nc<4>(skey, st, r, s, sdtype);
+  if (H <= 8192) return launch_phase1_nc<8>(skey, st, r, s, sdtype);
+  return false;
+}
+
+// Phase 2: routed gate/up (A) + shared down (B) in one grid.  The resident
+// round is split in proportion to the bytes each side's waves stream: the
+// shared side's waves each take one token over the same rows.
+struct DualPlan {
+  int64_t a_work, b_work;  // bytes streamed by all waves of each side
+  int slots;               // routed expert slots
+  int adtype, bdtype;
+};
+
+template <int FA, int CA, int FB, int CB>
+void launch_dual_t(hipStream_t st, FfnArgs a, FfnArgs b, const DualPlan& d) {
+  auto k = k_dual<FA, CA, true, FB, CB, false>;
+  const int64_t cap = resident_blocks(k);
+  int64_t bb = (int64_t)((double)cap * d.b_work / (double)(d.a_work + d.b_work) + 0.5);
+  if (bb < 1) bb = 1;
+  if (bb > cap / 2) bb = cap / 2;
+  size_role(a, d.adtype, d.slots, cap - bb);
+  size_role(b, d.bdtype, 1, bb);
+  const int at = tiles_of(a), na = at * d.slots;
+  hipLaunchKernelGGL(k, dim3(na + tiles_of(b)), dim3(kBlock), 0, st, a, at, na, b);
+}
+
+template <int FA, int CA>
+bool launch_dual_b(int bkey, hipStream_t st, const FfnArgs& a, const FfnArgs& b,
+                   const DualPlan& d) {
+  switch (bkey) {
+#define SVR_D(F, C) \
+  case key(F, C): launch_dual_t<FA, CA, F, C>(st, a, b, d); return true;
+    SVR_D(kQ8_0, 1) SVR_D(kQ8_0, 2) SVR_D(kQ8_0, 3) SVR_D(kQ8_0, 4) SVR_D(kQ8_0, 5)
+#undef SVR_D
+    default: return false;
+  }
+}
+
+bool launch_dual(int akey, int bkey, hipStream_t st, const FfnArgs& a, const FfnArgs& b,
+                 const DualPlan& d) {
+  switch (akey) {
+    case key(kQ4_K, 1): return launch_dual_b<kQ4_K, 1>(bkey, st, a, b, d);
+    case key(kQ4_K, 2): return launch_dual_b<kQ4_K, 2>(bkey, st, a, b, d);
+    case key(kQ8_0, 2): return launch_dual_b<kQ8_0, 2>(bkey, st, a, b, d);
+    case key(kQ8_0, 4): return launch_dual_b<kQ8_0, 4>(bkey, st, a, b, d);
+    default: return false;
+  }
+}
+
+// Phase 3: routed down + combine, one resident round of row tiles x slots.
+template <int F, int C>
+bool launch_down_combine_t(hipStream_t st, FfnArgs a, const CombineArgs& c, int dtype, int slots) {
+  auto k = k_down_combine<F, C>;
+  size_role(a, dtype, slots, resident_blocks(k));
+  const int tiles = tiles_of(a);
+  if (tiles > kMaxTiles) return false;
+  hipLaunchKernelGGL(k, dim3(tiles, slots), dim3(kBlock), 0, st, a, c);
+  return true;
+}
+
+bool launch_down_combine(int fmt, int cpl, hipStream_t st, const FfnArgs& a, const CombineArgs& c,
+                         int dtype, int slots) {
+#define SVR_DC(F, C) \
+  if (fmt == F && cpl == C) return launch_down_combine_t<F, C>(st, a, c, dtype, slots);
+  SVR_DC(kQ4_K, 1) SVR_DC(kQ4_K, 2) SVR_DC(kQ4_K, 3) SVR_DC(kQ4_K, 4) SVR_DC(kQ4_K, 5)
+  SVR_DC(kQ4_K, 6) SVR_DC(kQ8_0, 1) SVR_DC(kQ8_0, 2) SVR_DC(kQ8_0, 3) SVR_DC(kQ8_0, 4)
+  SVR_DC(kQ8_0, 5) SVR_DC(kQ8_0, 6)
+#undef SVR_DC
+  return false;
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -163,26 +303,109 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 // Records stage event i if the caller asked for events; a failure shows up
 // in the final hipGetLastError check.
 inline void mark(hipEvent_t* ev, int i, hipStream_t st) {
-  if (ev) (void)hipEventRecord(ev[i], st);
+  if (ev && ev[i]) (void)hipEventRecord(ev[i], st);
 }
 
-struct Routing {
+struct Buffers {
+  Counters* ctr;
+  float *logits, *w, *h, *hs, *o, *s;
   int32_t *ids, *counts, *offsets, *slots, *active, *nactive;
-  float *w, *logits;
 };
 
-void enqueue_route(const Plan& p, const float* router, const float* x, const Routing& r,
-                   hipStream_t st, hipEvent_t* ev) {
-  const int wpb = kBlock / kWave;
-  mark(ev, kStRouter, st);
-  hipLaunchKernelGGL(k_router_logits, dim3((p.E + wpb - 1) / wpb), dim3(kBlock), 0, st, router, x,
-                     r.logits, p.H, p.E, p.M);
-  mark(ev, kStTopk, st);
-  hipLaunchKernelGGL(k_topk, dim3((p.M + wpb - 1) / wpb), dim3(kBlock), 0, st, r.logits, r.ids,
-                     r.w, p.E, p.k, p.M);
-  mark(ev, kStBucket, st);
-  hipLaunchKernelGGL(k_bucket, dim3(1), dim3(kBlock), 0, st, r.ids, p.M * p.k, p.E, r.counts,
-                     r.offsets, r.slots, r.active, r.nactive);
+Buffers carve(const Plan& p, void* ws, int32_t* ids, float* w) {
+  uint8_t* b = (uint8_t*)ws;
+  Buffers r;
+  r.ctr = (Counters*)(b + p.ctr);
+  r.logits = (float*)(b + p.logits);
+  r.ids = ids ? ids : (int32_t*)(b + p.ids);
+  r.w = w ? w : (float*)(b + p.w);
+  r.counts = (int32_t*)(b + p.counts);
+  r.offsets = (int32_t*)(b + p.offsets);
+  r.slots = (int32_t*)(b + p.slots);
+  r.active = (int32_t*)(b + p.active);
+  r.nactive = (int32_t*)(b + p.nactive);
+  r.h = (float*)(b + p.h);
+  r.hs = (float*)(b + p.hs);
+  r.o = (float*)(b + p.o);
+  r.s = (float*)(b + p.s);
+  return r;
+}
+
+// Router + top-k + bucketing as three launches (any batch size).
+void enqueue_route_plain(const Plan& p, const float* router, const float* x, const Buffers& b,
+                         const BucketOut& bo, hipStream_t st) {
+  hipLaunchKernelGGL(k_router_logits, dim3((p.E + kWavesPerBlock - 1) / kWavesPerBlock),
+                     dim3(kBlock), 0, st, router, x, b.logits, p.H, p.E, p.M);
+  hipLaunchKernelGGL(k_topk, dim3((p.M + kWavesPerBlock - 1) / kWavesPerBlock), dim3(kBlock), 0,
+                     st, b.logits, b.ids, b.w, p.E, p.k, p.M);
+  hipLaunchKernelGGL(k_bucket, dim3(1), dim3(kBlock), 0, st, b.ids, p.M * p.k, p.E, bo);
+}
+
+FfnArgs shared_gateup_args(const Plan& p, const moe_layer_weights* wt, const float* x,
+                           const Buffers& b) {
+  FfnArgs a{};
+  a.w0 = (const uint8_t*)wt->shared_gate;
+  a.w1 = (const uint8_t*)wt->shared_up;
+  a.total_rows = p.Fs;
+  a.rows_per_expert = p.Fs;
+  a.K = p.H;
+  a.n_tokens = p.M;
+  a.top_k = 1;
+  a.act = x;
+  a.act_by_pair = 0;
+  a.out = b.hs;
+  a.split_tokens = 1;
+  return a;
+}
+
+FfnArgs shared_down_args(const Plan& p, const moe_layer_weights* wt, const Buffers& b) {
+  FfnArgs a{};
+  a.w0 = (const uint8_t*)wt->shared_down;
+  a.total_rows = p.H;
+  a.rows_per_expert = p.H;
+  a.K = p.Fs;
+  a.n_tokens = p.M;
+  a.top_k = 1;
+  a.act = b.hs;
+  a.act_by_pair = 1;
+  a.out = b.s;
+  a.split_tokens = 1;
+  return a;
+}
+
+FfnArgs routed_args(const Plan& p, const Buffers& b, bool gateup, const moe_layer_weights* wt,
+                    const float* x, bool pairs) {
+  FfnArgs a{};
+  if (pairs) {
+    a.pair_expert = b.ids;
+    a.n_pairs = p.M * p.k;
+  } else {
+    a.active = b.active;
+    a.n_active = b.nactive;
+    a.offsets = b.offsets;
+    a.slots = b.slots;
+  }
+  a.top_k = p.k;
+  a.split_tokens = 0;
+  if (gateup) {
+    a.w0 = (const uint8_t*)wt->gate;
+    a.w1 = (const uint8_t*)wt->up;
+    a.total_rows = (int64_t)p.E * p.F;
+    a.rows_per_expert = p.F;
+    a.K = p.H;
+    a.act = x;
+    a.act_by_pair = 0;
+    a.out = b.h;
+  } else {
+    a.w0 = (const uint8_t*)wt->down;
+    a.total_rows = (int64_t)p.E * p.H;
+    a.rows_per_expert = p.H;
+    a.K = p.F;
+    a.act = b.h;
+    a.act_by_pair = 1;
+    a.out = b.o;
+  }
+  return a;
 }
 
 int forward_impl(const moe_layer_desc* desc, const moe_layer_weights* wt, const float* x,
@@ -196,8 +419,7 @@ int forward_impl(const moe_layer_desc* desc, const moe_layer_weights* wt, const 
   hipStream_t st = (hipStream_t)hip_stream;
   hipEvent_t* ev = events ? (hipEvent_t*)events : nullptr;
   if (n_tokens == 0) {
-    if (ev)
-      for (int i = 0; i <= kNumStages; ++i) mark(ev, i, st);
+    for (int i = 0; i <= kNumStages; ++i) mark(ev, i, st);
     return MOE_OK;
   }
   if (!x || !y || !wt->router || !wt->gate || !wt->up || !wt->down) return MOE_ERR_NULL;
@@ -211,100 +433,79 @@ int forward_impl(const moe_layer_desc* desc, const moe_layer_weights* wt, const 
                    !aligned(wt->shared_down, 16)))
     return MOE_ERR_ARG;
 
-  uint8_t* ws = (uint8_t*)workspace;
-  Routing r;
-  r.logits = (float*)(ws + p.logits);
-  r.ids = topk_ids ? topk_ids : (int32_t*)(ws + p.ids);
-  r.w = topk_w ? topk_w : (float*)(ws + p.w);
-  r.counts = (int32_t*)(ws + p.counts);
-  r.offsets = (int32_t*)(ws + p.offsets);
-  r.slots = (int32_t*)(ws + p.slots);
-  r.active = (int32_t*)(ws + p.active);
-  r.nactive = (int32_t*)(ws + p.nactive);
-  float* h = (float*)(ws + p.h);
-  float* hs = (float*)(ws + p.hs);
-  float* o = (float*)(ws + p.o);
-  float* s = (float*)(ws + p.s);
-
+  const Buffers b = carve(p, workspace, topk_ids, topk_w);
+  const BucketOut bo{b.counts, b.offsets, b.slots, b.active, b.nactive};
+  const bool pairs = p.M <= kPairSlotTokens;
+  const int slots_max = pairs ? p.M * p.k : ((p.M * p.k < p.E) ? p.M * p.k : p.E);
+  const bool shared = p.Fs > 0;
   (void)hipGetLastError();  // clear a stale error from earlier, unrelated calls
-  enqueue_route(p, wt->router, x, r, st, ev);
 
-  const int slots_max = (p.M * p.k < p.E) ? p.M * p.k : p.E;
+  // ---- stage 1: routing and shared gate/up
+  mark(ev, kStPhase1, st);
+  FfnArgs sgu{};
+  FfnShape ss{};
+  if (shared) {
+    sgu = shared_gateup_args(p, wt, x, b);
+    ffn_shape(p.st, p.H, &ss);
+  }
+  bool fused1 = false;
+  if (p.M <= kFusedMaxTokens) {
+    RouteArgs r{wt->router, x, b.logits, b.ids, b.w, bo, p.H, p.E, p.k, p.M, p.E, b.ctr, !pairs};
+    const int skey = shared ? key(qfmt(p.st), ss.cpl) : 0;
+    fused1 = launch_phase1(p.H, skey, st, r, sgu, p.st);
+    if (!fused1 && shared) {
+      // No fused instantiation for this shared shape: route alone, then the
+      // shared gate/up as its own launch.
+      fused1 = launch_phase1(p.H, 0, st, r, sgu, p.st);
+      if (fused1 && !launch_ffn(p.st, true, sgu, 1, st)) return MOE_ERR_SHAPE;
+    }
+  }
+  if (!fused1) {
+    enqueue_route_plain(p, wt->router, x, b, bo, st);
+    if (shared && !launch_ffn(p.st, true, sgu, 1, st)) return MOE_ERR_SHAPE;
+  }
 
-  // Shared expert gate/up + SwiGLU (identity token list).
-  mark(ev, kStSharedGateUp, st);
-  if (p.Fs > 0) {
-    FfnArgs a{};
-    a.w0 = (const uint8_t*)wt->shared_gate;
-    a.w1 = (const uint8_t*)wt->shared_up;
-    a.total_rows = p.Fs;
-    a.rows_per_expert = p.Fs;
-    a.K = p.H;
-    a.n_tokens = p.M;
-    a.top_k = 1;
-    a.act = x;
-    a.act_by_pair = 0;
-    a.out = hs;
-    if (!launch_ffn(p.st, true, a, 1, st)) return MOE_ERR_SHAPE;
-  }
-  // Routed gate/up + SwiGLU: h[pair][F].
-  mark(ev, kStRoutedGateUp, st);
+  // ---- stage 2: routed gate/up (+ shared down)
+  mark(ev, kStPhase2, st);
   {
-    FfnArgs a{};
-    a.w0 = (const uint8_t*)wt->gate;
-    a.w1 = (const uint8_t*)wt->up;
-    a.total_rows = (int64_t)p.E * p.F;
-    a.rows_per_expert = p.F;
-    a.K = p.H;
-    a.active = r.active;
-    a.n_active = r.nactive;
-    a.offsets = r.offsets;
-    a.slots = r.slots;
-    a.top_k = p.k;
-    a.act = x;
-    a.act_by_pair = 0;
-    a.out = h;
-    if (!launch_ffn(p.et, true, a, slots_max, st)) return MOE_ERR_SHAPE;
+    FfnArgs rgu = routed_args(p, b, true, wt, x, pairs);
+    bool done = false;
+    if (shared) {
+      FfnArgs sd = shared_down_args(p, wt, b);
+      FfnShape rs, ds;
+      ffn_shape(p.et, p.H, &rs);
+      ffn_shape(p.st, p.Fs, &ds);
+      DualPlan dp;
+      dp.a_work = (int64_t)(row_bytes(p.et, p.H) * 2 * p.F * slots_max);
+      dp.b_work = (int64_t)(row_bytes(p.st, p.Fs) * p.H * (p.M < kWavesPerBlock ? p.M : kWavesPerBlock));
+      dp.slots = slots_max;
+      dp.adtype = p.et;
+      dp.bdtype = p.st;
+      done = launch_dual(key(qfmt(p.et), rs.cpl), key(qfmt(p.st), ds.cpl), st, rgu, sd, dp);
+      if (!done) {
+        if (!launch_ffn(p.et, true, rgu, slots_max, st)) return MOE_ERR_SHAPE;
+        if (!launch_ffn(p.st, false, sd, 1, st)) return MOE_ERR_SHAPE;
+        done = true;
+      }
+    }
+    if (!done && !launch_ffn(p.et, true, rgu, slots_max, st)) return MOE_ERR_SHAPE;
   }
-  // Shared down: s[t][H].
-  mark(ev, kStSharedDown, st);
-  if (p.Fs > 0) {
-    FfnArgs a{};
-    a.w0 = (const uint8_t*)wt->shared_down;
-    a.total_rows = p.H;
-    a.rows_per_expert = p.H;
-    a.K = p.Fs;
-    a.n_tokens = p.M;
-    a.top_k = 1;
-    a.act = hs;
-    a.act_by_pair = 1;
-    a.out = s;
-    if (!launch_ffn(p.st, false, a, 1, st)) return MOE_ERR_SHAPE;
-  }
-  // Routed down: o[pair][H].
-  mark(ev, kStRoutedDown, st);
+
+  // ---- stage 3: routed down + combine
+  mark(ev, kStPhase3, st);
   {
-    FfnArgs a{};
-    a.w0 = (const uint8_t*)wt->down;
-    a.total_rows = (int64_t)p.E * p.H;
-    a.rows_per_expert = p.H;
-    a.K = p.F;
-    a.active = r.active;
-    a.n_active = r.nactive;
-    a.offsets = r.offsets;
-    a.slots = r.slots;
-    a.top_k = p.k;
-    a.act = h;
-    a.act_by_pair = 1;
-    a.out = o;
-    if (!launch_ffn(p.et, false, a, slots_max, st)) return MOE_ERR_SHAPE;
-  }
-  // Combine.
-  mark(ev, kStCombine, st);
-  {
-    const int64_t n4 = (int64_t)p.M * (p.H / 4);
-    hipLaunchKernelGGL(k_combine, dim3((unsigned)((n4 + kBlock - 1) / kBlock)), dim3(kBlock), 0, st,
-                       o, p.Fs > 0 ? s : nullptr, r.w, y, p.M, p.H, p.k);
+    FfnArgs rd = routed_args(p, b, false, wt, x, pairs);
+    rd.coherent_out = 1;  // the last workgroup of each row tile reads them
+    FfnShape ds;
+    ffn_shape(p.et, p.F, &ds);
+    CombineArgs c{b.o, shared ? b.s : nullptr, b.w, y, p.M, p.H, p.k, b.ctr};
+    if (!launch_down_combine(qfmt(p.et), ds.cpl, st, rd, c, p.et, slots_max)) {
+      rd.coherent_out = 0;
+      if (!launch_ffn(p.et, false, rd, slots_max, st)) return MOE_ERR_SHAPE;
+      const int64_t n4 = (int64_t)p.M * (p.H / 4);
+      hipLaunchKernelGGL(k_combine, dim3((unsigned)((n4 + kBlock - 1) / kBlock)), dim3(kBlock), 0,
+                         st, b.o, shared ? b.s : nullptr, b.w, y, p.M, p.H, p.k);
+    }
   }
   mark(ev, kNumStages, st);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
@@ -373,18 +574,10 @@ int32_t moe_route(const moe_layer_desc* desc, const float* router, const float* 
   if (workspace_bytes < p.total) return MOE_ERR_WORKSPACE;
   if (!aligned(workspace, 256) || !aligned(x, 16) || !aligned(router, 16)) return MOE_ERR_ARG;
   hipStream_t st = (hipStream_t)hip_stream;
-  uint8_t* ws = (uint8_t*)workspace;
-  Routing r;
-  r.logits = (float*)(ws + p.logits);
-  r.ids = topk_ids;
-  r.w = topk_w;
-  r.counts = expert_counts;
-  r.offsets = expert_offsets;
-  r.slots = token_slots;
-  r.active = active_experts;
-  r.nactive = n_active;
+  Buffers b = carve(p, workspace, topk_ids, topk_w);
+  const BucketOut bo{expert_counts, expert_offsets, token_slots, active_experts, n_active};
   (void)hipGetLastError();
-  enqueue_route(p, router, x, r, st, nullptr);
+  enqueue_route_plain(p, router, x, b, bo, st);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }
 

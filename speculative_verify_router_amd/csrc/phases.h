@@ -1,0 +1,156 @@
+// Fused launches of the small-batch (decode / verify) path.
+//
+//   phase 1: router rows + shared-expert gate/up tiles; the last router
+//            workgroup to finish runs top-k for every token and the
+//            bucketing, so routing costs no launch of its own.
+//   phase 2: routed gate/up tiles + shared-expert down tiles.
+//   phase 3: routed down tiles; the last workgroup to finish a row tile
+//            (over all active experts) combines that tile of the output.
+//
+// Hand-off counters live at the start of the workspace.  Each is returned
+// to zero by the workgroup that consumes it, so a workspace that starts
+// zero-filled stays valid from call to call.
+#pragma once
+
+#include "ffn.h"
+#include "route.h"
+
+namespace svr {
+
+constexpr int kMaxTiles = 1008;  // combine counters available in the workspace
+
+struct Counters {
+  unsigned router_done;
+  unsigned pad[15];
+  unsigned tile_done[kMaxTiles];
+};
+static_assert(sizeof(Counters) == 4096, "counter page");
+
+struct RouteArgs {
+  const float* router;
+  const float* x;
+  float* logits;
+  int32_t* ids;
+  float* w;
+  BucketOut b;
+  int H, E, k, M;
+  int n_router_blocks;
+  Counters* ctr;
+  int bucket;  // 1: also build the per-expert lists (not needed with pair slots)
+};
+
+template <int NC>
+__device__ __forceinline__ void router_part(const RouteArgs& r, int blk) {
+  __shared__ int s_last;
+  const int wv = threadIdx.x >> 6;
+  router_row_block<NC>(r.router, r.x, r.logits, r.H, r.E, r.M, blk);
+  wait_stores();
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = arrive(&r.ctr->router_done) == (unsigned)(r.n_router_blocks - 1);
+  __syncthreads();
+  if (!s_last) return;
+  // Logits of the other workgroups are read with load_shared (coherent).
+  for (int t = wv; t < r.M; t += kWavesPerBlock)
+    topk_token<true>(r.logits + (int64_t)t * r.E, r.ids + (int64_t)t * r.k,
+                     r.w + (int64_t)t * r.k, r.E, r.k);
+  if (r.bucket) {
+    __syncthreads();
+    bucket_block(r.ids, r.M * r.k, r.E, r.b);
+  }
+  if (threadIdx.x == 0)
+    __hip_atomic_store(&r.ctr->router_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Phase 1.  SFMT == 0: no shared expert.
+template <int NC, int SFMT, int SCPL>
+__global__ __launch_bounds__(kBlock) void k_phase1(RouteArgs r, FfnArgs s) {
+  if ((int)blockIdx.x < r.n_router_blocks) {
+    router_part<NC>(r, blockIdx.x);
+  } else if constexpr (SFMT != 0) {
+    ffn_tile<SFMT, SCPL, true>(s, 0, blockIdx.x - r.n_router_blocks);
+  }
+}
+
+// Two FFN roles in one grid: blocks [0, na) take tiles of role A (grid of
+// a_tiles x slots, tile fastest), the rest tiles of role B (one slot).
+template <int FA, int CA, bool GA, int FB, int CB, bool GB>
+__global__ __launch_bounds__(kBlock) void k_dual(FfnArgs a, int a_tiles, int na, FfnArgs b) {
+  const int blk = blockIdx.x;
+  if (blk < na) {
+    ffn_tile<FA, CA, GA>(a, blk / a_tiles, blk % a_tiles);
+  } else {
+    ffn_tile<FB, CB, GB>(b, 0, blk - na);
+  }
+}
+
+// Combine of rows [r0, r1) of y: y[t][r] = s[t][r] + sum_j w[t][j] o[t*k+j][r],
+// the expert outputs o coming from other workgroups of the same launch.
+// Each thread takes four consecutive rows of one token and requests the
+// k slots' float4s eight at a time before adding them in slot order.
+__device__ __forceinline__ void combine_rows(const float* __restrict__ o,
+                                             const float* __restrict__ s,
+                                             const float* __restrict__ w, float* __restrict__ y,
+                                             int M, int H, int k, int r0, int r1) {
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(o, (uint32_t)((int64_t)M * k * H * 4));
+  const int n4 = (r1 - r0) >> 2;
+  for (int i = threadIdx.x; i < M * n4; i += kBlock) {
+    const int t = i / n4;
+    const int r = r0 + 4 * (i - t * n4);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (s) {
+      const float4 sv = ldf4(s + (int64_t)t * H + r);
+      acc = f32x4{sv.x, sv.y, sv.z, sv.w};
+    }
+    for (int j0 = 0; j0 < k; j0 += 8) {
+      f32x4 v[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        v[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (j0 + jj < k)
+          v[jj] = bload16_shared(ro, (uint32_t)((((int64_t)t * k + j0 + jj) * H + r) * 4));
+      }
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        if (j0 + jj < k) {
+          const float wj = w[t * k + j0 + jj];
+          acc.x = fmaf(wj, v[jj].x, acc.x);
+          acc.y = fmaf(wj, v[jj].y, acc.y);
+          acc.z = fmaf(wj, v[jj].z, acc.z);
+          acc.w = fmaf(wj, v[jj].w, acc.w);
+        }
+      }
+    }
+    *reinterpret_cast<float4*>(y + (int64_t)t * H + r) = make_float4(acc.x, acc.y, acc.z, acc.w);
+  }
+}
+
+struct CombineArgs {
+  const float* o;
+  const float* s;
+  const float* w;
+  float* y;
+  int M, H, k;
+  Counters* ctr;
+};
+
+// Phase 3: routed down tiles, then the combine of each finished row tile.
+template <int FMT, int CPL>
+__global__ __launch_bounds__(kBlock) void k_down_combine(FfnArgs a, CombineArgs c) {
+  __shared__ int s_last;
+  const int tile = blockIdx.x, slot = blockIdx.y;
+  const int n_act = a.pair_expert ? a.n_pairs : *a.n_active;
+  if (slot >= n_act) return;  // block-uniform; these blocks never count
+  ffn_tile<FMT, CPL, false>(a, slot, tile);  // o rows stored with store_shared
+  wait_stores();
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = arrive(&c.ctr->tile_done[tile]) == (unsigned)(n_act - 1);
+  __syncthreads();
+  if (!s_last) return;
+  const int r0 = tile * a.units_per_block;
+  const int r1 = min(r0 + a.units_per_block, c.H);
+  combine_rows(c.o, c.s, c.w, c.y, c.M, c.H, c.k, r0, r1);
+  if (threadIdx.x == 0)
+    __hip_atomic_store(&c.ctr->tile_done[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace svr

@@ -1,11 +1,11 @@
-// Routing kernels: router GEMV, wave-level top-k with renormalised softmax
-// weights, and per-expert bucketing of (token, slot) pairs.
+// Routing: router GEMV, wave-level top-k with renormalised softmax weights,
+// and per-expert bucketing of (token, slot) pairs.
 //
 // The router is an F32 matrix ("Step-5 Preview GGUF", Precision
 // distribution table, routers row); 8 of 352 experts are selected per token
 // ("Step-5 Preview GGUF", Model background, configuration table).  The score
 // function is not on the pages; the softmax top-k with renormalisation used
-// here is the layer's stated contract (include/moe_layer.h).
+// here is the layer's contract (include/moe_layer.h).
 #pragma once
 
 #include "common.h"
@@ -13,20 +13,76 @@
 namespace svr {
 
 // ---------------------------------------------------------------------------
-// Router GEMV: logits[t][e] = sum_h router[e][h] * x[t][h].
-// One wave per router row; lane l reads float4 chunks l, l+64, ... of the
-// row (1 KiB per wave instruction, fully coalesced) and the same chunks of
-// up to 4 tokens at a time, then a butterfly sum per token.
+// Router GEMV for a small batch: one workgroup per router row, wave w taking
+// quarter w of the row.  Each lane requests its float4 chunks of the row and
+// of up to four tokens at once (NC per lane), so a row costs about one
+// memory round trip; the four quarter sums are added in a fixed order.
 // ---------------------------------------------------------------------------
+template <int NC>
+__device__ __forceinline__ void router_row_block(const float* __restrict__ router,
+                                                 const float* __restrict__ x,
+                                                 float* __restrict__ logits, int H, int E, int M,
+                                                 int e) {
+  // s_part[wave][row of 16 lanes][token]: partial sums, added in a fixed order.
+  __shared__ float s_part[kWavesPerBlock][4][16];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x >> 6;
+  const int Q = H >> 4;  // float4 chunks per quarter
+  const int c0 = wv * Q;
+  const float* wrow = router + (int64_t)e * H;
+  float4 w[NC];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int c = lane + kWave * i;
+    w[i] = (c < Q) ? ldf4(wrow + 4 * (c0 + c)) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  for (int t0 = 0; t0 < M; t0 += 4) {
+    float4 v[4][NC];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        const int c = lane + kWave * i;
+        v[t][i] = (t0 + t < M && c < Q) ? ldf4(x + (int64_t)(t0 + t) * H + 4 * (c0 + c))
+                                         : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        a0 = fmaf(w[i].x, v[t][i].x, a0);
+        a1 = fmaf(w[i].y, v[t][i].y, a1);
+        a0 = fmaf(w[i].z, v[t][i].z, a0);
+        a1 = fmaf(w[i].w, v[t][i].w, a1);
+      }
+      const float rs = group_sum_last(a0 + a1, 16);  // row sums in lanes 15, 31, 47, 63
+      if ((lane & 15) == 15 && t0 + t < M) s_part[wv][lane >> 4][t0 + t] = rs;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < M) {
+    float acc = 0.f;
+#pragma unroll
+    for (int w4 = 0; w4 < kWavesPerBlock; ++w4)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc += s_part[w4][r][threadIdx.x];
+    store_shared(logits + (int64_t)threadIdx.x * E + e, acc);
+  }
+}
+
+// Router GEMV for any batch size (prefill): one wave per router row, tokens
+// four at a time, the row re-read from L2 per group.
 __global__ __launch_bounds__(kBlock) void k_router_logits(const float* __restrict__ router,
                                                           const float* __restrict__ x,
                                                           float* __restrict__ logits, int H,
                                                           int E, int M) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int e = blockIdx.x * (kBlock / kWave) + (threadIdx.x >> 6);
+  const int e = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
   if (e >= E) return;  // wave-uniform: no block-level barrier below
   const int H4 = H >> 2;
-  const float* wrow = router + (size_t)e * H;
+  const float* wrow = router + (int64_t)e * H;
   for (int t0 = 0; t0 < M; t0 += 4) {
     const int nt = min(4, M - t0);
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
@@ -35,7 +91,7 @@ __global__ __launch_bounds__(kBlock) void k_router_logits(const float* __restric
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if (i < nt) {
-          const float4 v = ldf4(x + (size_t)(t0 + i) * H + 4 * c);
+          const float4 v = ldf4(x + (int64_t)(t0 + i) * H + 4 * c);
           acc[i] = fmaf(w.x, v.x, acc[i]);
           acc[i] = fmaf(w.y, v.y, acc[i]);
           acc[i] = fmaf(w.z, v.z, acc[i]);
@@ -46,99 +102,134 @@ __global__ __launch_bounds__(kBlock) void k_router_logits(const float* __restric
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float s = wave_sum(acc[i]);
-      if (i < nt && lane == 0) logits[(size_t)(t0 + i) * E + e] = s;
+      if (i < nt && lane == 0) logits[(int64_t)(t0 + i) * E + e] = s;
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Top-k: one wave per token.  Lane l holds logits e = l + 64*i.  k rounds of
-// a wave arg-max on the key (value descending, index ascending); the winner
-// is marked taken.  Then w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0).
-// NaN logits are treated as -inf.
+// Top-k of one token by one wave.  Lane l holds logits e = l + 64*i as
+// order-preserving 32-bit keys (larger logit, larger key; -0 taken as +0,
+// NaN as -inf), and keeps as its candidate the best of its untaken ones
+// (largest key, then lowest index).  Each of the k rounds takes the wave
+// maximum of the candidate keys with DPP row scans and row broadcasts; the
+// lane holding it (the lowest expert index if keys tie exactly) owns the
+// winner, marks it taken and refreshes its candidate.  Then
+// w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ bool better(float va, int ea, float vb, int eb) {
-  return va > vb || (va == vb && ea < eb);
+__device__ __forceinline__ uint32_t order_key(float v) {
+  v = (v != v) ? -INFINITY : v + 0.0f;
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __builtin_bit_cast(float, (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+template <bool COHERENT, int NV>
+__device__ __forceinline__ void topk_token_nv(const float* __restrict__ row,
+                                              int32_t* __restrict__ ids, float* __restrict__ wts,
+                                              int E, int k) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int nv = (E + kWave - 1) / kWave;
+  uint32_t key[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int e = lane + kWave * i;
+    key[i] = 0u;  // below every real key: never selected while k <= E
+    if (i < nv && e < E) key[i] = order_key(COHERENT ? load_shared(row + e) : row[e]);
+  }
+  // Candidate: best untaken local key (bit i of `taken` marks key[i] taken).
+  uint32_t taken = 0u;
+  uint32_t ck = 0u;
+  int ci = 0;
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+    if (i < nv && key[i] > ck) {
+      ck = key[i];
+      ci = i;
+    }
+  uint32_t my_key = 0u;
+  int my_e = -1;
+  for (int j = 0; j < k; ++j) {
+    const uint32_t best = wave_max_u32(ck);
+    const uint64_t hold = __ballot(ck == best);
+    int wl;
+    if (__popcll(hold) == 1) {
+      wl = __ffsll((unsigned long long)hold) - 1;
+    } else {  // exact tie between lanes: the lowest expert index wins
+      const uint32_t e_me = (ck == best) ? (uint32_t)(lane + kWave * ci) : 0xFFFFFFFFu;
+      wl = (int)(wave_min_u32(e_me) & (kWave - 1));
+    }
+    const int we = __builtin_amdgcn_readlane(lane + kWave * ci, wl);
+    if (lane == j) {
+      my_key = best;
+      my_e = we;
+    }
+    if (lane == wl) {
+      taken |= 1u << ci;
+      ck = 0u;
+      ci = 0;
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+        if (i < nv && !((taken >> i) & 1u) && key[i] > ck) {
+          ck = key[i];
+          ci = i;
+        }
+    }
+  }
+  const float my_v = key_value(my_key);
+  const float vmax = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_v), 0));
+  const float ex = (lane < k) ? __expf(my_v - vmax) : 0.f;
+  const float tot = wave_sum(ex);
+  if (lane < k) {
+    ids[lane] = my_e;
+    wts[lane] = ex / tot;
+  }
+}
+
+// NV keys per lane: 8 for up to 512 experts, 16 for up to 1024.
+template <bool COHERENT>
+__device__ __forceinline__ void topk_token(const float* __restrict__ row, int32_t* __restrict__ ids,
+                                           float* __restrict__ wts, int E, int k) {
+  if (E <= 8 * kWave)
+    topk_token_nv<COHERENT, 8>(row, ids, wts, E, k);
+  else
+    topk_token_nv<COHERENT, kMaxExperts / kWave>(row, ids, wts, E, k);
 }
 
 __global__ __launch_bounds__(kBlock) void k_topk(const float* __restrict__ logits,
                                                  int32_t* __restrict__ ids,
                                                  float* __restrict__ wts, int E, int k, int M) {
-  constexpr int NV = kMaxExperts / kWave;  // 16 values per lane at most
-  const int lane = threadIdx.x & (kWave - 1);
-  const int t = blockIdx.x * (kBlock / kWave) + (threadIdx.x >> 6);
+  const int t = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
   if (t >= M) return;
-  const float* row = logits + (size_t)t * E;
-  float v[NV];
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int e = lane + kWave * i;
-    float a = (e < E) ? row[e] : -INFINITY;
-    v[i] = (a != a) ? -INFINITY : a;
-  }
-  uint32_t taken = 0;
-  for (int i = 0; i < NV; ++i)
-    if (lane + kWave * i >= E) taken |= 1u << i;
-  float my_v = -INFINITY;
-  int my_e = -1;
-  for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int be = 0x7FFFFFFF;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int e = lane + kWave * i;
-      if (!((taken >> i) & 1u) && better(v[i], e, bv, be)) {
-        bv = v[i];
-        be = e;
-      }
-    }
-    for (int off = kWave / 2; off > 0; off >>= 1) {
-      const float ov = __shfl_xor(bv, off, kWave);
-      const int oe = __shfl_xor(be, off, kWave);
-      if (better(ov, oe, bv, be)) {
-        bv = ov;
-        be = oe;
-      }
-    }
-    if ((be & (kWave - 1)) == lane) taken |= 1u << (be / kWave);
-    if (lane == j) {
-      my_v = bv;
-      my_e = be;
-    }
-  }
-  const float vmax = __shfl(my_v, 0, kWave);
-  const float ex = (lane < k) ? __expf(my_v - vmax) : 0.f;
-  const float tot = wave_sum(ex);
-  if (lane < k) {
-    ids[(size_t)t * k + lane] = my_e;
-    wts[(size_t)t * k + lane] = ex / tot;
-  }
+  topk_token<false>(logits + (int64_t)t * E, ids + (int64_t)t * k, wts + (int64_t)t * k, E, k);
 }
 
 // ---------------------------------------------------------------------------
-// Bucketing: one workgroup.  counts[E], offsets[E+1] (exclusive scan),
-// active[] (experts with pairs, ascending, then -1), n_active, and
-// slots[]: the pair indices p = t*k + j of each expert in ascending p (and
-// so ascending t).  Pairs are ranked in order by wave 0, 64 at a time: lanes
-// holding the same expert are matched with ballots over the id bits, so the
-// rank of a pair among equal ids of its chunk is a popcount.
+// Bucketing by one workgroup: counts[E], offsets[E+1] (exclusive scan),
+// active[] (experts with pairs, ascending, then -1), n_active, and slots[]:
+// the pair indices p = t*k + j of each expert in ascending p (so ascending
+// t).  Pairs are ranked in order by wave 0, 64 at a time: lanes holding the
+// same expert are matched with ballots over the id bits, and the rank of a
+// pair among equal ids of its chunk is a popcount.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kBlock) void k_bucket(const int32_t* __restrict__ ids, int n_pairs,
-                                                   int E, int32_t* __restrict__ counts,
-                                                   int32_t* __restrict__ offsets,
-                                                   int32_t* __restrict__ slots,
-                                                   int32_t* __restrict__ active,
-                                                   int32_t* __restrict__ n_active) {
+struct BucketOut {
+  int32_t *counts, *offsets, *slots, *active, *n_active;
+};
+
+__device__ void bucket_block(const int32_t* __restrict__ ids, int n_pairs, int E,
+                             const BucketOut& o) {
   __shared__ int32_t s_cnt[kMaxExperts];
   __shared__ int32_t s_cur[kMaxExperts];
-  __shared__ int32_t s_wave_tot[kBlock / kWave];
+  __shared__ int32_t s_wave_c[kWavesPerBlock], s_wave_a[kWavesPerBlock];
   const int tid = threadIdx.x;
   for (int e = tid; e < E; e += kBlock) s_cnt[e] = 0;
   __syncthreads();
   for (int p = tid; p < n_pairs; p += kBlock) atomicAdd(&s_cnt[ids[p]], 1);
   __syncthreads();
-  // Exclusive scan of counts and of the "active" flags over E <= 1024
-  // entries: each thread owns 4 consecutive experts.
+  // Exclusive scans of the counts and of the active flags over E <= 1024
+  // experts: each thread owns 4 consecutive experts.
   int c4[4], a4[4];
   int csum = 0, asum = 0;
 #pragma unroll
@@ -149,8 +240,6 @@ __global__ __launch_bounds__(kBlock) void k_bucket(const int32_t* __restrict__ i
     csum += c4[i];
     asum += a4[i];
   }
-  // Block scan of (csum, asum) packed: counts < 2^16 per expert is not
-  // guaranteed, so scan the two sums separately.
   int cinc = csum, ainc = asum;
   const int lane = tid & (kWave - 1), wv = tid >> 6;
   for (int off = 1; off < kWave; off <<= 1) {
@@ -161,41 +250,40 @@ __global__ __launch_bounds__(kBlock) void k_bucket(const int32_t* __restrict__ i
       ainc += oa;
     }
   }
-  __shared__ int32_t s_wave_a[kBlock / kWave];
   if (lane == kWave - 1) {
-    s_wave_tot[wv] = cinc;
+    s_wave_c[wv] = cinc;
     s_wave_a[wv] = ainc;
   }
   __syncthreads();
   int cbase = 0, abase = 0;
   for (int w = 0; w < wv; ++w) {
-    cbase += s_wave_tot[w];
+    cbase += s_wave_c[w];
     abase += s_wave_a[w];
   }
   int cex = cbase + cinc - csum, aex = abase + ainc - asum;
+  if (tid == kBlock - 1 && o.n_active) *o.n_active = aex + asum;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = tid * 4 + i;
     if (e < E) {
-      if (counts) counts[e] = c4[i];
-      if (offsets) offsets[e] = cex;
+      if (o.counts) o.counts[e] = c4[i];
+      if (o.offsets) o.offsets[e] = cex;
       s_cur[e] = cex;
-      if (active) active[e] = -1;
+      if (o.active) o.active[e] = -1;
     }
     cex += c4[i];
   }
-  if (tid == kBlock - 1 && offsets) offsets[E] = cex;
-  if (tid == kBlock - 1 && n_active) *n_active = aex + asum;
+  if (tid == kBlock - 1 && o.offsets) o.offsets[E] = cex;
   __syncthreads();
-  if (active) {
+  if (o.active) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = tid * 4 + i;
-      if (e < E && a4[i]) active[aex] = e;
+      if (e < E && a4[i]) o.active[aex] = e;
       aex += a4[i];
     }
   }
-  if (slots && wv == 0) {
+  if (o.slots && wv == 0) {
     int nbits = 0;
     while ((1 << nbits) < E) ++nbits;
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
@@ -209,15 +297,17 @@ __global__ __launch_bounds__(kBlock) void k_bucket(const int32_t* __restrict__ i
         const uint64_t bal = __ballot(bit);
         same &= bit ? bal : ~bal;
       }
-      if (valid) {
-        const int rank = __popcll(same & below);
-        slots[s_cur[e] + rank] = p;
-      }
+      if (valid) o.slots[s_cur[e] + __popcll(same & below)] = p;
       __builtin_amdgcn_wave_barrier();
       if (valid && (same & below) == 0) s_cur[e] += __popcll(same);
       __builtin_amdgcn_wave_barrier();
     }
   }
+}
+
+__global__ __launch_bounds__(kBlock) void k_bucket(const int32_t* __restrict__ ids, int n_pairs,
+                                                   int E, BucketOut o) {
+  bucket_block(ids, n_pairs, E, o);
 }
 
 }  // namespace svr

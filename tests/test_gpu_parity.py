@@ -219,3 +219,22 @@ def test_timed_forward_matches_and_records_events():
     assert all(m >= 0 for m in ms)
     with pytest.raises(svr.MoeError):
         svr.moe_layer_forward_timed(desc_of(cfg), w, dev(x), y, [e.cuda_event for e in evs[:-1]])
+
+
+def test_prepared_forward_matches_plain_call():
+    cfg = small_config(hidden=512, n_experts=16, top_k=4, ffn=256, shared_ffn=128,
+                       expert_type="q4_k", n_tokens=3, router_std=0.2, seed_index=559)
+    inp = synth.draw_layer(cfg)
+    x, _ = conditioned_tokens(inp)
+    w = upload(inp)
+    y0, ids0, tw0 = gpu_forward(cfg, w, x)
+    y = torch.empty((3, 512), dtype=torch.float32, device="cuda")
+    ids = torch.empty((3, 4), dtype=torch.int32, device="cuda")
+    tw = torch.empty((3, 4), dtype=torch.float32, device="cuda")
+    call = svr.PreparedForward(desc_of(cfg), w, dev(x), y, ids, tw)
+    for _ in range(3):  # the workspace is reused call after call
+        y.zero_()
+        call()
+        torch.cuda.synchronize()
+        assert np.array_equal(y.cpu().numpy(), y0)
+        assert np.array_equal(ids.cpu().numpy(), ids0)
