@@ -12,9 +12,11 @@ finds its weights in the 256 MB Infinity Cache left by the previous one.
 Prints one JSON line.  `roofline` reports the dominant kernel (routed
 gate/up) against the 8 TB/s HBM peak, timed with HIP events recorded by
 the library on the launch stream; `cpu_baseline` times the CPU oracle on a
-bounded sample (one layer call) on the host.
+bounded sample (repeated layer calls, about 12 s) on the host.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--instances 4]
+                    [--events dominant|all] [--graph] [--copy-calibration MIB]
+    python bench.py --summarize-counters FETCH_DIR WRITE_DIR [--copy-calibration MIB]
 """
 
 from __future__ import annotations
@@ -33,7 +35,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "step35_verify_m4"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gateup_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_dual_step35_verify_m4_hbm_counters.json")
 DOMINANT = "gateup"
 
 
@@ -80,7 +82,7 @@ def traffic_for(workload: str):
 
 
 def cpu_baseline(cfg, inp, x) -> dict:
-    """The oracle as it stands, one layer call of the workload, BLAS on one thread."""
+    """The oracle as it stands on whole layer calls of the workload, BLAS on one thread."""
     from oracle import moe_oracle as om
     try:
         from threadpoolctl import threadpool_limits
@@ -91,14 +93,62 @@ def cpu_baseline(cfg, inp, x) -> dict:
     if cfg.shared_ffn:
         kw.update(shared=(inp.shared_gate, inp.shared_up, inp.shared_down),
                   shared_ffn=cfg.shared_ffn, shared_type=cfg.shared_type)
-    t0 = time.perf_counter()
-    om.moe_layer(x, inp.router, inp.gate, inp.up, inp.down, **kw)
-    dt = time.perf_counter() - t0
+    # Repeat whole layer calls on the same weights and tokens until about
+    # 12 s of CPU work have been timed (at least one call, at most 30).
+    calls, t0 = 0, time.perf_counter()
+    while True:
+        om.moe_layer(x, inp.router, inp.gate, inp.up, inp.down, **kw)
+        calls += 1
+        dt = time.perf_counter() - t0
+        if dt >= 12.0 or calls >= 30:
+            break
     if limiter is not None:
         limiter.unregister()
-    return {"value": cfg.n_tokens / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"one layer call of {cfg.name} ({cfg.n_tokens} tokens), float64 NumPy, "
-                      f"{dt:.1f} s"}
+    return {"value": calls * cfg.n_tokens / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{calls} layer call(s) of {cfg.name} ({cfg.n_tokens} tokens each, "
+                      f"instance 0), float64 NumPy on one thread, {dt:.1f} s"}
+
+
+def _counter_rows(path: str):
+    """(kernel name, counter name, value) rows of every rocprofv3
+    counter_collection.csv under `path`."""
+    import csv
+    for dirpath, _, files in os.walk(path):
+        for fn in sorted(files):
+            if fn.endswith("counter_collection.csv"):
+                with open(os.path.join(dirpath, fn), newline="") as f:
+                    for row in csv.DictReader(f):
+                        yield row["Kernel_Name"], row["Counter_Name"], float(row["Counter_Value"])
+
+
+def summarize_counters(fetch_dir: str, write_dir: str, workload: str, copy_bytes: int) -> dict:
+    """Scale the dominant kernel's FETCH_SIZE / WRITE_SIZE (KiB per dispatch)
+    by the factors a plain copy of `copy_bytes` bytes reads on the same
+    counters, and store the HBM bytes per launch for later bench runs."""
+    def per_kernel(path, counter):
+        acc = {}
+        for name, cname, v in _counter_rows(path):
+            if cname == counter:
+                acc.setdefault(name, []).append(v)
+        return acc
+
+    out = {"workload": workload, "source_hash": source_hash(), "copy_bytes": copy_bytes}
+    for counter, path in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        acc = per_kernel(path, counter)
+        dom = [v for n, vs in acc.items() if n.startswith("void svr::k_dual") for v in vs]
+        # The runtime's device-to-device copy kernel moving copy_bytes
+        # (smaller copies of the same kernel are left out).
+        cpy = [v for n, vs in acc.items() if "copybuffer" in n.lower()
+               for v in vs if v * 1024 > copy_bytes / 4]
+        if not dom or not cpy:
+            raise SystemExit(f"{counter}: no dispatches of the dominant or copy kernel in {path}")
+        scale = copy_bytes / (float(np.median(cpy)) * 1024.0)
+        out[counter] = {"kib_per_launch": float(np.mean(dom)), "dispatches": len(dom),
+                        "copy_kib": float(np.median(cpy)), "scale": scale,
+                        "bytes_per_launch": float(np.mean(dom)) * 1024.0 * scale}
+    out["bytes_per_launch"] = int(round(out["FETCH_SIZE"]["bytes_per_launch"]
+                                        + out["WRITE_SIZE"]["bytes_per_launch"]))
+    return out
 
 
 def main(argv=None) -> int:
@@ -113,7 +163,21 @@ def main(argv=None) -> int:
                     help="HIP events per step: around the dominant stage only, or every stage")
     ap.add_argument("--graph", action="store_true",
                     help="also time the same steps replayed from a captured HIP graph")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after the timed steps, run five plain device copies of MIB MiB "
+                         "(the reference kernel for the HBM byte counters)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="read rocprofv3 FETCH_SIZE / WRITE_SIZE runs of this script (taken "
+                         "with --copy-calibration) and write the dominant kernel's HBM bytes")
     args = ap.parse_args(argv)
+
+    if args.summarize_counters:
+        t = summarize_counters(*args.summarize_counters, args.workload,
+                               (args.copy_calibration or 512) << 20)
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(t, f, indent=1)
+        print(json.dumps(t))
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the layer is built and timed on a single MI355X; "
@@ -228,6 +292,15 @@ def main(argv=None) -> int:
             g.replay()
         torch.cuda.synchronize()
         graph_ms = (time.perf_counter() - t1) * 1e3 / (reps * R)
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 18  # floats
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     ms_per_step = elapsed * 1e3 / K
     value = M * K / elapsed

@@ -20,7 +20,7 @@ blocks exactly, then dense products.  What the layer computes:
   Step3.5/3.7 flash mtp3", Overview, data-flow trace, target batch step).
 
 The pages do not write down the router formula, the activation or the
-block layouts.  Readings taken here (each listed in the design doc):
+block layouts.  Readings taken here:
 
 * router: softmax over all experts of the F32 logits l = Wr x; the k largest
   logits are selected, ties to the lower expert index, in descending order;
