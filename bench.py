@@ -9,9 +9,11 @@ accepted token and 3 drafts), hidden 4096, 288 routed experts, top-8, FFN
 router.  Calls rotate over R independent layer instances so that no call
 finds its weights in the 256 MB Infinity Cache left by the previous one.
 
-Prints one JSON line.  `roofline` reports the dominant kernel (routed
-gate/up) against the 8 TB/s HBM peak, timed with HIP events recorded by
-the library on the launch stream; `cpu_baseline` times the CPU oracle on a
+Prints one JSON line.  `roofline` reports the dominant kernel against the
+8 TB/s HBM peak: for batches of up to four tokens the whole layer is one
+launch (k_flow, every byte of the layer); otherwise the routed gate/up
+stage (k_dual).  Its time comes from HIP events recorded by the library on
+the launch stream; `cpu_baseline` times the CPU oracle on a
 bounded sample (repeated layer calls, about 12 s) on the host.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--instances 4]
@@ -35,8 +37,14 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "step35_verify_m4"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_dual_step35_verify_m4_hbm_counters.json")
-DOMINANT = "gateup"
+# Dominant stage -> its kernel.  Batches of up to four tokens run the whole
+# layer as one launch (stage "layer"); larger ones in three stages, of which
+# "gateup" moves the most bytes.
+KERNEL_OF_STAGE = {"layer": "k_flow", "gateup": "k_dual"}
+
+
+def traffic_file(kernel: str, workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_counters.json")
 
 
 def _bytes_per_row(dtype: str, cols: int) -> float:
@@ -56,7 +64,8 @@ def layer_bytes(cfg, distinct: int) -> dict:
     gateup = distinct * 2 * F * _bytes_per_row(cfg.expert_type, H) + M * H * 4 + M * k * F * 4
     if Fs:
         gateup += H * _bytes_per_row(cfg.shared_type, Fs) + M * Fs * 4 + M * H * 4
-    return dict(total=router + distinct * expert + shared + xy, gateup=gateup)
+    total = router + distinct * expert + shared + xy
+    return dict(total=total, layer=total, gateup=gateup)
 
 
 def source_hash() -> str:
@@ -68,11 +77,11 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_for(workload: str):
+def traffic_for(kernel: str, workload: str):
     """HBM bytes per launch of the dominant kernel from committed counter runs,
     or None if they were taken on other kernel sources."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(kernel, workload)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -121,7 +130,8 @@ def _counter_rows(path: str):
                         yield row["Kernel_Name"], row["Counter_Name"], float(row["Counter_Value"])
 
 
-def summarize_counters(fetch_dir: str, write_dir: str, workload: str, copy_bytes: int) -> dict:
+def summarize_counters(fetch_dir: str, write_dir: str, workload: str, copy_bytes: int,
+                       kernel: str) -> dict:
     """Scale the dominant kernel's FETCH_SIZE / WRITE_SIZE (KiB per dispatch)
     by the factors a plain copy of `copy_bytes` bytes reads on the same
     counters, and store the HBM bytes per launch for later bench runs."""
@@ -132,10 +142,11 @@ def summarize_counters(fetch_dir: str, write_dir: str, workload: str, copy_bytes
                 acc.setdefault(name, []).append(v)
         return acc
 
-    out = {"workload": workload, "source_hash": source_hash(), "copy_bytes": copy_bytes}
+    out = {"kernel": kernel, "workload": workload, "source_hash": source_hash(),
+           "copy_bytes": copy_bytes}
     for counter, path in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         acc = per_kernel(path, counter)
-        dom = [v for n, vs in acc.items() if n.startswith("void svr::k_dual") for v in vs]
+        dom = [v for n, vs in acc.items() if n.startswith(f"void svr::{kernel}<") for v in vs]
         # The runtime's device-to-device copy kernel moving copy_bytes
         # (smaller copies of the same kernel are left out).
         cpy = [v for n, vs in acc.items() if "copybuffer" in n.lower()
@@ -161,20 +172,26 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--events", choices=["dominant", "all"], default="dominant",
                     help="HIP events per step: around the dominant stage only, or every stage")
+    ap.add_argument("--event-every", type=int, default=5, metavar="N",
+                    help="record the stage events on every N-th timed step only (the markers "
+                         "delay the next launch; the other steps run without them)")
+    ap.add_argument("--single-launch", action="store_true",
+                    help="run the layer as one kernel launch (MOE_SINGLE_LAUNCH)")
     ap.add_argument("--graph", action="store_true",
                     help="also time the same steps replayed from a captured HIP graph")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the timed steps, run five plain device copies of MIB MiB "
                          "(the reference kernel for the HBM byte counters)")
-    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+    ap.add_argument("--summarize-counters", nargs=3, metavar=("KERNEL", "FETCH_DIR", "WRITE_DIR"),
                     help="read rocprofv3 FETCH_SIZE / WRITE_SIZE runs of this script (taken "
-                         "with --copy-calibration) and write the dominant kernel's HBM bytes")
+                         "with --copy-calibration) and write KERNEL's HBM bytes per launch")
     args = ap.parse_args(argv)
 
     if args.summarize_counters:
-        t = summarize_counters(*args.summarize_counters, args.workload,
-                               (args.copy_calibration or 512) << 20)
-        with open(TRAFFIC_FILE, "w") as f:
+        kern, fdir, wdir = args.summarize_counters
+        t = summarize_counters(fdir, wdir, args.workload, (args.copy_calibration or 512) << 20,
+                               kern)
+        with open(traffic_file(kern, args.workload), "w") as f:
             json.dump(t, f, indent=1)
         print(json.dumps(t))
         return 0
@@ -192,7 +209,7 @@ def main(argv=None) -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     desc = svr.LayerDesc(cfg.hidden, cfg.n_experts, cfg.top_k, cfg.ffn, cfg.shared_ffn,
-                         cfg.expert_type, cfg.shared_type)
+                         cfg.expert_type, cfg.shared_type, single_launch=args.single_launch)
     M, k = cfg.n_tokens, cfg.top_k
     R = max(1, args.instances)
 
@@ -229,8 +246,10 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
     distinct = [len(np.unique(t.cpu().numpy())) for t in ids]
 
-    nst = svr.moe_stage_count()
-    names = [svr.moe_stage_name(j) for j in range(nst)]
+    nst = svr.moe_stage_count(desc, M)
+    names = [svr.moe_stage_name(desc, M, j) for j in range(nst)]
+    DOMINANT = "layer" if "layer" in names else "gateup"
+    kernel = KERNEL_OF_STAGE[DOMINANT]
     K = args.steps
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(K)]
     for row in evs:  # create the underlying HIP events before the timed region
@@ -248,10 +267,12 @@ def main(argv=None) -> int:
             for row in evs]
     torch.cuda.synchronize()
 
+    every = max(1, args.event_every)
+    timed = [s for s in range(K) if s % every == 0]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(K):
-        calls[s % R](ev_arrays[s])
+        calls[s % R](ev_arrays[s] if s % every == 0 else None)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
@@ -259,13 +280,13 @@ def main(argv=None) -> int:
     dom_ms, dom_bytes = 0.0, 0.0
     lay_bytes = 0.0
     for s in range(K):
+        lay_bytes += layer_bytes(cfg, distinct[s % R])["total"]
+    for s in timed:
         i = s % R
         if args.events == "all":
             stage_ms += [evs[s][j].elapsed_time(evs[s][j + 1]) for j in range(nst)]
         dom_ms += evs[s][dom].elapsed_time(evs[s][dom + 1])
-        b = layer_bytes(cfg, distinct[i])
-        dom_bytes += b["gateup"]
-        lay_bytes += b["total"]
+        dom_bytes += layer_bytes(cfg, distinct[i])[DOMINANT]
 
     graph_ms = None
     if args.graph:
@@ -305,7 +326,7 @@ def main(argv=None) -> int:
     ms_per_step = elapsed * 1e3 / K
     value = M * K / elapsed
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-    traffic = traffic_for(cfg.name)
+    traffic = traffic_for(kernel, cfg.name)
 
     out = {
         "metric": "MoE layer tokens/s + achieved HBM GB/s at verify batch M=4 (Q4_K), 1 MI355X",
@@ -330,14 +351,14 @@ def main(argv=None) -> int:
         "layer_bytes": int(round(lay_bytes / K)),
         "events": args.events,
         "roofline": {
-            "kernel": DOMINANT, "bound": "hbm", "achieved": round(achieved, 1),
+            "kernel": kernel, "stage": DOMINANT, "bound": "hbm", "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic, "bytes_per_launch": int(round(dom_bytes / K)),
-            "avg_launch_us": round(dom_ms * 1e3 / K, 3),
+            "traffic": traffic, "bytes_per_launch": int(round(dom_bytes / len(timed))),
+            "avg_launch_us": round(dom_ms * 1e3 / len(timed), 3), "timed_launches": len(timed),
         },
     }
     if args.events == "all":
-        out["stage_us"] = {n: round(v * 1e3 / K, 2) for n, v in zip(names, stage_ms)}
+        out["stage_us"] = {n: round(v * 1e3 / len(timed), 2) for n, v in zip(names, stage_ms)}
     if graph_ms is not None:
         out["graph_replay"] = {"ms_per_step": round(graph_ms, 5),
                                "tokens_per_s": round(M / (graph_ms * 1e-3), 1)}

@@ -102,7 +102,12 @@ typedef struct moe_layer_desc {
   int32_t shared_ffn;  /* Fs, shared expert FFN width; 0 = no shared expert */
   int32_t expert_type; /* MOE_Q8_0 or MOE_Q4_K: routed gate/up/down */
   int32_t shared_type; /* MOE_Q8_0 or MOE_Q4_K: shared gate/up/down */
+  int32_t flags;       /* 0 or MOE_SINGLE_LAUNCH; other bits: MOE_ERR_ARG */
 } moe_layer_desc;
+
+/* desc->flags: run batches of 1 to 4 tokens as one kernel launch where the
+ * shapes have a single-launch instantiation (see moe_layer_forward). */
+#define MOE_SINGLE_LAUNCH 1
 
 /* Device pointers to the layer's tensors (layouts above). */
 typedef struct moe_layer_weights {
@@ -127,12 +132,15 @@ const char* moe_strerror(int32_t status);
 int32_t moe_tensor_bytes(int32_t dtype, int64_t rows, int64_t cols, int64_t* bytes);
 
 /* Device workspace, in *bytes, that moe_layer_forward and moe_route need for
- * up to max_tokens tokens: a 4 KiB page of hand-off counters, router logits,
+ * up to max_tokens tokens: 16 KiB of hand-off counters, router logits,
  * routing lists, the SwiGLU activations of every (token, slot) pair and the
- * per-pair expert outputs.  The counter page (the first 4096 bytes) must be
+ * per-pair expert outputs.  The counter area (the first 16384 bytes) must be
  * zero before the first call that uses the workspace; every call leaves it
  * zero again, so zero-fill a workspace once when it is allocated.  Calls that
- * share a workspace must not overlap in time. */
+ * share a workspace must not overlap in time.  One exception: in the
+ * single-launch path every device-side wait is bounded, and if one ever gave
+ * up, the 32-bit word at byte offset 20 of the page becomes nonzero and stays
+ * so (that call's outputs are then undefined); it is zero in normal use. */
 int32_t moe_workspace_bytes(const moe_layer_desc* desc, int32_t max_tokens, size_t* bytes);
 
 /* Routing only (steps: router GEMV, top-k with renormalised softmax weights,
@@ -154,23 +162,30 @@ int32_t moe_route(const moe_layer_desc* desc, const float* router, const float* 
 /* The whole layer: y [M][H] float from x [M][H] float.  topk_ids [M][k] and
  * topk_w [M][k] receive the routing if non-NULL.  workspace must hold
  * moe_workspace_bytes(desc, n_tokens) bytes (device, 256-byte aligned,
- * counter page zero as described above).  The stages are listed by
- * moe_stage_count / moe_stage_name. */
+ * counter page zero as described above).
+ * With MOE_SINGLE_LAUNCH in desc->flags, batches of 1 to 4 tokens whose
+ * shapes have a single-launch instantiation run as ONE kernel launch (stage
+ * "layer"): a work queue in dependency order
+ * (router rows; shared gate/up; routed gate/up per (token, slot) pair;
+ * shared down; routed down, each output row tile combined by the last item
+ * to finish it).  Other calls run three stages ("route_shared_gateup",
+ * "gateup", "down_combine").  moe_stage_count / moe_stage_name say which. */
 int32_t moe_layer_forward(const moe_layer_desc* desc, const moe_layer_weights* weights,
                           const float* x, int32_t n_tokens, float* y,
                           int32_t* topk_ids, float* topk_w,
                           void* workspace, size_t workspace_bytes, void* hip_stream);
 
-/* Number of stages moe_layer_forward enqueues (fixed for a build) and the
- * name of stage i (static string; NULL if i is out of range). */
-int32_t moe_stage_count(void);
-const char* moe_stage_name(int32_t i);
+/* Number of stages a moe_layer_forward call with this desc and n_tokens
+ * enqueues (1 or 3; the negated status code if desc is invalid), and the
+ * name of stage i (static string; NULL if i or desc is invalid). */
+int32_t moe_stage_count(const moe_layer_desc* desc, int32_t n_tokens);
+const char* moe_stage_name(const moe_layer_desc* desc, int32_t n_tokens, int32_t i);
 
 /* moe_layer_forward that also records events[i] (hipEvent_t, created by the
- * caller) on hip_stream before stage i and events[moe_stage_count()] after
- * the last stage, so that the caller can time each stage.  A NULL entry is
- * skipped (no event recorded at that boundary).  n_events must be
- * moe_stage_count() + 1, else MOE_ERR_ARG. */
+ * caller) on hip_stream before stage i and events[n] after the last stage,
+ * n = moe_stage_count(desc, n_tokens), so that the caller can time each
+ * stage.  A NULL entry is skipped (no event recorded at that boundary).
+ * n_events must be n + 1, else MOE_ERR_ARG. */
 int32_t moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_weights* weights,
                                 const float* x, int32_t n_tokens, float* y,
                                 int32_t* topk_ids, float* topk_w,

@@ -30,11 +30,14 @@ class MoeError(RuntimeError):
         self.status = status
 
 
+SINGLE_LAUNCH = 1  # MOE_SINGLE_LAUNCH
+
+
 class _Desc(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("n_experts", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("ffn", ctypes.c_int32),
                 ("shared_ffn", ctypes.c_int32), ("expert_type", ctypes.c_int32),
-                ("shared_type", ctypes.c_int32)]
+                ("shared_type", ctypes.c_int32), ("flags", ctypes.c_int32)]
 
 
 class _Weights(ctypes.Structure):
@@ -52,10 +55,12 @@ class LayerDesc:
     shared_ffn: int = 0
     expert_type: str = "q4_k"
     shared_type: str = "q8_0"
+    single_launch: bool = False  # MOE_SINGLE_LAUNCH
 
     def c(self) -> _Desc:
         return _Desc(self.hidden, self.n_experts, self.top_k, self.ffn, self.shared_ffn,
-                     _DTYPES[self.expert_type], _DTYPES[self.shared_type])
+                     _DTYPES[self.expert_type], _DTYPES[self.shared_type],
+                     SINGLE_LAUNCH if self.single_launch else 0)
 
 
 @dataclasses.dataclass
@@ -97,8 +102,8 @@ def lib():
             "moe_layer_forward": (i32, [D, W, vp, i32, vp, vp, vp, vp, sz, vp]),
             "moe_layer_forward_timed": (i32, [D, W, vp, i32, vp, vp, vp, vp, sz, vp,
                                               ctypes.POINTER(vp), i32]),
-            "moe_stage_count": (i32, []),
-            "moe_stage_name": (ctypes.c_char_p, [i32]),
+            "moe_stage_count": (i32, [D, i32]),
+            "moe_stage_name": (ctypes.c_char_p, [D, i32, i32]),
             "moe_dequant_rows": (i32, [i32, vp, i64, i32, i64, i64, vp, vp]),
         }
         for name, (res, args) in sig.items():
@@ -164,19 +169,28 @@ def moe_workspace_bytes(desc: LayerDesc, max_tokens: int) -> int:
     return out.value
 
 
-def moe_stage_count() -> int:
-    return lib().moe_stage_count()
+def moe_stage_count(desc: LayerDesc, n_tokens: int) -> int:
+    d = desc.c()
+    n = lib().moe_stage_count(ctypes.byref(d), n_tokens)
+    if n <= 0:
+        raise MoeError(-n, "moe_stage_count")
+    return n
 
 
-def moe_stage_name(i: int) -> Optional[str]:
-    s = lib().moe_stage_name(i)
+def moe_stage_name(desc: LayerDesc, n_tokens: int, i: int) -> Optional[str]:
+    d = desc.c()
+    s = lib().moe_stage_name(ctypes.byref(d), n_tokens, i)
     return None if s is None else s.decode()
+
+
+# Leading workspace bytes that hold hand-off counters (zero between calls).
+COUNTER_BYTES = 16384
 
 
 def workspace(desc: LayerDesc, max_tokens: int, device="cuda") -> torch.Tensor:
     """A zero-filled device workspace of moe_workspace_bytes(desc, max_tokens)
     bytes (its counter page must start at zero; calls keep it so)."""
-    n = max(moe_workspace_bytes(desc, max_tokens), 4096)
+    n = max(moe_workspace_bytes(desc, max_tokens), COUNTER_BYTES)
     return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
@@ -212,7 +226,7 @@ def moe_layer_forward(desc: LayerDesc, weights: LayerWeights, x: torch.Tensor, y
 def moe_layer_forward_timed(desc: LayerDesc, weights: LayerWeights, x: torch.Tensor,
                             y: torch.Tensor, events: Sequence, topk_ids=None, topk_w=None,
                             ws: torch.Tensor = None, stream=None):
-    """``events``: moe_stage_count() + 1 raw hipEvent_t handles (ints)."""
+    """``events``: moe_stage_count(desc, M) + 1 raw hipEvent_t handles (ints)."""
     M = x.shape[0]
     d, w = desc.c(), weights.c()
     if ws is None:

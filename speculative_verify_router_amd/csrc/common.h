@@ -14,6 +14,8 @@ constexpr int kWavesPerBlock = kBlock / kWave;
 constexpr int kMaxExperts = 1024;  // experts per layer
 constexpr int kMaxTopK = 64;       // selected experts per token
 constexpr int kMaxChunksPerLane = 8;
+// Hand-off counters at the start of the workspace (zero between calls).
+constexpr int kCounterBytes = 16384;
 
 // fp16 bit pattern -> float (v_cvt_f32_f16; subnormals kept: the kernels run
 // with fp16/fp64 denormals enabled).

@@ -50,6 +50,7 @@ struct FfnArgs {
   int coherent_out;         // 1: outputs are read by other workgroups of this launch
   const int32_t* pair_expert;  // pair slots: slot p is pair p, expert pair_expert[p]
   int n_pairs;                 // number of pair slots (pair_expert != NULL)
+  int coherent_in;  // 1: act and pair_expert were written earlier in this launch
 };
 
 // Tokens per pass: keep the per-lane activation slice within 64 floats.
@@ -69,28 +70,41 @@ struct Stage {
   Chunk<FMT> c1[GATEUP ? CPL : 1];
 };
 
+// cc[ci]: the chunk lane loads for its ci-th position.  Where the lane
+// groups cover more positions than the row has chunks, the spare positions
+// load the row's last chunk (a line the group reads anyway) against a zero
+// activation slice, so they add nothing.
 template <int FMT, int CPL, bool GATEUP>
 __device__ __forceinline__ void load_stage(Stage<FMT, CPL, GATEUP>& s, const QPlanes& p0,
-                                           const QPlanes& p1, uint32_t row, int j, int lpr) {
+                                           const QPlanes& p1, uint32_t row, const int (&cc)[CPL]) {
   const uint32_t qo = row * p0.qrow, so = row * p0.srow;
 #pragma unroll
   for (int ci = 0; ci < CPL; ++ci) {
-    load_chunk(s.c0[ci], p0, qo, so, j + lpr * ci);
-    if (GATEUP) load_chunk(s.c1[ci], p1, qo, so, j + lpr * ci);
+    load_chunk(s.c0[ci], p0, qo, so, cc[ci]);
+    if (GATEUP) load_chunk(s.c1[ci], p1, qo, so, cc[ci]);
   }
 }
 
-template <int FMT, int CPL, int NT, bool GATEUP>
+// Outputs kept in LDS instead of being stored row by row: row u of token
+// slot t goes to p[t * ld + u - row0].  Stores inside the row loop would
+// count against the same wait counter as the ring's loads.
+struct LdsOut {
+  float* p;
+  int row0, ld;
+};
+
+template <int FMT, int CPL, int NT, bool GATEUP, bool LDSOUT>
 __device__ __forceinline__ void compute_stage(const Stage<FMT, CPL, GATEUP>& s,
                                               const XSlice<FMT> (&xs)[NT][CPL], const FfnArgs& a,
                                               int j, int lpr, int u, bool ok,
-                                              const int (&out_row)[NT]) {
+                                              const int (&out_row)[NT], const int (&cc)[CPL],
+                                              const LdsOut& lo, const int (&slot)[NT]) {
   float acc0[NT], acc1[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc0[t] = acc1[t] = 0.f;
 #pragma unroll
   for (int ci = 0; ci < CPL; ++ci) {
-    const int sub = (j + lpr * ci) & 7;  // Q4_K sub-block of this chunk
+    const int sub = cc[ci] & 7;  // Q4_K sub-block of this chunk
     const ChunkScale k0 = decode_scale(s.c0[ci], sub);
 #pragma unroll
     for (int t = 0; t < NT; ++t)
@@ -108,21 +122,27 @@ __device__ __forceinline__ void compute_stage(const Stage<FMT, CPL, GATEUP>& s,
     float v = v0;
     if (GATEUP) v = silu(v0) * group_sum_last(acc1[t], lpr);
     if (ok && j == lpr - 1) {
-      float* dst = a.out + (int64_t)out_row[t] * a.rows_per_expert + u;
-      if (a.coherent_out)
-        store_shared(dst, v);
-      else
-        *dst = v;
+      if (LDSOUT) {
+        lo.p[slot[t] * lo.ld + (u - lo.row0)] = v;
+      } else {
+        float* dst = a.out + (int64_t)out_row[t] * a.rows_per_expert + u;
+        if (a.coherent_out)
+          store_shared(dst, v);
+        else
+          *dst = v;
+      }
     }
   }
 }
 
 // One pass of a wave over rows first, first+step, ... < ue of `expert`, for
-// the NT tokens whose pair ids are given.
-template <int FMT, int CPL, int NT, bool GATEUP>
+// the NT tokens whose pair ids are given (LDSOUT: outputs to lo, token t of
+// the pass in slot lds_slot[t]).
+template <int FMT, int CPL, int NT, bool GATEUP, int NSTMAX = 3, bool LDSOUT = false>
 __device__ __forceinline__ void ffn_pass(const FfnArgs& a, int expert, const int* pair_ids,
-                                         int first, int step, int ue) {
-  constexpr int NST = nst_for(FMT, CPL, GATEUP);
+                                         int first, int step, int ue, LdsOut lo = LdsOut{},
+                                         const int* lds_slot = nullptr) {
+  constexpr int NST = nst_for(FMT, CPL, GATEUP) < NSTMAX ? nst_for(FMT, CPL, GATEUP) : NSTMAX;
   const int lane = threadIdx.x & (kWave - 1);
   const int lpr = a.lpr;
   const int g = lane / lpr;
@@ -134,31 +154,50 @@ __device__ __forceinline__ void ffn_pass(const FfnArgs& a, int expert, const int
   const QPlanes p1 =
       expert_planes<FMT>(GATEUP ? a.w1 : a.w0, a.total_rows, a.K, row0, a.rows_per_expert);
 
+  const int nchunks = a.K / QTraits<FMT>::kWpc;
+  int cc[CPL];
+#pragma unroll
+  for (int ci = 0; ci < CPL; ++ci) cc[ci] = min(j + lpr * ci, nchunks - 1);
+
   XSlice<FMT> xs[NT][CPL];
-  int out_row[NT];
+  int out_row[NT], slot[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const int p = pair_ids[t];
     out_row[t] = p;
-    const float* xr = a.act + (int64_t)(a.act_by_pair ? p : p / a.top_k) * a.K;
+    slot[t] = LDSOUT ? lds_slot[t] : 0;
+    const int xrow = a.act_by_pair ? p : p / a.top_k;
 #pragma unroll
-    for (int ci = 0; ci < CPL; ++ci) load_x<FMT>(xs[t][ci], xr, j + lpr * ci);
+    for (int ci = 0; ci < CPL; ++ci) {
+      if (j + lpr * ci < nchunks) {
+        if (a.coherent_in)
+          load_x_shared<FMT>(xs[t][ci], a.act, xrow * a.K, j + lpr * ci);
+        else
+          load_x<FMT>(xs[t][ci], a.act + (int64_t)xrow * a.K, j + lpr * ci);
+      } else {
+        zero_x<FMT>(xs[t][ci]);
+      }
+    }
   }
 
-  // Row of lane group g at step base: base + g.  Bounds are wave-uniform;
-  // rows at or past `ue` are loaded (zeros past the expert) but not stored.
+  // Row of lane group g at step base: base + g.  The loop is branch-free
+  // over whole groups of NST steps: every prefetch is issued, its row
+  // clamped to the tile's last row (a line already fetched), so the wait
+  // before each step counts a fixed number of loads issued after it.  Rows
+  // at or past `ue` are computed but not written.
+  const int last = ue - 1;
   Stage<FMT, CPL, GATEUP> S[NST];
 #pragma unroll
   for (int s = 0; s < NST - 1; ++s)
-    if (first + s * step < ue) load_stage(S[s], p0, p1, (uint32_t)(first + s * step + g), j, lpr);
+    load_stage(S[s], p0, p1, (uint32_t)min(first + s * step + g, last), cc);
   for (int base = first; base < ue; base += NST * step) {
 #pragma unroll
     for (int s = 0; s < NST; ++s) {
       const int cur = base + s * step;
-      if (cur >= ue) break;
       const int pre = cur + (NST - 1) * step;
-      if (pre < ue) load_stage(S[(s + NST - 1) % NST], p0, p1, (uint32_t)(pre + g), j, lpr);
-      compute_stage<FMT, CPL, NT, GATEUP>(S[s], xs, a, j, lpr, cur + g, cur + g < ue, out_row);
+      load_stage(S[(s + NST - 1) % NST], p0, p1, (uint32_t)min(pre + g, last), cc);
+      compute_stage<FMT, CPL, NT, GATEUP, LDSOUT>(S[s], xs, a, j, lpr, cur + g, cur + g < ue,
+                                                  out_row, cc, lo, slot);
     }
   }
 }
@@ -177,6 +216,38 @@ __device__ __forceinline__ void ffn_pass_nt(const FfnArgs& a, int expert, const 
   }
 }
 
+// Pair slots: rows [tile * units_per_block, ...) of the expert of (token,
+// slot) pair `slot`, the four waves taking different rows.
+template <int FMT, int CPL, bool GATEUP, int NSTMAX = 3, bool LDSOUT = false>
+__device__ __forceinline__ void ffn_tile_pair(const FfnArgs& a, int slot, int tile,
+                                              float* lds = nullptr) {
+  if (slot >= a.n_pairs) return;
+  const int ub = tile * a.units_per_block;
+  const int ue = min(ub + a.units_per_block, a.rows_per_expert);
+  if (ub >= ue) return;
+  const int G = kWave / a.lpr;
+  const int ids1[1] = {slot}, slot0[1] = {0};
+  const int e = a.coherent_in ? load_shared(a.pair_expert + slot) : a.pair_expert[slot];
+  ffn_pass<FMT, CPL, 1, GATEUP, NSTMAX, LDSOUT>(a, e, ids1, ub + (threadIdx.x >> 6) * G,
+                                                kWavesPerBlock * G, ue,
+                                                LdsOut{lds, ub, a.units_per_block}, slot0);
+}
+
+// One expert for the identity token list (the shared expert): rows
+// [tile * units_per_block, ...) for tokens wv, wv + 4, ... of wave wv, one
+// token per pass, so the four waves stream the same rows.
+template <int FMT, int CPL, bool GATEUP, int NSTMAX = 3>
+__device__ __forceinline__ void ffn_tile_tokens(const FfnArgs& a, int tile) {
+  const int ub = tile * a.units_per_block;
+  const int ue = min(ub + a.units_per_block, a.rows_per_expert);
+  if (ub >= ue) return;
+  const int G = kWave / a.lpr;
+  for (int t = threadIdx.x >> 6; t < a.n_tokens; t += kWavesPerBlock) {
+    const int ids1[1] = {t};
+    ffn_pass<FMT, CPL, 1, GATEUP, NSTMAX>(a, 0, ids1, ub, G, ue);
+  }
+}
+
 // Work of workgroup (tile, slot): rows [tile * units_per_block, ...) of the
 // expert in `slot`, for every token routed to it.
 template <int FMT, int CPL, bool GATEUP>
@@ -185,13 +256,7 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int slot, int tile) {
   const int ub = tile * a.units_per_block;
   if (a.pair_expert) {
     // One (token, slot) pair per slot: every workgroup does the same work.
-    if (slot >= a.n_pairs) return;
-    const int ue = min(ub + a.units_per_block, a.rows_per_expert);
-    if (ub >= ue) return;
-    const int G = kWave / a.lpr;
-    const int ids1[1] = {slot};
-    ffn_pass<FMT, CPL, 1, GATEUP>(a, a.pair_expert[slot], ids1, ub + (threadIdx.x >> 6) * G,
-                                  kWavesPerBlock * G, ue);
+    ffn_tile_pair<FMT, CPL, GATEUP>(a, slot, tile);
     return;
   }
   if (a.n_active && slot >= *a.n_active) return;

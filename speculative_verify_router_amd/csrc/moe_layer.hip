@@ -2,17 +2,27 @@
 // include/moe_layer.h): argument validation, workspace layout, kernel
 // selection and the launch sequence on the caller's HIP stream.
 //
-// Launch sequence (three stages, each one launch on the fast path):
-//   1 route_shared_gateup  router GEMV + shared gate/up; last router
-//                          workgroup: top-k, weights, bucketing
-//   2 gateup               routed gate/up + SwiGLU, shared down
-//   3 down_combine         routed down; last workgroup per row tile combines
-// Shapes outside the fused instantiations, and batches above 16 tokens,
-// take the same steps as separate launches.
+// Two launch sequences:
+//  * flow (MOE_SINGLE_LAUNCH, 1 to 4 tokens, shapes with a k_flow
+//    instantiation): the whole layer is one launch of k_flow, a
+//    dependency-ordered work queue; one stage, "layer".
+//  * staged (everything else), three stages, each one launch where a fused
+//    instantiation exists:
+//      1 route_shared_gateup  router GEMV + shared gate/up; last router
+//                             workgroup: top-k, weights, bucketing
+//      2 gateup               routed gate/up + SwiGLU, shared down
+//      3 down_combine         routed down; last workgroup per row tile
+//                             combines
+//    Shapes outside the fused instantiations, and batches above 16 tokens,
+//    take the same steps as separate launches.
 #include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <unordered_map>
 
 #include "common.h"
 #include "ffn.h"
+#include "flow.h"
 #include "misc.h"
 #include "phases.h"
 #include "route.h"
@@ -21,7 +31,7 @@ using namespace svr;
 
 namespace {
 
-constexpr int kVersion = 200;  // 0.2.0
+constexpr int kVersion = 300;  // 0.3.0
 constexpr int kFusedMaxTokens = 16;
 // Batches up to this size give every (token, slot) pair its own workgroups
 // (equal work per workgroup); larger ones go by expert with token passes.
@@ -29,6 +39,12 @@ constexpr int kPairSlotTokens = 4;
 
 enum Stage { kStPhase1 = 0, kStPhase2, kStPhase3, kNumStages };
 const char* const kStageNames[kNumStages] = {"route_shared_gateup", "gateup", "down_combine"};
+const char* const kFlowStageName = "layer";
+constexpr int kFlowTokens = 4;
+// Weight bytes a routed flow item streams, and bytes each wave of a shared
+// expert item streams (its waves take different tokens over the same rows).
+constexpr double kFlowItemBytes = 256.0 * 1024.0;
+constexpr double kFlowSharedWaveBytes = 64.0 * 1024.0;
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -37,25 +53,40 @@ int blk_of(int dtype) { return dtype == MOE_Q8_0 ? 32 : 256; }
 bool quant_type(int dtype) { return dtype == MOE_Q8_0 || dtype == MOE_Q4_K; }
 int qfmt(int dtype) { return dtype == MOE_Q8_0 ? kQ8_0 : kQ4_K; }
 
-// Lanes per row and 16-byte chunks per lane for a row of K columns.
+// Lanes per row and 16-byte chunks per lane for a row of K columns.  The
+// shape keeps the per-lane activation slice within 96 floats (Q4_K: 3
+// chunks of 32, Q8_0: 6 chunks of 16) where possible and wastes the fewest
+// lane positions (chunk positions past the row's end load the row's last
+// chunk against a zero activation); among equal shapes the fewest chunks
+// per lane.  Rows too long for that take 64 lanes and up to 8 chunks.
 struct FfnShape {
   int lpr, cpl;
 };
 bool ffn_shape(int dtype, int K, FfnShape* s) {
   if (K <= 0 || K % blk_of(dtype)) return false;
   const int chunks = K / wpc_of(dtype);
+  const int cap = dtype == MOE_Q8_0 ? 6 : 3;
+  double best = 0.0;
   for (int lpr = 64; lpr >= 1; lpr >>= 1) {
-    if (chunks % lpr == 0 && chunks / lpr <= kMaxChunksPerLane) {
+    const int cpl = (chunks + lpr - 1) / lpr;
+    if (cpl > cap) continue;
+    const double eff = (double)chunks / (double)(lpr * cpl);
+    if (eff > best + 1e-12) {
+      best = eff;
       s->lpr = lpr;
-      s->cpl = chunks / lpr;
-      return true;
+      s->cpl = cpl;
     }
   }
-  return false;
+  if (best > 0.0) return true;
+  const int cpl = (chunks + kWave - 1) / kWave;
+  if (cpl > kMaxChunksPerLane) return false;
+  s->lpr = kWave;
+  s->cpl = cpl;
+  return true;
 }
 
 struct Plan {
-  int H, E, k, F, Fs, et, st, M;
+  int H, E, k, F, Fs, et, st, M, flags;
   size_t ctr, logits, ids, w, counts, offsets, slots, active, nactive, h, hs, o, s, total;
 };
 
@@ -63,6 +94,7 @@ int check_desc(const moe_layer_desc* d) {
   if (!d) return MOE_ERR_NULL;
   if (d->hidden <= 0 || d->n_experts <= 0 || d->top_k <= 0 || d->ffn <= 0 || d->shared_ffn < 0)
     return MOE_ERR_SHAPE;
+  if (d->flags & ~MOE_SINGLE_LAUNCH) return MOE_ERR_ARG;
   if (!quant_type(d->expert_type)) return MOE_ERR_DTYPE;
   if (d->shared_ffn > 0 && !quant_type(d->shared_type)) return MOE_ERR_DTYPE;
   if (d->n_experts > kMaxExperts) return MOE_ERR_SHAPE;
@@ -87,6 +119,7 @@ int make_plan(const moe_layer_desc* d, int M, Plan* p) {
   p->Fs = d->shared_ffn;
   p->et = d->expert_type;
   p->st = d->shared_type;
+  p->flags = d->flags;
   p->M = M;
   const size_t Mz = (size_t)M, P = Mz * p->k;
   size_t off = 0;
@@ -95,7 +128,7 @@ int make_plan(const moe_layer_desc* d, int M, Plan* p) {
     off = align256(off + bytes);
     return o;
   };
-  p->ctr = take(sizeof(Counters));
+  p->ctr = take(kCounterBytes);
   p->logits = take(Mz * p->E * 4);
   p->ids = take(P * 4);
   p->w = take(P * 4);
@@ -131,16 +164,26 @@ int device_cus() {
   return cache[dev];
 }
 
+// Workgroups of `kernel` resident at once on the device: CUs x the
+// occupancy query, cached per kernel.
 template <typename K>
 int resident_blocks(K kernel) {
-  static int per_cu = 0;  // one value per kernel instantiation
-  if (!per_cu) {
-    int v = 0;
+  static std::mutex mu;
+  static std::unordered_map<const void*, int> per_cu;
+  const void* key = reinterpret_cast<const void*>(kernel);
+  int v = 0;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = per_cu.find(key);
+    if (it != per_cu.end()) v = it->second;
+  }
+  if (!v) {
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, kernel, kBlock, 0) != hipSuccess || v < 1)
       v = 1;
-    per_cu = v;
+    std::lock_guard<std::mutex> lock(mu);
+    per_cu[key] = v;
   }
-  return per_cu * device_cus();
+  return v * device_cus();
 }
 
 // Rows per workgroup for `blocks` workgroups over `slots` experts.
@@ -279,7 +322,16 @@ bool launch_dual(int akey, int bkey, hipStream_t st, const FfnArgs& a, const Ffn
 // Phase 3: routed down + combine, one resident round of row tiles x slots.
 template <int F, int C>
 bool launch_down_combine_t(hipStream_t st, FfnArgs a, const CombineArgs& c, int dtype, int slots) {
-  auto k = k_down_combine<F, C>;
+  const bool pair_lds = a.pair_expert != nullptr;
+  if (pair_lds) {
+    auto k = k_down_combine<F, C, true>;
+    size_role(a, dtype, slots, resident_blocks(k));
+    if (tiles_of(a) <= kMaxTiles && a.units_per_block <= kDownLdsRows) {
+      hipLaunchKernelGGL(k, dim3(tiles_of(a), slots), dim3(kBlock), 0, st, a, c);
+      return true;
+    }
+  }
+  auto k = k_down_combine<F, C, false>;
   size_role(a, dtype, slots, resident_blocks(k));
   const int tiles = tiles_of(a);
   if (tiles > kMaxTiles) return false;
@@ -291,11 +343,72 @@ bool launch_down_combine(int fmt, int cpl, hipStream_t st, const FfnArgs& a, con
                          int dtype, int slots) {
 #define SVR_DC(F, C) \
   if (fmt == F && cpl == C) return launch_down_combine_t<F, C>(st, a, c, dtype, slots);
-  SVR_DC(kQ4_K, 1) SVR_DC(kQ4_K, 2) SVR_DC(kQ4_K, 3) SVR_DC(kQ4_K, 4) SVR_DC(kQ4_K, 5)
-  SVR_DC(kQ4_K, 6) SVR_DC(kQ8_0, 1) SVR_DC(kQ8_0, 2) SVR_DC(kQ8_0, 3) SVR_DC(kQ8_0, 4)
-  SVR_DC(kQ8_0, 5) SVR_DC(kQ8_0, 6)
+  SVR_DC(kQ4_K, 1) SVR_DC(kQ4_K, 2) SVR_DC(kQ4_K, 3) SVR_DC(kQ8_0, 1) SVR_DC(kQ8_0, 2)
+  SVR_DC(kQ8_0, 3) SVR_DC(kQ8_0, 4) SVR_DC(kQ8_0, 5) SVR_DC(kQ8_0, 6)
 #undef SVR_DC
   return false;
+}
+
+// --------------------------------------------------------------------------
+// Flow path.
+// --------------------------------------------------------------------------
+int router_nc(int H) { return H <= 1024 ? 1 : H <= 2048 ? 2 : H <= 4096 ? 4 : H <= 8192 ? 8 : 0; }
+
+struct FlowKey {
+  int nc, sf, sgc, sdc, rf, gc, dc;
+  bool operator==(const FlowKey& o) const {
+    return nc == o.nc && sf == o.sf && sgc == o.sgc && sdc == o.sdc && rf == o.rf && gc == o.gc &&
+           dc == o.dc;
+  }
+};
+
+bool flow_key(const Plan& p, FlowKey* k) {
+  if (!(p.flags & MOE_SINGLE_LAUNCH)) return false;
+  if (p.M < 1 || p.M > kFlowTokens || p.M * p.k > kFlowMaxPairs) return false;
+  FfnShape a{}, b{};
+  if (!(k->nc = router_nc(p.H))) return false;
+  if (!ffn_shape(p.et, p.H, &a) || !ffn_shape(p.et, p.F, &b)) return false;
+  k->rf = qfmt(p.et);
+  k->gc = a.cpl;
+  k->dc = b.cpl;
+  k->sf = 0;
+  k->sgc = k->sdc = 1;
+  if (p.Fs > 0) {
+    if (!ffn_shape(p.st, p.H, &a) || !ffn_shape(p.st, p.Fs, &b)) return false;
+    k->sf = qfmt(p.st);
+    k->sgc = a.cpl;
+    k->sdc = b.cpl;
+  }
+  return true;
+}
+
+// One workgroup per item.
+template <int NC, int SF, int SGC, int SDC, int RF, int GC, int DC>
+void launch_flow_t(const FlowArgs& f, hipStream_t st) {
+  const int64_t total = (int64_t)f.n_r + f.n_sg + f.n_g + f.n_sd + f.n_d;
+  hipLaunchKernelGGL((k_flow<NC, SF, SGC, SDC, RF, GC, DC>), dim3((unsigned)total), dim3(kBlock),
+                     0, st, f);
+}
+
+// True if `key` has an instantiation; launches it when f is given.
+bool flow_dispatch(const FlowKey& key, const FlowArgs* f, hipStream_t st) {
+#define SVR_FLOW_CASE(A, B, C, D, E, G, H)                    \
+  if (key == FlowKey{A, B, C, D, E, G, H}) {                 \
+    if (f) launch_flow_t<A, B, C, D, E, G, H>(*f, st);       \
+    return true;                                             \
+  }
+  SVR_FLOW_VARIANTS(SVR_FLOW_CASE)
+#undef SVR_FLOW_CASE
+  return false;
+}
+
+// Rows per item: about kFlowItemBytes of weights, a whole number of steps.
+int flow_rows(double row_bytes_, int step, int rows, double bytes = kFlowItemBytes) {
+  int r = (int)(bytes / row_bytes_) / step * step;
+  if (r < step) r = step;
+  const int all = (rows + step - 1) / step * step;
+  r = r < all ? r : all;
+  return r <= kFlowLdsOut ? r : kFlowLdsOut / step * step;
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -408,6 +521,87 @@ FfnArgs routed_args(const Plan& p, const Buffers& b, bool gateup, const moe_laye
   return a;
 }
 
+// Work items of the flow path (see flow.h).  Returns false if the shapes
+// do not fit it; fills f (pointers from b) if given.
+bool flow_args(const Plan& p, const moe_layer_weights* wt, const float* x, float* y,
+               const Buffers& b, FlowArgs* f) {
+  FlowKey key;
+  if (!flow_key(p, &key) || !flow_dispatch(key, nullptr, nullptr)) return false;
+  const bool shared = p.Fs > 0;
+  FfnShape gs, ds, sgs{}, sds{};
+  ffn_shape(p.et, p.H, &gs);
+  ffn_shape(p.et, p.F, &ds);
+  if (shared) {
+    ffn_shape(p.st, p.H, &sgs);
+    ffn_shape(p.st, p.Fs, &sds);
+  }
+  const int n_pairs = p.M * p.k;
+  // Routed gate/up: the four waves of an item take different rows.
+  const int g_step = kWavesPerBlock * (kWave / gs.lpr);
+  const int g_rows = flow_rows(2.0 * row_bytes(p.et, p.H), g_step, p.F);
+  // Routed down: output row tiles, which the combine follows.
+  const int d_step = kWavesPerBlock * (kWave / ds.lpr);
+  const int d_rows = flow_rows(row_bytes(p.et, p.F), d_step, p.H);
+  const int d_tiles = (p.H + d_rows - 1) / d_rows;
+  if (d_tiles > kFlowMaxTiles) return false;
+  // Shared expert items: the waves of one token split its rows (4 / M
+  // waves per token), about kFlowSharedWaveBytes per wave.  Shared down
+  // items divide an output row tile into sd_per_tile parts.
+  int sg_rows = 0, sd_rows = 0, sd_per_tile = 1;
+  if (shared) {
+    const int rg = kWavesPerBlock / p.M;
+    const int sg_step = rg * (kWave / sgs.lpr), sd_step = rg * (kWave / sds.lpr);
+    sg_rows = flow_rows(2.0 * row_bytes(p.st, p.H), sg_step, p.Fs, kFlowSharedWaveBytes * rg);
+    if (sg_rows * p.M > kFlowLdsOut) sg_rows = kFlowLdsOut / p.M / sg_step * sg_step;
+    const double sd_target = kFlowSharedWaveBytes * rg / row_bytes(p.st, p.Fs);
+    sd_per_tile = 0;
+    for (int n = 1; n <= d_rows; ++n) {
+      const int rows = d_rows / n;
+      if (d_rows % n || rows % sd_step) continue;
+      if (rows * p.M <= kFlowLdsOut && rows <= sd_target) {
+        sd_per_tile = n;
+        break;
+      }
+    }
+    if (!sd_per_tile || sg_rows < sg_step) return false;
+    sd_rows = d_rows / sd_per_tile;
+  }
+  if (!f) return true;
+
+  *f = FlowArgs{};
+  f->r = RouteArgs{wt->router, x, b.logits, b.ids, b.w, BucketOut{}, p.H, p.E, p.k, p.M, p.E,
+                   nullptr, 0};
+  f->n_pairs = n_pairs;
+  f->g = routed_args(p, b, true, wt, x, true);
+  f->g.lpr = gs.lpr;
+  f->g.units_per_block = g_rows;
+  f->g.coherent_in = 1;  // pair experts come from the top-k
+  f->g_tiles = (p.F + g_rows - 1) / g_rows;
+  f->d = routed_args(p, b, false, wt, x, true);
+  f->d.lpr = ds.lpr;
+  f->d.units_per_block = d_rows;
+  f->d.coherent_in = 1;
+  f->d_tiles = d_tiles;
+  f->sd_per_tile = sd_per_tile;
+  if (shared) {
+    f->sg = shared_gateup_args(p, wt, x, b);
+    f->sg.lpr = sgs.lpr;
+    f->sg.units_per_block = sg_rows;
+    f->n_sg = (p.Fs + sg_rows - 1) / sg_rows;
+    f->sd = shared_down_args(p, wt, b);
+    f->sd.lpr = sds.lpr;
+    f->sd.units_per_block = sd_rows;
+    f->sd.coherent_in = 1;
+    f->n_sd = d_tiles * sd_per_tile;
+  }
+  f->c = CombineArgs{b.o, shared ? b.s : nullptr, b.w, y, p.M, p.H, p.k, nullptr};
+  f->ctr = reinterpret_cast<FlowCounters*>(b.ctr);
+  f->n_r = p.E;
+  f->n_g = n_pairs * f->g_tiles;
+  f->n_d = n_pairs * d_tiles;
+  return true;
+}
+
 int forward_impl(const moe_layer_desc* desc, const moe_layer_weights* wt, const float* x,
                  int32_t n_tokens, float* y, int32_t* topk_ids, float* topk_w, void* workspace,
                  size_t workspace_bytes, void* hip_stream, void* const* events, int32_t n_events) {
@@ -415,11 +609,14 @@ int forward_impl(const moe_layer_desc* desc, const moe_layer_weights* wt, const 
   Plan p;
   int rc = make_plan(desc, n_tokens, &p);
   if (rc != MOE_OK) return rc;
-  if (events && n_events != kNumStages + 1) return MOE_ERR_ARG;
+  const Buffers nob{};
+  const bool flow = flow_args(p, wt, x, y, nob, nullptr);
+  const int n_stages = flow ? 1 : kNumStages;
+  if (events && n_events != n_stages + 1) return MOE_ERR_ARG;
   hipStream_t st = (hipStream_t)hip_stream;
   hipEvent_t* ev = events ? (hipEvent_t*)events : nullptr;
   if (n_tokens == 0) {
-    for (int i = 0; i <= kNumStages; ++i) mark(ev, i, st);
+    for (int i = 0; i <= n_stages; ++i) mark(ev, i, st);
     return MOE_OK;
   }
   if (!x || !y || !wt->router || !wt->gate || !wt->up || !wt->down) return MOE_ERR_NULL;
@@ -434,6 +631,17 @@ int forward_impl(const moe_layer_desc* desc, const moe_layer_weights* wt, const 
     return MOE_ERR_ARG;
 
   const Buffers b = carve(p, workspace, topk_ids, topk_w);
+  if (flow) {
+    FlowArgs f;
+    flow_args(p, wt, x, y, b, &f);
+    FlowKey key;
+    flow_key(p, &key);
+    (void)hipGetLastError();
+    mark(ev, 0, st);
+    flow_dispatch(key, &f, st);
+    mark(ev, 1, st);
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
+  }
   const BucketOut bo{b.counts, b.offsets, b.slots, b.active, b.nactive};
   const bool pairs = p.M <= kPairSlotTokens;
   const int slots_max = pairs ? p.M * p.k : ((p.M * p.k < p.E) ? p.M * p.k : p.E);
@@ -556,10 +764,18 @@ int32_t moe_workspace_bytes(const moe_layer_desc* desc, int32_t max_tokens, size
   return MOE_OK;
 }
 
-int32_t moe_stage_count(void) { return kNumStages; }
+int32_t moe_stage_count(const moe_layer_desc* desc, int32_t n_tokens) {
+  Plan p;
+  const int rc = make_plan(desc, n_tokens, &p);
+  if (rc != MOE_OK) return -rc;
+  const Buffers nob{};
+  return flow_args(p, nullptr, nullptr, nullptr, nob, nullptr) ? 1 : kNumStages;
+}
 
-const char* moe_stage_name(int32_t i) {
-  return (i >= 0 && i < kNumStages) ? kStageNames[i] : nullptr;
+const char* moe_stage_name(const moe_layer_desc* desc, int32_t n_tokens, int32_t i) {
+  const int n = moe_stage_count(desc, n_tokens);
+  if (n <= 0 || i < 0 || i >= n) return nullptr;
+  return n == 1 ? kFlowStageName : kStageNames[i];
 }
 
 int32_t moe_route(const moe_layer_desc* desc, const float* router, const float* x,

@@ -84,23 +84,22 @@ __global__ __launch_bounds__(kBlock) void k_dual(FfnArgs a, int a_tiles, int na,
 }
 
 // Combine of rows [r0, r1) of y: y[t][r] = s[t][r] + sum_j w[t][j] o[t*k+j][r],
-// the expert outputs o coming from other workgroups of the same launch.
-// Each thread takes four consecutive rows of one token and requests the
-// k slots' float4s eight at a time before adding them in slot order.
+// with s, w and the expert outputs o written by other workgroups of the
+// same launch (all read past the per-XCD L2).  Each thread takes four
+// consecutive rows of one token and requests the k slots' float4s eight at
+// a time before adding them in slot order.
 __device__ __forceinline__ void combine_rows(const float* __restrict__ o,
                                              const float* __restrict__ s,
                                              const float* __restrict__ w, float* __restrict__ y,
                                              int M, int H, int k, int r0, int r1) {
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(o, (uint32_t)((int64_t)M * k * H * 4));
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(s, s ? (uint32_t)((int64_t)M * H * 4) : 0u);
   const int n4 = (r1 - r0) >> 2;
   for (int i = threadIdx.x; i < M * n4; i += kBlock) {
     const int t = i / n4;
     const int r = r0 + 4 * (i - t * n4);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (s) {
-      const float4 sv = ldf4(s + (int64_t)t * H + r);
-      acc = f32x4{sv.x, sv.y, sv.z, sv.w};
-    }
+    if (s) acc = bload16_shared(rs, (uint32_t)(((int64_t)t * H + r) * 4));
     for (int j0 = 0; j0 < k; j0 += 8) {
       f32x4 v[8];
 #pragma unroll
@@ -112,7 +111,7 @@ __device__ __forceinline__ void combine_rows(const float* __restrict__ o,
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
         if (j0 + jj < k) {
-          const float wj = w[t * k + j0 + jj];
+          const float wj = load_shared(w + t * k + j0 + jj);
           acc.x = fmaf(wj, v[jj].x, acc.x);
           acc.y = fmaf(wj, v[jj].y, acc.y);
           acc.z = fmaf(wj, v[jj].z, acc.z);
@@ -134,13 +133,28 @@ struct CombineArgs {
 };
 
 // Phase 3: routed down tiles, then the combine of each finished row tile.
-template <int FMT, int CPL>
+// PAIR_LDS (per-pair slots): the tile's outputs are gathered in LDS and
+// written out as one contiguous range after the row loop, so that no store
+// sits between the row loop's loads and their waits.
+constexpr int kDownLdsRows = 2048;
+
+template <int FMT, int CPL, bool PAIR_LDS>
 __global__ __launch_bounds__(kBlock) void k_down_combine(FfnArgs a, CombineArgs c) {
   __shared__ int s_last;
+  __shared__ float s_out[PAIR_LDS ? kDownLdsRows : 1];
   const int tile = blockIdx.x, slot = blockIdx.y;
   const int n_act = a.pair_expert ? a.n_pairs : *a.n_active;
   if (slot >= n_act) return;  // block-uniform; these blocks never count
-  ffn_tile<FMT, CPL, false>(a, slot, tile);  // o rows stored with store_shared
+  if constexpr (PAIR_LDS) {
+    ffn_tile_pair<FMT, CPL, false, 3, true>(a, slot, tile, s_out);
+    __syncthreads();
+    const int ub = tile * a.units_per_block;
+    const int ue = min(ub + a.units_per_block, a.rows_per_expert);
+    float* o = a.out + (int64_t)slot * a.rows_per_expert;
+    for (int r = ub + threadIdx.x; r < ue; r += kBlock) store_shared(o + r, s_out[r - ub]);
+  } else {
+    ffn_tile<FMT, CPL, false>(a, slot, tile);  // o rows stored with store_shared
+  }
   wait_stores();
   __syncthreads();
   if (threadIdx.x == 0) s_last = arrive(&c.ctr->tile_done[tile]) == (unsigned)(n_act - 1);

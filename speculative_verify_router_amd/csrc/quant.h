@@ -109,6 +109,36 @@ __device__ __forceinline__ void load_x(XSlice<FMT>& xs, const float* row, int c)
   xs.sum = (FMT == kQ8_0) ? 128.f * s : s;
 }
 
+// load_x for activations another workgroup of this launch wrote with
+// store_shared: 16-byte loads past the per-XCD L2.  `base` is the start of
+// the activation buffer, `row_off` the row's first element.
+template <int FMT>
+__device__ __forceinline__ void load_x_shared(XSlice<FMT>& xs, const float* base, int row_off,
+                                              int c) {
+  constexpr int W = QTraits<FMT>::kWpc;
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(base, 0x7FFFFFF0u);
+  const uint32_t off = 4u * (uint32_t)(row_off + W * c);
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < W / 4; ++i) {
+    const f32x4 a = bload16_shared(r, off + 16u * i);
+    s += (a.x + a.y) + (a.z + a.w);
+    const float odd = (FMT == kQ4_K) ? 0.0625f : 1.0f;
+    xs.v[4 * i + 0] = a.x;
+    xs.v[4 * i + 1] = a.y * odd;
+    xs.v[4 * i + 2] = a.z;
+    xs.v[4 * i + 3] = a.w * odd;
+  }
+  xs.sum = (FMT == kQ8_0) ? 128.f * s : s;
+}
+
+template <int FMT>
+__device__ __forceinline__ void zero_x(XSlice<FMT>& xs) {
+#pragma unroll
+  for (int i = 0; i < QTraits<FMT>::kWpc; ++i) xs.v[i] = 0.f;
+  xs.sum = 0.f;
+}
+
 // acc += a * dot - b * xs.sum for one chunk: the chunk's contribution.
 struct ChunkScale {
   float a, b;

@@ -18,13 +18,14 @@ namespace svr {
 // of up to four tokens at once (NC per lane), so a row costs about one
 // memory round trip; the four quarter sums are added in a fixed order.
 // ---------------------------------------------------------------------------
+// s_part[wave][row of 16 lanes][token]: partial sums, added in a fixed order.
+typedef float RouterPart[kWavesPerBlock][4][16];
+
+// Part 1: each wave's partial sums of row e for up to 16 tokens into s_part.
 template <int NC>
-__device__ __forceinline__ void router_row_block(const float* __restrict__ router,
-                                                 const float* __restrict__ x,
-                                                 float* __restrict__ logits, int H, int E, int M,
-                                                 int e) {
-  // s_part[wave][row of 16 lanes][token]: partial sums, added in a fixed order.
-  __shared__ float s_part[kWavesPerBlock][4][16];
+__device__ __forceinline__ void router_row_partials(const float* __restrict__ router,
+                                                    const float* __restrict__ x, int H, int M,
+                                                    int e, RouterPart& s_part) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x >> 6;
   const int Q = H >> 4;  // float4 chunks per quarter
@@ -61,7 +62,11 @@ __device__ __forceinline__ void router_row_block(const float* __restrict__ route
       if ((lane & 15) == 15 && t0 + t < M) s_part[wv][lane >> 4][t0 + t] = rs;
     }
   }
-  __syncthreads();
+}
+
+// Part 2, after a barrier: logit of token threadIdx.x < M (fixed order).
+__device__ __forceinline__ void router_row_finish(float* __restrict__ logits, int E, int M, int e,
+                                                  const RouterPart& s_part) {
   if (threadIdx.x < M) {
     float acc = 0.f;
 #pragma unroll
@@ -70,6 +75,17 @@ __device__ __forceinline__ void router_row_block(const float* __restrict__ route
       for (int r = 0; r < 4; ++r) acc += s_part[w4][r][threadIdx.x];
     store_shared(logits + (int64_t)threadIdx.x * E + e, acc);
   }
+}
+
+template <int NC>
+__device__ __forceinline__ void router_row_block(const float* __restrict__ router,
+                                                 const float* __restrict__ x,
+                                                 float* __restrict__ logits, int H, int E, int M,
+                                                 int e) {
+  __shared__ RouterPart s_part;
+  router_row_partials<NC>(router, x, H, M, e, s_part);
+  __syncthreads();
+  router_row_finish(logits, E, M, e, s_part);
 }
 
 // Router GEMV for any batch size (prefill): one wave per router row, tokens
@@ -183,8 +199,13 @@ __device__ __forceinline__ void topk_token_nv(const float* __restrict__ row,
   const float ex = (lane < k) ? __expf(my_v - vmax) : 0.f;
   const float tot = wave_sum(ex);
   if (lane < k) {
-    ids[lane] = my_e;
-    wts[lane] = ex / tot;
+    if (COHERENT) {  // read by other workgroups of the same launch
+      store_shared(ids + lane, (int32_t)my_e);
+      store_shared(wts + lane, ex / tot);
+    } else {
+      ids[lane] = my_e;
+      wts[lane] = ex / tot;
+    }
   }
 }
 

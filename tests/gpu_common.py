@@ -38,13 +38,13 @@ def upload(inp) -> svr.LayerWeights:
     return w
 
 
-def gpu_forward(cfg, weights, x: np.ndarray):
+def gpu_forward(cfg, weights, x: np.ndarray, desc=None):
     M = x.shape[0]
     xd = dev(x.astype(np.float32))
     y = torch.empty((M, cfg.hidden), dtype=torch.float32, device="cuda")
     ids = torch.empty((M, cfg.top_k), dtype=torch.int32, device="cuda")
     tw = torch.empty((M, cfg.top_k), dtype=torch.float32, device="cuda")
-    svr.moe_layer_forward(desc_of(cfg), weights, xd, y, ids, tw)
+    svr.moe_layer_forward(desc or desc_of(cfg), weights, xd, y, ids, tw)
     torch.cuda.synchronize()
     return y.cpu().numpy(), ids.cpu().numpy(), tw.cpu().numpy()
 

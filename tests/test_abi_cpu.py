@@ -33,9 +33,29 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert svr.moe_version() >= 100
     assert svr.moe_strerror(0) == "ok"
     assert svr.moe_strerror(12345) == "unknown status"
-    names = [svr.moe_stage_name(i) for i in range(svr.moe_stage_count())]
-    assert names == ["route_shared_gateup", "gateup", "down_combine"]
-    assert svr.moe_stage_name(-1) is None and svr.moe_stage_name(len(names)) is None
+
+
+
+def _stage_names(desc, M):
+    return [svr.moe_stage_name(desc, M, i) for i in range(svr.moe_stage_count(desc, M))]
+
+
+def test_stage_lists_follow_the_launch_path():
+    # Step-3.5-shaped verify layer: with the single-launch flag one launch for
+    # 1..4 tokens, three stages above; three stages without the flag.
+    d = svr.LayerDesc(4096, 288, 8, 1280, 1280, "q4_k", "q8_0", single_launch=True)
+    for M in (1, 2, 3, 4):
+        assert _stage_names(d, M) == ["layer"]
+        assert _stage_names(svr.LayerDesc(4096, 288, 8, 1280, 1280, "q4_k", "q8_0"), M) == [
+            "route_shared_gateup", "gateup", "down_combine"]
+    for M in (5, 16, 512):
+        assert _stage_names(d, M) == ["route_shared_gateup", "gateup", "down_combine"]
+    # Shapes without a single-launch instantiation take the staged path.
+    odd = svr.LayerDesc(640, 5, 2, 96, 160, "q8_0", "q8_0", single_launch=True)
+    assert _stage_names(odd, 2) == ["route_shared_gateup", "gateup", "down_combine"]
+    assert svr.moe_stage_name(d, 4, -1) is None and svr.moe_stage_name(d, 4, 1) is None
+    with pytest.raises(svr.MoeError):
+        svr.moe_stage_count(svr.LayerDesc(4096, 288, 8, 1000, 0, "q4_k", "q8_0"), 4)
 
 
 def test_missing_library_fails_loudly(monkeypatch):
@@ -85,7 +105,7 @@ def test_workspace_grows_with_tokens():
     (dict(top_k=0), B.ERR_SHAPE),
     (dict(top_k=300), B.ERR_SHAPE),
     (dict(top_k=65, n_experts=100), B.ERR_SHAPE),
-    (dict(hidden=288, expert_type="q8_0", shared_type="q8_0"), B.ERR_SHAPE),  # 18 chunks
+        (dict(hidden=100, expert_type="q8_0", shared_type="q8_0"), B.ERR_SHAPE),  # not k*32
     (dict(expert_type="f32"), B.ERR_DTYPE),
     (dict(shared_type="f32"), B.ERR_DTYPE),
 ])
@@ -161,3 +181,12 @@ def test_route_and_dequant_error_paths():
     assert L.moe_dequant_rows(1, FAKE, 10, 64, 5, 6, FAKE, None) == B.ERR_SHAPE
     assert L.moe_dequant_rows(1, None, 10, 64, 0, 5, FAKE, None) == B.ERR_NULL
     assert L.moe_dequant_rows(1, None, 10, 64, 0, 0, None, None) == B.OK    # empty range
+
+
+def test_unknown_flag_bits_are_rejected():
+    d = _desc().c()
+    d.flags = 2
+    out = ctypes.c_size_t()
+    assert svr.lib().moe_workspace_bytes(ctypes.byref(d), 4, ctypes.byref(out)) == B.ERR_ARG
+    d.flags = B.SINGLE_LAUNCH
+    assert svr.lib().moe_workspace_bytes(ctypes.byref(d), 4, ctypes.byref(out)) == B.OK

@@ -142,6 +142,18 @@ def test_ragged_rows_and_lanes():
                              n_tokens=5, router_std=0.2, seed_index=553))
 
 
+@pytest.mark.parametrize("M", [2, 6])
+def test_partial_lane_groups(M):
+    # H = 288 (18 Q8_0 chunks per gate/up row: 4 lanes x 5 chunks, two
+    # positions past the row end) and F = 1280 Q4_K (40 chunks per down row:
+    # 16 lanes x 3 chunks, eight positions past the end).
+    _layer_case(small_config(hidden=288, n_experts=6, top_k=2, ffn=96, shared_ffn=96,
+                             n_tokens=M, router_std=0.3, seed_index=556 + M))
+    _layer_case(small_config(hidden=512, n_experts=4, top_k=2, ffn=1280, shared_ffn=0,
+                             expert_type="q4_k", n_tokens=M, router_std=0.2,
+                             seed_index=560 + M))
+
+
 def test_all_tokens_on_the_same_experts():
     cfg = small_config(hidden=512, n_experts=16, top_k=4, ffn=256, shared_ffn=128,
                        expert_type="q4_k", n_tokens=8, router_std=0.2, seed_index=554)
@@ -206,7 +218,7 @@ def test_timed_forward_matches_and_records_events():
     x, _ = conditioned_tokens(inp)
     w = upload(inp)
     y0, _, _ = gpu_forward(cfg, w, x)
-    n = svr.moe_stage_count() + 1
+    n = svr.moe_stage_count(desc_of(cfg), 4) + 1
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
     for e in evs:
         e.record()
