@@ -53,6 +53,12 @@ struct FfnArgs {
   int coherent_in;  // 1: act and pair_expert were written earlier in this launch
 };
 
+// A role's lane shape as one template argument: chunks per lane | lanes
+// per row << 8 (lanes per row 0: read from FfnArgs::lpr at run time).
+constexpr int shape_code(int cpl, int lpr) { return cpl | (lpr << 8); }
+constexpr int shape_cpl(int code) { return code & 255; }
+constexpr int shape_lpr(int code) { return code >> 8; }
+
 // Tokens per pass: keep the per-lane activation slice within 64 floats.
 constexpr int tp_for(int fmt, int cpl) {
   return (cpl * (fmt == kQ8_0 ? 16 : 32) <= 16) ? 4 : (cpl * (fmt == kQ8_0 ? 16 : 32) <= 32) ? 2 : 1;
@@ -76,8 +82,8 @@ struct Stage {
 // activation slice, so they add nothing.
 template <int FMT, int CPL, bool GATEUP>
 __device__ __forceinline__ void load_stage(Stage<FMT, CPL, GATEUP>& s, const QPlanes& p0,
-                                           const QPlanes& p1, uint32_t row, const int (&cc)[CPL]) {
-  const uint32_t qo = row * p0.qrow, so = row * p0.srow;
+                                           const QPlanes& p1, uint32_t qo, uint32_t so,
+                                           const int (&cc)[CPL]) {
 #pragma unroll
   for (int ci = 0; ci < CPL; ++ci) {
     load_chunk(s.c0[ci], p0, qo, so, cc[ci]);
@@ -93,12 +99,13 @@ struct LdsOut {
   int row0, ld;
 };
 
-template <int FMT, int CPL, int NT, bool GATEUP, bool LDSOUT>
+template <int FMT, int CPL, int NT, bool GATEUP, bool LDSOUT, int LPR>
 __device__ __forceinline__ void compute_stage(const Stage<FMT, CPL, GATEUP>& s,
                                               const XSlice<FMT> (&xs)[NT][CPL], const FfnArgs& a,
-                                              int j, int lpr, int u, bool ok,
+                                              int j, int lpr_rt, int u, bool ok,
                                               const int (&out_row)[NT], const int (&cc)[CPL],
                                               const LdsOut& lo, const int (&slot)[NT]) {
+  const int lpr = LPR ? LPR : lpr_rt;
   float acc0[NT], acc1[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc0[t] = acc1[t] = 0.f;
@@ -138,13 +145,14 @@ __device__ __forceinline__ void compute_stage(const Stage<FMT, CPL, GATEUP>& s,
 // One pass of a wave over rows first, first+step, ... < ue of `expert`, for
 // the NT tokens whose pair ids are given (LDSOUT: outputs to lo, token t of
 // the pass in slot lds_slot[t]).
-template <int FMT, int CPL, int NT, bool GATEUP, int NSTMAX = 3, bool LDSOUT = false>
+// LPR: lanes per row when known at compile time (0: a.lpr).
+template <int FMT, int CPL, int NT, bool GATEUP, int NSTMAX = 3, bool LDSOUT = false, int LPR = 0>
 __device__ __forceinline__ void ffn_pass(const FfnArgs& a, int expert, const int* pair_ids,
                                          int first, int step, int ue, LdsOut lo = LdsOut{},
                                          const int* lds_slot = nullptr) {
   constexpr int NST = nst_for(FMT, CPL, GATEUP) < NSTMAX ? nst_for(FMT, CPL, GATEUP) : NSTMAX;
   const int lane = threadIdx.x & (kWave - 1);
-  const int lpr = a.lpr;
+  const int lpr = LPR ? LPR : a.lpr;
   const int g = lane / lpr;
   const int j = lane - g * lpr;
   if (first >= ue) return;  // wave-uniform
@@ -185,78 +193,97 @@ __device__ __forceinline__ void ffn_pass(const FfnArgs& a, int expert, const int
   // clamped to the tile's last row (a line already fetched), so the wait
   // before each step counts a fixed number of loads issued after it.  Rows
   // at or past `ue` are computed but not written.
-  const int last = ue - 1;
+  // Plane offsets advance by a fixed amount per step; clamping an offset
+  // to the last row's is clamping the row (both are increasing in it).
+  const uint32_t q_last = (uint32_t)(ue - 1) * p0.qrow, s_last = (uint32_t)(ue - 1) * p0.srow;
+  const uint32_t q_step = (uint32_t)step * p0.qrow, s_step = (uint32_t)step * p0.srow;
+  uint32_t q_pre = (uint32_t)(first + g) * p0.qrow, s_pre = (uint32_t)(first + g) * p0.srow;
   Stage<FMT, CPL, GATEUP> S[NST];
 #pragma unroll
-  for (int s = 0; s < NST - 1; ++s)
-    load_stage(S[s], p0, p1, (uint32_t)min(first + s * step + g, last), cc);
+  for (int s = 0; s < NST - 1; ++s) {
+    load_stage(S[s], p0, p1, min(q_pre, q_last), min(s_pre, s_last), cc);
+    q_pre += q_step;
+    s_pre += s_step;
+  }
   for (int base = first; base < ue; base += NST * step) {
 #pragma unroll
     for (int s = 0; s < NST; ++s) {
       const int cur = base + s * step;
-      const int pre = cur + (NST - 1) * step;
-      load_stage(S[(s + NST - 1) % NST], p0, p1, (uint32_t)min(pre + g, last), cc);
-      compute_stage<FMT, CPL, NT, GATEUP, LDSOUT>(S[s], xs, a, j, lpr, cur + g, cur + g < ue,
-                                                  out_row, cc, lo, slot);
+      load_stage(S[(s + NST - 1) % NST], p0, p1, min(q_pre, q_last), min(s_pre, s_last), cc);
+      q_pre += q_step;
+      s_pre += s_step;
+      compute_stage<FMT, CPL, NT, GATEUP, LDSOUT, LPR>(S[s], xs, a, j, lpr, cur + g, cur + g < ue,
+                                                       out_row, cc, lo, slot);
     }
   }
 }
 
-template <int FMT, int CPL, int TP, bool GATEUP>
+template <int FMT, int CPL, int TP, bool GATEUP, int LPR>
 __device__ __forceinline__ void ffn_pass_nt(const FfnArgs& a, int expert, const int* ids, int nt,
                                             int first, int step, int ue) {
   if (nt >= TP) {
-    ffn_pass<FMT, CPL, TP, GATEUP>(a, expert, ids, first, step, ue);
+    ffn_pass<FMT, CPL, TP, GATEUP, 3, false, LPR>(a, expert, ids, first, step, ue);
   } else if (TP > 1 && nt == 1) {
-    ffn_pass<FMT, CPL, 1, GATEUP>(a, expert, ids, first, step, ue);
+    ffn_pass<FMT, CPL, 1, GATEUP, 3, false, LPR>(a, expert, ids, first, step, ue);
   } else if (TP > 2 && nt == 2) {
-    ffn_pass<FMT, CPL, (TP > 2 ? 2 : 1), GATEUP>(a, expert, ids, first, step, ue);
+    ffn_pass<FMT, CPL, (TP > 2 ? 2 : 1), GATEUP, 3, false, LPR>(a, expert, ids, first, step, ue);
   } else if (TP > 3 && nt == 3) {
-    ffn_pass<FMT, CPL, (TP > 3 ? 3 : 1), GATEUP>(a, expert, ids, first, step, ue);
+    ffn_pass<FMT, CPL, (TP > 3 ? 3 : 1), GATEUP, 3, false, LPR>(a, expert, ids, first, step, ue);
   }
 }
 
 // Pair slots: rows [tile * units_per_block, ...) of the expert of (token,
 // slot) pair `slot`, the four waves taking different rows.
-template <int FMT, int CPL, bool GATEUP, int NSTMAX = 3, bool LDSOUT = false>
+template <int FMT, int CPL, bool GATEUP, int NSTMAX = 3, bool LDSOUT = false, int LPR = 0>
 __device__ __forceinline__ void ffn_tile_pair(const FfnArgs& a, int slot, int tile,
                                               float* lds = nullptr) {
   if (slot >= a.n_pairs) return;
   const int ub = tile * a.units_per_block;
   const int ue = min(ub + a.units_per_block, a.rows_per_expert);
   if (ub >= ue) return;
-  const int G = kWave / a.lpr;
+  const int G = kWave / (LPR ? LPR : a.lpr);
   const int ids1[1] = {slot}, slot0[1] = {0};
   const int e = a.coherent_in ? load_shared(a.pair_expert + slot) : a.pair_expert[slot];
-  ffn_pass<FMT, CPL, 1, GATEUP, NSTMAX, LDSOUT>(a, e, ids1, ub + (threadIdx.x >> 6) * G,
-                                                kWavesPerBlock * G, ue,
-                                                LdsOut{lds, ub, a.units_per_block}, slot0);
+  ffn_pass<FMT, CPL, 1, GATEUP, NSTMAX, LDSOUT, LPR>(a, e, ids1, ub + (threadIdx.x >> 6) * G,
+                                                     kWavesPerBlock * G, ue,
+                                                     LdsOut{lds, ub, a.units_per_block}, slot0);
 }
 
 // One expert for the identity token list (the shared expert): rows
-// [tile * units_per_block, ...) for tokens wv, wv + 4, ... of wave wv, one
-// token per pass, so the four waves stream the same rows.
-template <int FMT, int CPL, bool GATEUP, int NSTMAX = 3>
+// [tile * units_per_block, ...) for every token.  With up to four tokens
+// the waves form one group of 4 / M waves per token that share its rows
+// (M = 3: one wave idles); with more, wave w takes tokens w, w + 4, ...
+// over all rows.  So the rows are fetched from HBM once per workgroup and
+// idle waves of a small batch still stream.
+template <int FMT, int CPL, bool GATEUP, int NSTMAX = 3, int LPR = 0>
 __device__ __forceinline__ void ffn_tile_tokens(const FfnArgs& a, int tile) {
   const int ub = tile * a.units_per_block;
   const int ue = min(ub + a.units_per_block, a.rows_per_expert);
   if (ub >= ue) return;
-  const int G = kWave / a.lpr;
-  for (int t = threadIdx.x >> 6; t < a.n_tokens; t += kWavesPerBlock) {
+  const int G = kWave / (LPR ? LPR : a.lpr);
+  const int wv = threadIdx.x >> 6;
+  if (a.n_tokens <= kWavesPerBlock) {
+    const int rg = kWavesPerBlock / a.n_tokens;
+    const int t = wv / rg, q = wv - t * rg;
     const int ids1[1] = {t};
-    ffn_pass<FMT, CPL, 1, GATEUP, NSTMAX>(a, 0, ids1, ub, G, ue);
+    if (t < a.n_tokens) ffn_pass<FMT, CPL, 1, GATEUP, NSTMAX, false, LPR>(a, 0, ids1, ub + q * G, rg * G, ue);
+    return;
+  }
+  for (int t = wv; t < a.n_tokens; t += kWavesPerBlock) {
+    const int ids1[1] = {t};
+    ffn_pass<FMT, CPL, 1, GATEUP, NSTMAX, false, LPR>(a, 0, ids1, ub, G, ue);
   }
 }
 
 // Work of workgroup (tile, slot): rows [tile * units_per_block, ...) of the
 // expert in `slot`, for every token routed to it.
-template <int FMT, int CPL, bool GATEUP>
+template <int FMT, int CPL, bool GATEUP, int LPR = 0>
 __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int slot, int tile) {
   constexpr int TP = tp_for(FMT, CPL);
   const int ub = tile * a.units_per_block;
   if (a.pair_expert) {
     // One (token, slot) pair per slot: every workgroup does the same work.
-    ffn_tile_pair<FMT, CPL, GATEUP>(a, slot, tile);
+    ffn_tile_pair<FMT, CPL, GATEUP, 3, false, LPR>(a, slot, tile);
     return;
   }
   if (a.n_active && slot >= *a.n_active) return;
@@ -266,18 +293,10 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int slot, int tile) {
   const int ue = min(ub + a.units_per_block, a.rows_per_expert);
   if (ub >= ue || count <= 0) return;
   const int wv = threadIdx.x >> 6;
-  const int G = kWave / a.lpr;
+  const int G = kWave / (LPR ? LPR : a.lpr);
   int ids[TP];
   if (a.split_tokens) {
-    // Wave wv takes passes wv, wv + 4, ... over all rows of the tile.
-    for (int p0 = wv * TP; p0 < count; p0 += kWavesPerBlock * TP) {
-#pragma unroll
-      for (int t = 0; t < TP; ++t) {
-        const int q = min(p0 + t, count - 1);
-        ids[t] = a.slots ? a.slots[begin + q] : q;
-      }
-      ffn_pass_nt<FMT, CPL, TP, GATEUP>(a, expert, ids, min(TP, count - p0), ub, G, ue);
-    }
+    ffn_tile_tokens<FMT, CPL, GATEUP, 3, LPR>(a, tile);
   } else {
     for (int p0 = 0; p0 < count; p0 += TP) {
 #pragma unroll
@@ -285,7 +304,7 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int slot, int tile) {
         const int q = min(p0 + t, count - 1);
         ids[t] = a.slots ? a.slots[begin + q] : q;
       }
-      ffn_pass_nt<FMT, CPL, TP, GATEUP>(a, expert, ids, min(TP, count - p0), ub + wv * G,
+      ffn_pass_nt<FMT, CPL, TP, GATEUP, LPR>(a, expert, ids, min(TP, count - p0), ub + wv * G,
                                         kWavesPerBlock * G, ue);
     }
   }

@@ -86,14 +86,14 @@ __device__ __forceinline__ int flow_poll(const unsigned* p, unsigned target, uns
 }
 
 // Instantiated k_flow variants: (router NC, shared format, shared gate/up
-// and down chunks per lane, routed format, routed gate/up and down chunks
-// per lane).  H = 4096 with F = Fs = 1280 or 1536, Q4_K or Q8_0 routed,
+// and down shape codes, routed format, routed gate/up and down shape
+// codes).  H = 4096 with F = Fs = 1280 or 1536, Q4_K or Q8_0 routed,
 // Q8_0 shared; and H <= 1024 with small Q8_0 experts and no shared expert.
-#define SVR_FLOW_VARIANTS(X)     \
-  X(4, kQ8_0, 4, 5, kQ4_K, 2, 3) \
-  X(4, kQ8_0, 4, 3, kQ4_K, 2, 3) \
-  X(4, kQ8_0, 4, 5, kQ8_0, 4, 5) \
-  X(1, 0, 1, 1, kQ8_0, 1, 1)
+#define SVR_FLOW_VARIANTS(X)                                                               \
+  X(4, kQ8_0, shape_code(4, 64), shape_code(5, 16), kQ4_K, shape_code(2, 64), shape_code(3, 16)) \
+  X(4, kQ8_0, shape_code(4, 64), shape_code(3, 32), kQ4_K, shape_code(2, 64), shape_code(3, 16)) \
+  X(4, kQ8_0, shape_code(4, 64), shape_code(5, 16), kQ8_0, shape_code(4, 64), shape_code(5, 16)) \
+  X(1, 0, shape_code(1, 0), shape_code(1, 0), kQ8_0, shape_code(1, 16), shape_code(1, 8))
 
 enum FlowKind { kItemRouter = 0, kItemSharedGateUp, kItemGateUp, kItemSharedDown, kItemDown };
 
@@ -101,17 +101,18 @@ enum FlowKind { kItemRouter = 0, kItemSharedGateUp, kItemGateUp, kItemSharedDown
 // (token t in slot t).  The waves are split into M token groups of
 // 4 / M waves (M <= 4) that divide the rows among them; with M = 3 one wave
 // idles.  No wave-dependent loop: each wave runs at most one pass.
-template <int FMT, int CPL, bool GATEUP>
+template <int FMT, int S, bool GATEUP>
 __device__ __forceinline__ void flow_shared_tile(const FfnArgs& a, int tile, float* lds) {
+  constexpr int CPL = shape_cpl(S), LPR = shape_lpr(S);
   const int ub = tile * a.units_per_block;
   const int ue = min(ub + a.units_per_block, a.rows_per_expert);
-  const int G = kWave / a.lpr;
+  const int G = kWave / (LPR ? LPR : a.lpr);
   const int wv = threadIdx.x >> 6;
   const int rg = kWavesPerBlock / a.n_tokens;  // waves per token
   const int t = wv / rg, q = wv - t * rg;
   const int ids1[1] = {t};
   if (t < a.n_tokens && ub + q * G < ue)
-    ffn_pass<FMT, CPL, 1, GATEUP, 3, true>(a, 0, ids1, ub + q * G, rg * G, ue,
+    ffn_pass<FMT, CPL, 1, GATEUP, 3, true, LPR>(a, 0, ids1, ub + q * G, rg * G, ue,
                                            LdsOut{lds, ub, a.units_per_block}, ids1);
 }
 
@@ -126,9 +127,9 @@ __device__ __forceinline__ void flow_copy_out(const float* lds, int ld, float* o
   }
 }
 
-// NC: router float4 chunks per lane; S*: shared format and chunks per lane
-// of gate/up (SGC) and down (SDC), SF == 0 without a shared expert; R*:
-// routed format and chunks per lane of gate/up (GC) and down (DC).
+// NC: router float4 chunks per lane; SF: shared format (0: no shared
+// expert) with gate/up and down shape codes SGC, SDC; RF: routed format
+// with gate/up and down shape codes GC, DC.
 //
 // One workgroup per item.  It takes its item from the queue counter when it
 // starts, so items are handed out in queue order to workgroups that are
@@ -188,8 +189,10 @@ __global__ __launch_bounds__(kBlock) void k_flow(FlowArgs f) {
       if (kind == kItemSharedGateUp) flow_shared_tile<SF, SGC, true>(f.sg, tile, s_out);
       if (kind == kItemSharedDown) flow_shared_tile<SF, SDC, false>(f.sd, tile, s_out);
     }
-    if (kind == kItemGateUp) ffn_tile_pair<RF, GC, true, 3, true>(f.g, pair, tile, s_out);
-    if (kind == kItemDown) ffn_tile_pair<RF, DC, false, 3, true>(f.d, pair, tile, s_out);
+    if (kind == kItemGateUp)
+      ffn_tile_pair<RF, shape_cpl(GC), true, 3, true, shape_lpr(GC)>(f.g, pair, tile, s_out);
+    if (kind == kItemDown)
+      ffn_tile_pair<RF, shape_cpl(DC), false, 3, true, shape_lpr(DC)>(f.d, pair, tile, s_out);
   }
   // B3: the router's partial sums and the item's LDS outputs are complete.
   __syncthreads();

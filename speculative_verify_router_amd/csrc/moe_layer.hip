@@ -205,6 +205,21 @@ void size_role(FfnArgs& a, int dtype, int slots, int64_t blocks) {
   a.units_per_block = (int)upb;
 }
 
+// Shared-expert tiles sized by the bytes each wave streams: a wave's token
+// group of 4 / M waves shares a tile's rows (see ffn_tile_tokens).
+constexpr double kSharedWaveBytes = 24.0 * 1024.0;
+void size_shared_tiles(FfnArgs& a, int dtype, bool gateup, double wave_bytes) {
+  FfnShape s;
+  ffn_shape(dtype, a.K, &s);
+  a.lpr = s.lpr;
+  const int G = kWave / s.lpr;
+  const int rg = a.n_tokens < kWavesPerBlock ? kWavesPerBlock / a.n_tokens : 1;
+  const double rb = (gateup ? 2.0 : 1.0) * (dtype == MOE_Q8_0 ? a.K / 32 * 34.0 : a.K / 256 * 144.0);
+  int rows = (int)(wave_bytes * rg / rb) / (rg * G) * (rg * G);
+  if (rows < rg * G) rows = rg * G;
+  a.units_per_block = rows;
+}
+
 int tiles_of(const FfnArgs& a) {
   return (a.rows_per_expert + a.units_per_block - 1) / a.units_per_block;
 }
@@ -239,39 +254,54 @@ bool launch_ffn(int dtype, bool gateup, FfnArgs a, int slots_max, hipStream_t st
                 : launch_ffn_c<kQ4_K, false>(s.cpl, a, dtype, slots_max, st);
 }
 
-// Fused instantiations.  A key packs (format, chunks per lane).
-constexpr int key(int fmt, int cpl) { return fmt * 16 + cpl; }
+// Fused instantiations.  A key packs (format, shape code); each launcher
+// tries the exact lane shape first (lanes per row fixed at compile time),
+// then a generic instantiation with the same chunks per lane that reads the
+// lanes per row at run time.
+constexpr int key(int fmt, int code) { return fmt * 65536 + code; }
+int exact_key(int dtype, const FfnShape& s) { return key(qfmt(dtype), shape_code(s.cpl, s.lpr)); }
+int generic_key(int dtype, const FfnShape& s) { return key(qfmt(dtype), shape_code(s.cpl, 0)); }
 
-// Phase 1: router rows (NC float4 per lane) + shared gate/up.  The shared
-// tiles get the residency the E router workgroups leave free (at least half).
+// Phase 1: router rows (NC float4 per lane) + shared gate/up in small tiles
+// (about kSharedWaveBytes per wave), which also fill the slots the router
+// workgroups free.
 template <int NC>
 bool launch_phase1_nc(int skey, hipStream_t st, const RouteArgs& r, FfnArgs s, int sdtype) {
   switch (skey) {
-#define SVR_P1(F, C)                                                                     \
-  case key(F, C): {                                                                      \
-    auto k = k_phase1<NC, F, C>;                                                         \
-    const int64_t cap = resident_blocks(k);                                              \
-    size_role(s, sdtype, 1, cap - r.n_router_blocks > cap / 2 ? cap - r.n_router_blocks : cap / 2); \
+#define SVR_P1(F, C, L)                                                                  \
+  case key(F, shape_code(C, L)): {                                                       \
+    auto k = k_phase1<NC, F, shape_code(C, L)>;                                          \
+    size_shared_tiles(s, sdtype, true, kSharedWaveBytes);                               \
     hipLaunchKernelGGL(k, dim3(r.n_router_blocks + tiles_of(s)), dim3(kBlock), 0, st, r, s); \
     return true;                                                                         \
   }
     case 0:
       hipLaunchKernelGGL((k_phase1<NC, 0, 1>), dim3(r.n_router_blocks), dim3(kBlock), 0, st, r, s);
       return true;
-    SVR_P1(kQ8_0, 1) SVR_P1(kQ8_0, 2) SVR_P1(kQ8_0, 4) SVR_P1(kQ4_K, 1) SVR_P1(kQ4_K, 2)
+    SVR_P1(kQ8_0, 4, 64)
+    SVR_P1(kQ8_0, 1, 0) SVR_P1(kQ8_0, 2, 0) SVR_P1(kQ8_0, 4, 0) SVR_P1(kQ8_0, 5, 0)
+    SVR_P1(kQ4_K, 1, 0) SVR_P1(kQ4_K, 2, 0)
 #undef SVR_P1
     default: return false;
   }
 }
 
 // NC: float4 chunks per lane in a quarter row (H/16 chunks per quarter).
-bool launch_phase1(int H, int skey, hipStream_t st, const RouteArgs& r, const FfnArgs& s,
-                   int sdtype) {
+bool launch_phase1_k(int H, int skey, hipStream_t st, const RouteArgs& r, const FfnArgs& s,
+                     int sdtype) {
   if (H <= 1024) return launch_phase1_nc<1>(skey, st, r, s, sdtype);
   if (H <= 2048) return launch_phase1_nc<2>(skey, st, r, s, sdtype);
   if (H <= 4096) return launch_phase1_nc<4>(skey, st, r, s, sdtype);
   if (H <= 8192) return launch_phase1_nc<8>(skey, st, r, s, sdtype);
   return false;
+}
+
+// sshape: the shared gate/up lane shape (ignored without a shared expert).
+bool launch_phase1(int H, bool shared, int sdtype, const FfnShape& sshape, hipStream_t st,
+                   const RouteArgs& r, const FfnArgs& s) {
+  if (!shared) return launch_phase1_k(H, 0, st, r, s, sdtype);
+  return launch_phase1_k(H, exact_key(sdtype, sshape), st, r, s, sdtype) ||
+         launch_phase1_k(H, generic_key(sdtype, sshape), st, r, s, sdtype);
 }
 
 // Phase 2: routed gate/up (A) + shared down (B) in one grid.  The resident
@@ -283,9 +313,9 @@ struct DualPlan {
   int adtype, bdtype;
 };
 
-template <int FA, int CA, int FB, int CB>
+template <int FA, int SA, int FB, int SB>
 void launch_dual_t(hipStream_t st, FfnArgs a, FfnArgs b, const DualPlan& d) {
-  auto k = k_dual<FA, CA, true, FB, CB, false>;
+  auto k = k_dual<FA, SA, true, FB, SB, false>;
   const int64_t cap = resident_blocks(k);
   int64_t bb = (int64_t)((double)cap * d.b_work / (double)(d.a_work + d.b_work) + 0.5);
   if (bb < 1) bb = 1;
@@ -296,42 +326,43 @@ void launch_dual_t(hipStream_t st, FfnArgs a, FfnArgs b, const DualPlan& d) {
   hipLaunchKernelGGL(k, dim3(na + tiles_of(b)), dim3(kBlock), 0, st, a, at, na, b);
 }
 
-template <int FA, int CA>
-bool launch_dual_b(int bkey, hipStream_t st, const FfnArgs& a, const FfnArgs& b,
-                   const DualPlan& d) {
-  switch (bkey) {
-#define SVR_D(F, C) \
-  case key(F, C): launch_dual_t<FA, CA, F, C>(st, a, b, d); return true;
-    SVR_D(kQ8_0, 1) SVR_D(kQ8_0, 2) SVR_D(kQ8_0, 3) SVR_D(kQ8_0, 4) SVR_D(kQ8_0, 5)
-#undef SVR_D
-    default: return false;
+bool launch_dual_keys(int akey, int bkey, hipStream_t st, const FfnArgs& a, const FfnArgs& b,
+                      const DualPlan& d) {
+#define SVR_D(FA, CA, LA, FB, CB, LB)                                                   \
+  if (akey == key(FA, shape_code(CA, LA)) && bkey == key(FB, shape_code(CB, LB))) {    \
+    launch_dual_t<FA, shape_code(CA, LA), FB, shape_code(CB, LB)>(st, a, b, d);        \
+    return true;                                                                         \
   }
+#define SVR_DG(FA, CA)                                                                  \
+  SVR_D(FA, CA, 0, kQ8_0, 1, 0) SVR_D(FA, CA, 0, kQ8_0, 2, 0) SVR_D(FA, CA, 0, kQ8_0, 3, 0) \
+  SVR_D(FA, CA, 0, kQ8_0, 5, 0)
+  SVR_D(kQ4_K, 2, 64, kQ8_0, 5, 16) SVR_D(kQ4_K, 2, 64, kQ8_0, 3, 32)
+  SVR_D(kQ8_0, 4, 64, kQ8_0, 5, 16) SVR_D(kQ8_0, 4, 64, kQ8_0, 3, 32)
+  SVR_DG(kQ4_K, 1) SVR_DG(kQ4_K, 2) SVR_DG(kQ4_K, 3) SVR_DG(kQ8_0, 4)
+#undef SVR_DG
+#undef SVR_D
+  return false;
 }
 
-bool launch_dual(int akey, int bkey, hipStream_t st, const FfnArgs& a, const FfnArgs& b,
-                 const DualPlan& d) {
-  switch (akey) {
-    case key(kQ4_K, 1): return launch_dual_b<kQ4_K, 1>(bkey, st, a, b, d);
-    case key(kQ4_K, 2): return launch_dual_b<kQ4_K, 2>(bkey, st, a, b, d);
-    case key(kQ8_0, 2): return launch_dual_b<kQ8_0, 2>(bkey, st, a, b, d);
-    case key(kQ8_0, 4): return launch_dual_b<kQ8_0, 4>(bkey, st, a, b, d);
-    default: return false;
-  }
+bool launch_dual(int adtype, const FfnShape& as, int bdtype, const FfnShape& bs, hipStream_t st,
+                 const FfnArgs& a, const FfnArgs& b, const DualPlan& d) {
+  return launch_dual_keys(exact_key(adtype, as), exact_key(bdtype, bs), st, a, b, d) ||
+         launch_dual_keys(generic_key(adtype, as), generic_key(bdtype, bs), st, a, b, d);
 }
 
 // Phase 3: routed down + combine, one resident round of row tiles x slots.
-template <int F, int C>
+template <int F, int S>
 bool launch_down_combine_t(hipStream_t st, FfnArgs a, const CombineArgs& c, int dtype, int slots) {
   const bool pair_lds = a.pair_expert != nullptr;
   if (pair_lds) {
-    auto k = k_down_combine<F, C, true>;
+    auto k = k_down_combine<F, S, true>;
     size_role(a, dtype, slots, resident_blocks(k));
     if (tiles_of(a) <= kMaxTiles && a.units_per_block <= kDownLdsRows) {
       hipLaunchKernelGGL(k, dim3(tiles_of(a), slots), dim3(kBlock), 0, st, a, c);
       return true;
     }
   }
-  auto k = k_down_combine<F, C, false>;
+  auto k = k_down_combine<F, S, false>;
   size_role(a, dtype, slots, resident_blocks(k));
   const int tiles = tiles_of(a);
   if (tiles > kMaxTiles) return false;
@@ -339,14 +370,21 @@ bool launch_down_combine_t(hipStream_t st, FfnArgs a, const CombineArgs& c, int 
   return true;
 }
 
-bool launch_down_combine(int fmt, int cpl, hipStream_t st, const FfnArgs& a, const CombineArgs& c,
-                         int dtype, int slots) {
-#define SVR_DC(F, C) \
-  if (fmt == F && cpl == C) return launch_down_combine_t<F, C>(st, a, c, dtype, slots);
-  SVR_DC(kQ4_K, 1) SVR_DC(kQ4_K, 2) SVR_DC(kQ4_K, 3) SVR_DC(kQ8_0, 1) SVR_DC(kQ8_0, 2)
-  SVR_DC(kQ8_0, 3) SVR_DC(kQ8_0, 4) SVR_DC(kQ8_0, 5) SVR_DC(kQ8_0, 6)
+bool launch_down_combine_key(int k, hipStream_t st, const FfnArgs& a, const CombineArgs& c,
+                             int dtype, int slots) {
+#define SVR_DC(F, C, L) \
+  if (k == key(F, shape_code(C, L))) return launch_down_combine_t<F, shape_code(C, L)>(st, a, c, dtype, slots);
+  SVR_DC(kQ4_K, 3, 16) SVR_DC(kQ8_0, 5, 16)
+  SVR_DC(kQ4_K, 1, 0) SVR_DC(kQ4_K, 2, 0) SVR_DC(kQ4_K, 3, 0) SVR_DC(kQ8_0, 1, 0) SVR_DC(kQ8_0, 2, 0)
+  SVR_DC(kQ8_0, 3, 0) SVR_DC(kQ8_0, 4, 0) SVR_DC(kQ8_0, 5, 0) SVR_DC(kQ8_0, 6, 0)
 #undef SVR_DC
   return false;
+}
+
+bool launch_down_combine(int dtype, const FfnShape& ds, hipStream_t st, const FfnArgs& a,
+                         const CombineArgs& c, int slots) {
+  return launch_down_combine_key(exact_key(dtype, ds), st, a, c, dtype, slots) ||
+         launch_down_combine_key(generic_key(dtype, ds), st, a, c, dtype, slots);
 }
 
 // --------------------------------------------------------------------------
@@ -369,15 +407,15 @@ bool flow_key(const Plan& p, FlowKey* k) {
   if (!(k->nc = router_nc(p.H))) return false;
   if (!ffn_shape(p.et, p.H, &a) || !ffn_shape(p.et, p.F, &b)) return false;
   k->rf = qfmt(p.et);
-  k->gc = a.cpl;
-  k->dc = b.cpl;
+  k->gc = shape_code(a.cpl, a.lpr);
+  k->dc = shape_code(b.cpl, b.lpr);
   k->sf = 0;
-  k->sgc = k->sdc = 1;
+  k->sgc = k->sdc = shape_code(1, 0);
   if (p.Fs > 0) {
     if (!ffn_shape(p.st, p.H, &a) || !ffn_shape(p.st, p.Fs, &b)) return false;
     k->sf = qfmt(p.st);
-    k->sgc = a.cpl;
-    k->sdc = b.cpl;
+    k->sgc = shape_code(a.cpl, a.lpr);
+    k->sdc = shape_code(b.cpl, b.lpr);
   }
   return true;
 }
@@ -659,12 +697,11 @@ int forward_impl(const moe_layer_desc* desc, const moe_layer_weights* wt, const 
   bool fused1 = false;
   if (p.M <= kFusedMaxTokens) {
     RouteArgs r{wt->router, x, b.logits, b.ids, b.w, bo, p.H, p.E, p.k, p.M, p.E, b.ctr, !pairs};
-    const int skey = shared ? key(qfmt(p.st), ss.cpl) : 0;
-    fused1 = launch_phase1(p.H, skey, st, r, sgu, p.st);
+    fused1 = launch_phase1(p.H, shared, p.st, ss, st, r, sgu);
     if (!fused1 && shared) {
       // No fused instantiation for this shared shape: route alone, then the
       // shared gate/up as its own launch.
-      fused1 = launch_phase1(p.H, 0, st, r, sgu, p.st);
+      fused1 = launch_phase1(p.H, false, p.st, ss, st, r, sgu);
       if (fused1 && !launch_ffn(p.st, true, sgu, 1, st)) return MOE_ERR_SHAPE;
     }
   }
@@ -689,7 +726,7 @@ int forward_impl(const moe_layer_desc* desc, const moe_layer_weights* wt, const 
       dp.slots = slots_max;
       dp.adtype = p.et;
       dp.bdtype = p.st;
-      done = launch_dual(key(qfmt(p.et), rs.cpl), key(qfmt(p.st), ds.cpl), st, rgu, sd, dp);
+      done = launch_dual(p.et, rs, p.st, ds, st, rgu, sd, dp);
       if (!done) {
         if (!launch_ffn(p.et, true, rgu, slots_max, st)) return MOE_ERR_SHAPE;
         if (!launch_ffn(p.st, false, sd, 1, st)) return MOE_ERR_SHAPE;
@@ -707,7 +744,7 @@ int forward_impl(const moe_layer_desc* desc, const moe_layer_weights* wt, const 
     FfnShape ds;
     ffn_shape(p.et, p.F, &ds);
     CombineArgs c{b.o, shared ? b.s : nullptr, b.w, y, p.M, p.H, p.k, b.ctr};
-    if (!launch_down_combine(qfmt(p.et), ds.cpl, st, rd, c, p.et, slots_max)) {
+    if (!launch_down_combine(p.et, ds, st, rd, c, slots_max)) {
       rd.coherent_out = 0;
       if (!launch_ffn(p.et, false, rd, slots_max, st)) return MOE_ERR_SHAPE;
       const int64_t n4 = (int64_t)p.M * (p.H / 4);

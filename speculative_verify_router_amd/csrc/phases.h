@@ -61,25 +61,26 @@ __device__ __forceinline__ void router_part(const RouteArgs& r, int blk) {
     __hip_atomic_store(&r.ctr->router_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Phase 1.  SFMT == 0: no shared expert.
-template <int NC, int SFMT, int SCPL>
+// Phase 1.  SFMT == 0: no shared expert; SS: shared gate/up shape code.
+template <int NC, int SFMT, int SS>
 __global__ __launch_bounds__(kBlock) void k_phase1(RouteArgs r, FfnArgs s) {
   if ((int)blockIdx.x < r.n_router_blocks) {
     router_part<NC>(r, blockIdx.x);
   } else if constexpr (SFMT != 0) {
-    ffn_tile<SFMT, SCPL, true>(s, 0, blockIdx.x - r.n_router_blocks);
+    ffn_tile<SFMT, shape_cpl(SS), true, shape_lpr(SS)>(s, 0, blockIdx.x - r.n_router_blocks);
   }
 }
 
 // Two FFN roles in one grid: blocks [0, na) take tiles of role A (grid of
 // a_tiles x slots, tile fastest), the rest tiles of role B (one slot).
-template <int FA, int CA, bool GA, int FB, int CB, bool GB>
+// SA, SB: shape codes.
+template <int FA, int SA, bool GA, int FB, int SB, bool GB>
 __global__ __launch_bounds__(kBlock) void k_dual(FfnArgs a, int a_tiles, int na, FfnArgs b) {
   const int blk = blockIdx.x;
   if (blk < na) {
-    ffn_tile<FA, CA, GA>(a, blk / a_tiles, blk % a_tiles);
+    ffn_tile<FA, shape_cpl(SA), GA, shape_lpr(SA)>(a, blk / a_tiles, blk % a_tiles);
   } else {
-    ffn_tile<FB, CB, GB>(b, 0, blk - na);
+    ffn_tile<FB, shape_cpl(SB), GB, shape_lpr(SB)>(b, 0, blk - na);
   }
 }
 
@@ -138,22 +139,23 @@ struct CombineArgs {
 // sits between the row loop's loads and their waits.
 constexpr int kDownLdsRows = 2048;
 
-template <int FMT, int CPL, bool PAIR_LDS>
+template <int FMT, int S, bool PAIR_LDS>
 __global__ __launch_bounds__(kBlock) void k_down_combine(FfnArgs a, CombineArgs c) {
+  constexpr int CPL = shape_cpl(S), LPR = shape_lpr(S);
   __shared__ int s_last;
   __shared__ float s_out[PAIR_LDS ? kDownLdsRows : 1];
   const int tile = blockIdx.x, slot = blockIdx.y;
   const int n_act = a.pair_expert ? a.n_pairs : *a.n_active;
   if (slot >= n_act) return;  // block-uniform; these blocks never count
   if constexpr (PAIR_LDS) {
-    ffn_tile_pair<FMT, CPL, false, 3, true>(a, slot, tile, s_out);
+    ffn_tile_pair<FMT, CPL, false, 3, true, LPR>(a, slot, tile, s_out);
     __syncthreads();
     const int ub = tile * a.units_per_block;
     const int ue = min(ub + a.units_per_block, a.rows_per_expert);
     float* o = a.out + (int64_t)slot * a.rows_per_expert;
     for (int r = ub + threadIdx.x; r < ue; r += kBlock) store_shared(o + r, s_out[r - ub]);
   } else {
-    ffn_tile<FMT, CPL, false>(a, slot, tile);  // o rows stored with store_shared
+    ffn_tile<FMT, CPL, false, LPR>(a, slot, tile);  // o rows stored with store_shared
   }
   wait_stores();
   __syncthreads();
