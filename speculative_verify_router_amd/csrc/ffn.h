@@ -145,12 +145,13 @@ __device__ __forceinline__ void compute_stage(const Stage<FMT, CPL, GATEUP>& s,
 // One pass of a wave over rows first, first+step, ... < ue of `expert`, for
 // the NT tokens whose pair ids are given (LDSOUT: outputs to lo, token t of
 // the pass in slot lds_slot[t]).
-// LPR: lanes per row when known at compile time (0: a.lpr).
-template <int FMT, int CPL, int NT, bool GATEUP, int NSTMAX = 3, bool LDSOUT = false, int LPR = 0>
+// NSTD: ring depth (0: nst_for); LPR: lanes per row when known at compile
+// time (0: a.lpr).
+template <int FMT, int CPL, int NT, bool GATEUP, int NSTD = 0, bool LDSOUT = false, int LPR = 0>
 __device__ __forceinline__ void ffn_pass(const FfnArgs& a, int expert, const int* pair_ids,
                                          int first, int step, int ue, LdsOut lo = LdsOut{},
                                          const int* lds_slot = nullptr) {
-  constexpr int NST = nst_for(FMT, CPL, GATEUP) < NSTMAX ? nst_for(FMT, CPL, GATEUP) : NSTMAX;
+  constexpr int NST = NSTD ? NSTD : nst_for(FMT, CPL, GATEUP);
   const int lane = threadIdx.x & (kWave - 1);
   const int lpr = LPR ? LPR : a.lpr;
   const int g = lane / lpr;
@@ -222,19 +223,19 @@ template <int FMT, int CPL, int TP, bool GATEUP, int LPR>
 __device__ __forceinline__ void ffn_pass_nt(const FfnArgs& a, int expert, const int* ids, int nt,
                                             int first, int step, int ue) {
   if (nt >= TP) {
-    ffn_pass<FMT, CPL, TP, GATEUP, 3, false, LPR>(a, expert, ids, first, step, ue);
+    ffn_pass<FMT, CPL, TP, GATEUP, 0, false, LPR>(a, expert, ids, first, step, ue);
   } else if (TP > 1 && nt == 1) {
-    ffn_pass<FMT, CPL, 1, GATEUP, 3, false, LPR>(a, expert, ids, first, step, ue);
+    ffn_pass<FMT, CPL, 1, GATEUP, 0, false, LPR>(a, expert, ids, first, step, ue);
   } else if (TP > 2 && nt == 2) {
-    ffn_pass<FMT, CPL, (TP > 2 ? 2 : 1), GATEUP, 3, false, LPR>(a, expert, ids, first, step, ue);
+    ffn_pass<FMT, CPL, (TP > 2 ? 2 : 1), GATEUP, 0, false, LPR>(a, expert, ids, first, step, ue);
   } else if (TP > 3 && nt == 3) {
-    ffn_pass<FMT, CPL, (TP > 3 ? 3 : 1), GATEUP, 3, false, LPR>(a, expert, ids, first, step, ue);
+    ffn_pass<FMT, CPL, (TP > 3 ? 3 : 1), GATEUP, 0, false, LPR>(a, expert, ids, first, step, ue);
   }
 }
 
 // Pair slots: rows [tile * units_per_block, ...) of the expert of (token,
 // slot) pair `slot`, the four waves taking different rows.
-template <int FMT, int CPL, bool GATEUP, int NSTMAX = 3, bool LDSOUT = false, int LPR = 0>
+template <int FMT, int CPL, bool GATEUP, int NSTD = 0, bool LDSOUT = false, int LPR = 0>
 __device__ __forceinline__ void ffn_tile_pair(const FfnArgs& a, int slot, int tile,
                                               float* lds = nullptr) {
   if (slot >= a.n_pairs) return;
@@ -244,9 +245,9 @@ __device__ __forceinline__ void ffn_tile_pair(const FfnArgs& a, int slot, int ti
   const int G = kWave / (LPR ? LPR : a.lpr);
   const int ids1[1] = {slot}, slot0[1] = {0};
   const int e = a.coherent_in ? load_shared(a.pair_expert + slot) : a.pair_expert[slot];
-  ffn_pass<FMT, CPL, 1, GATEUP, NSTMAX, LDSOUT, LPR>(a, e, ids1, ub + (threadIdx.x >> 6) * G,
-                                                     kWavesPerBlock * G, ue,
-                                                     LdsOut{lds, ub, a.units_per_block}, slot0);
+  ffn_pass<FMT, CPL, 1, GATEUP, NSTD, LDSOUT, LPR>(a, e, ids1, ub + (threadIdx.x >> 6) * G,
+                                                   kWavesPerBlock * G, ue,
+                                                   LdsOut{lds, ub, a.units_per_block}, slot0);
 }
 
 // One expert for the identity token list (the shared expert): rows
@@ -255,7 +256,7 @@ __device__ __forceinline__ void ffn_tile_pair(const FfnArgs& a, int slot, int ti
 // (M = 3: one wave idles); with more, wave w takes tokens w, w + 4, ...
 // over all rows.  So the rows are fetched from HBM once per workgroup and
 // idle waves of a small batch still stream.
-template <int FMT, int CPL, bool GATEUP, int NSTMAX = 3, int LPR = 0>
+template <int FMT, int CPL, bool GATEUP, int NSTD = 0, int LPR = 0>
 __device__ __forceinline__ void ffn_tile_tokens(const FfnArgs& a, int tile) {
   const int ub = tile * a.units_per_block;
   const int ue = min(ub + a.units_per_block, a.rows_per_expert);
@@ -266,12 +267,12 @@ __device__ __forceinline__ void ffn_tile_tokens(const FfnArgs& a, int tile) {
     const int rg = kWavesPerBlock / a.n_tokens;
     const int t = wv / rg, q = wv - t * rg;
     const int ids1[1] = {t};
-    if (t < a.n_tokens) ffn_pass<FMT, CPL, 1, GATEUP, NSTMAX, false, LPR>(a, 0, ids1, ub + q * G, rg * G, ue);
+    if (t < a.n_tokens) ffn_pass<FMT, CPL, 1, GATEUP, NSTD, false, LPR>(a, 0, ids1, ub + q * G, rg * G, ue);
     return;
   }
   for (int t = wv; t < a.n_tokens; t += kWavesPerBlock) {
     const int ids1[1] = {t};
-    ffn_pass<FMT, CPL, 1, GATEUP, NSTMAX, false, LPR>(a, 0, ids1, ub, G, ue);
+    ffn_pass<FMT, CPL, 1, GATEUP, NSTD, false, LPR>(a, 0, ids1, ub, G, ue);
   }
 }
 
@@ -283,7 +284,7 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int slot, int tile) {
   const int ub = tile * a.units_per_block;
   if (a.pair_expert) {
     // One (token, slot) pair per slot: every workgroup does the same work.
-    ffn_tile_pair<FMT, CPL, GATEUP, 3, false, LPR>(a, slot, tile);
+    ffn_tile_pair<FMT, CPL, GATEUP, 0, false, LPR>(a, slot, tile);
     return;
   }
   if (a.n_active && slot >= *a.n_active) return;
@@ -296,7 +297,7 @@ __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int slot, int tile) {
   const int G = kWave / (LPR ? LPR : a.lpr);
   int ids[TP];
   if (a.split_tokens) {
-    ffn_tile_tokens<FMT, CPL, GATEUP, 3, LPR>(a, tile);
+    ffn_tile_tokens<FMT, CPL, GATEUP, 0, LPR>(a, tile);
   } else {
     for (int p0 = 0; p0 < count; p0 += TP) {
 #pragma unroll

@@ -112,7 +112,7 @@ __device__ __forceinline__ void flow_shared_tile(const FfnArgs& a, int tile, flo
   const int t = wv / rg, q = wv - t * rg;
   const int ids1[1] = {t};
   if (t < a.n_tokens && ub + q * G < ue)
-    ffn_pass<FMT, CPL, 1, GATEUP, 3, true, LPR>(a, 0, ids1, ub + q * G, rg * G, ue,
+    ffn_pass<FMT, CPL, 1, GATEUP, 0, true, LPR>(a, 0, ids1, ub + q * G, rg * G, ue,
                                            LdsOut{lds, ub, a.units_per_block}, ids1);
 }
 
@@ -190,9 +190,10 @@ __global__ __launch_bounds__(kBlock) void k_flow(FlowArgs f) {
       if (kind == kItemSharedDown) flow_shared_tile<SF, SDC, false>(f.sd, tile, s_out);
     }
     if (kind == kItemGateUp)
-      ffn_tile_pair<RF, shape_cpl(GC), true, 3, true, shape_lpr(GC)>(f.g, pair, tile, s_out);
+      ffn_tile_pair<RF, shape_cpl(GC), true, 0, true, shape_lpr(GC)>(f.g, pair, tile, s_out);
     if (kind == kItemDown)
-      ffn_tile_pair<RF, shape_cpl(DC), false, 3, true, shape_lpr(DC)>(f.d, pair, tile, s_out);
+      ffn_tile_pair<RF, shape_cpl(DC), false, kDownNst, true, shape_lpr(DC)>(f.d, pair, tile,
+                                                                             s_out);
   }
   // B3: the router's partial sums and the item's LDS outputs are complete.
   __syncthreads();

@@ -138,6 +138,9 @@ struct CombineArgs {
 // written out as one contiguous range after the row loop, so that no store
 // sits between the row loop's loads and their waits.
 constexpr int kDownLdsRows = 2048;
+// Ring depth of the routed down rows: a one-matrix row of a few hundred
+// bytes per lane group needs several steps in flight to cover the latency.
+constexpr int kDownNst = 4;
 
 template <int FMT, int S, bool PAIR_LDS>
 __global__ __launch_bounds__(kBlock) void k_down_combine(FfnArgs a, CombineArgs c) {
@@ -148,7 +151,7 @@ __global__ __launch_bounds__(kBlock) void k_down_combine(FfnArgs a, CombineArgs 
   const int n_act = a.pair_expert ? a.n_pairs : *a.n_active;
   if (slot >= n_act) return;  // block-uniform; these blocks never count
   if constexpr (PAIR_LDS) {
-    ffn_tile_pair<FMT, CPL, false, 3, true, LPR>(a, slot, tile, s_out);
+    ffn_tile_pair<FMT, CPL, false, kDownNst, true, LPR>(a, slot, tile, s_out);
     __syncthreads();
     const int ub = tile * a.units_per_block;
     const int ue = min(ub + a.units_per_block, a.rows_per_expert);
