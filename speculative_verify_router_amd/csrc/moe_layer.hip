@@ -13,16 +13,24 @@
 //      2 gateup               routed gate/up + SwiGLU, shared down
 //      3 down_combine         routed down; last workgroup per row tile
 //                             combines
-//    Shapes outside the fused instantiations, and batches above 16 tokens,
-//    take the same steps as separate launches.
+//    Shapes outside the fused instantiations take the same steps as
+//    separate launches.
+//  * batched (more than 16 tokens), three stages of several launches:
+//      1 route          router GEMM (fp32 MFMA), top-k, bucketing, token
+//                       tiles, bf16 hi/lo split of x
+//      2 gateup         shared and routed gate/up + SwiGLU as grouped GEMMs
+//                       (bf16 MFMA)
+//      3 down_combine   shared and routed down GEMMs, combine
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <mutex>
 #include <unordered_map>
 
 #include "common.h"
 #include "ffn.h"
 #include "flow.h"
+#include "gemm.h"
 #include "misc.h"
 #include "phases.h"
 #include "route.h"
@@ -87,7 +95,9 @@ bool ffn_shape(int dtype, int K, FfnShape* s) {
 
 struct Plan {
   int H, E, k, F, Fs, et, st, M, flags;
-  size_t ctr, logits, ids, w, counts, offsets, slots, active, nactive, h, hs, o, s, total;
+  size_t ctr, logits, ids, w, counts, offsets, slots, active, nactive, h, hs, o, s, xs, tiles,
+      total;
+  int tiles_cap;  // routed token tiles of the batched path, at most
 };
 
 int check_desc(const moe_layer_desc* d) {
@@ -141,6 +151,11 @@ int make_plan(const moe_layer_desc* d, int M, Plan* p) {
   p->hs = take(Mz * p->Fs * 4);
   p->o = take(P * p->H * 4);
   p->s = take(Mz * p->H * 4);
+  // Batched path: x split into bf16 hi/lo terms, and the routed token tiles
+  // (every active expert has at most one partial tile).
+  p->xs = take(Mz * p->H * 4);
+  p->tiles_cap = (int)(std::min<size_t>(P, (size_t)p->E) + P / 16);
+  p->tiles = take((size_t)(3 * p->tiles_cap + 1) * 4);
   p->total = off;
   return MOE_OK;
 }
@@ -460,7 +475,8 @@ inline void mark(hipEvent_t* ev, int i, hipStream_t st) {
 struct Buffers {
   Counters* ctr;
   float *logits, *w, *h, *hs, *o, *s;
-  int32_t *ids, *counts, *offsets, *slots, *active, *nactive;
+  int32_t *ids, *counts, *offsets, *slots, *active, *nactive, *tiles, *ntiles;
+  uint4* xs;
 };
 
 Buffers carve(const Plan& p, void* ws, int32_t* ids, float* w) {
@@ -479,14 +495,29 @@ Buffers carve(const Plan& p, void* ws, int32_t* ids, float* w) {
   r.hs = (float*)(b + p.hs);
   r.o = (float*)(b + p.o);
   r.s = (float*)(b + p.s);
+  r.xs = (uint4*)(b + p.xs);
+  r.tiles = (int32_t*)(b + p.tiles);
+  r.ntiles = r.tiles + 3 * p.tiles_cap;
   return r;
+}
+
+// Router logits of a batch: the fp32 MFMA GEMM above the fused batch
+// sizes (H a multiple of 64), else a wave per expert row.
+void enqueue_logits(const Plan& p, const float* router, const float* x, float* logits,
+                    hipStream_t st) {
+  if (p.M > kFusedMaxTokens && p.H % 64 == 0) {
+    hipLaunchKernelGGL(k_router_mfma, dim3((p.M + 15) / 16, (p.E + 15) / 16), dim3(kBlock), 0, st,
+                       router, x, logits, p.H, p.E, p.M);
+    return;
+  }
+  hipLaunchKernelGGL(k_router_logits, dim3((p.E + kWavesPerBlock - 1) / kWavesPerBlock),
+                     dim3(kBlock), 0, st, router, x, logits, p.H, p.E, p.M);
 }
 
 // Router + top-k + bucketing as three launches (any batch size).
 void enqueue_route_plain(const Plan& p, const float* router, const float* x, const Buffers& b,
                          const BucketOut& bo, hipStream_t st) {
-  hipLaunchKernelGGL(k_router_logits, dim3((p.E + kWavesPerBlock - 1) / kWavesPerBlock),
-                     dim3(kBlock), 0, st, router, x, b.logits, p.H, p.E, p.M);
+  enqueue_logits(p, router, x, b.logits, st);
   hipLaunchKernelGGL(k_topk, dim3((p.M + kWavesPerBlock - 1) / kWavesPerBlock), dim3(kBlock), 0,
                      st, b.logits, b.ids, b.w, p.E, p.k, p.M);
   hipLaunchKernelGGL(k_bucket, dim3(1), dim3(kBlock), 0, st, b.ids, p.M * p.k, p.E, bo);
@@ -640,6 +671,122 @@ bool flow_args(const Plan& p, const moe_layer_weights* wt, const float* x, float
   return true;
 }
 
+// ---- Batched path: grouped GEMMs on the matrix cores.
+constexpr int kGemmGateUpRtr = 2;  // row tiles of 16 per wave and matrix
+constexpr int kGemmDownRtr = 4;
+const char* const kGemmStageNames[kNumStages] = {"route", "gateup", "down_combine"};
+
+bool gemm_path(const Plan& p) {
+  if (p.M <= kFusedMaxTokens) return false;
+  // Split activations and h are addressed with 32-bit byte offsets.
+  const int64_t P = (int64_t)p.M * p.k;
+  if (P * std::max(p.H, p.F) * 4 >= (1ll << 31)) return false;
+  if ((int64_t)p.M * std::max(p.H, p.Fs) * 4 >= (1ll << 31)) return false;
+  return true;
+}
+
+template <int FMT, bool GU>
+void launch_gemm_t(const GemmArgs& a, int tiles_cap, hipStream_t st) {
+  constexpr int RTR = GU ? kGemmGateUpRtr : kGemmDownRtr;
+  const int t8 = (tiles_cap + 7) & ~7;
+  hipLaunchKernelGGL((k_gemm<FMT, GU, RTR>), dim3((unsigned)(t8 * a.row_blocks)), dim3(kBlock), 0,
+                     st, a);
+}
+
+void launch_gemm(int dtype, bool gateup, GemmArgs a, int tiles_cap, hipStream_t st) {
+  const int per = kWavesPerBlock * 16 * (gateup ? kGemmGateUpRtr : kGemmDownRtr);
+  a.row_blocks = (a.rows + per - 1) / per;
+  if (dtype == MOE_Q4_K) {
+    if (gateup) launch_gemm_t<kQ4_K, true>(a, tiles_cap, st);
+    else launch_gemm_t<kQ4_K, false>(a, tiles_cap, st);
+  } else {
+    if (gateup) launch_gemm_t<kQ8_0, true>(a, tiles_cap, st);
+    else launch_gemm_t<kQ8_0, false>(a, tiles_cap, st);
+  }
+}
+
+void forward_gemm(const Plan& p, const moe_layer_weights* wt, const float* x, float* y,
+                  const Buffers& b, hipStream_t st, hipEvent_t* ev) {
+  const bool shared = p.Fs > 0;
+  const int P = p.M * p.k;
+  const int dense_tiles = (p.M + 15) / 16;
+
+  mark(ev, 0, st);
+  const BucketOut bo{b.counts, b.offsets, b.slots, b.active, b.nactive};
+  enqueue_route_plain(p, wt->router, x, b, bo, st);
+  hipLaunchKernelGGL(k_tiles, dim3(1), dim3(kBlock), 0, st, b.offsets, p.E,
+                     TileList{b.tiles, b.ntiles});
+  const int64_t n8 = (int64_t)p.M * p.H / 8;
+  hipLaunchKernelGGL(k_split_act, dim3((unsigned)((n8 + kBlock - 1) / kBlock)), dim3(kBlock), 0,
+                     st, x, n8, b.xs);
+
+  mark(ev, 1, st);
+  if (shared) {
+    GemmArgs a{};
+    a.w0 = (const uint8_t*)wt->shared_gate;
+    a.w1 = (const uint8_t*)wt->shared_up;
+    a.total_rows = p.Fs;
+    a.rows = p.Fs;
+    a.K = p.H;
+    a.act = b.xs;
+    a.act_rows = p.M;
+    a.out = b.hs;
+    a.dense_tokens = p.M;
+    launch_gemm(p.st, true, a, dense_tiles, st);
+  }
+  {
+    GemmArgs a{};
+    a.w0 = (const uint8_t*)wt->gate;
+    a.w1 = (const uint8_t*)wt->up;
+    a.total_rows = (int64_t)p.E * p.F;
+    a.rows = p.F;
+    a.K = p.H;
+    a.act = b.xs;
+    a.act_rows = p.M;
+    a.out = b.h;
+    a.tiles = b.tiles;
+    a.n_tiles = b.ntiles;
+    a.slots = b.slots;
+    a.top_k = p.k;
+    a.act_gather = 1;
+    launch_gemm(p.et, true, a, p.tiles_cap, st);
+  }
+
+  mark(ev, 2, st);
+  if (shared) {
+    GemmArgs a{};
+    a.w0 = (const uint8_t*)wt->shared_down;
+    a.total_rows = p.H;
+    a.rows = p.H;
+    a.K = p.Fs;
+    a.act = reinterpret_cast<const uint4*>(b.hs);
+    a.act_rows = p.M;
+    a.out = b.s;
+    a.dense_tokens = p.M;
+    launch_gemm(p.st, false, a, dense_tiles, st);
+  }
+  {
+    GemmArgs a{};
+    a.w0 = (const uint8_t*)wt->down;
+    a.total_rows = (int64_t)p.E * p.H;
+    a.rows = p.H;
+    a.K = p.F;
+    a.act = reinterpret_cast<const uint4*>(b.h);
+    a.act_rows = P;
+    a.out = b.o;
+    a.tiles = b.tiles;
+    a.n_tiles = b.ntiles;
+    a.slots = b.slots;
+    a.top_k = p.k;
+    a.out_scatter = 1;
+    launch_gemm(p.et, false, a, p.tiles_cap, st);
+  }
+  const int64_t n4 = (int64_t)p.M * (p.H / 4);
+  hipLaunchKernelGGL(k_combine, dim3((unsigned)((n4 + kBlock - 1) / kBlock)), dim3(kBlock), 0, st,
+                     b.o, shared ? b.s : nullptr, b.w, y, p.M, p.H, p.k);
+  mark(ev, 3, st);
+}
+
 int forward_impl(const moe_layer_desc* desc, const moe_layer_weights* wt, const float* x,
                  int32_t n_tokens, float* y, int32_t* topk_ids, float* topk_w, void* workspace,
                  size_t workspace_bytes, void* hip_stream, void* const* events, int32_t n_events) {
@@ -669,6 +816,11 @@ int forward_impl(const moe_layer_desc* desc, const moe_layer_weights* wt, const 
     return MOE_ERR_ARG;
 
   const Buffers b = carve(p, workspace, topk_ids, topk_w);
+  if (gemm_path(p)) {
+    (void)hipGetLastError();
+    forward_gemm(p, wt, x, y, b, st, ev);
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
+  }
   if (flow) {
     FlowArgs f;
     flow_args(p, wt, x, y, b, &f);
@@ -812,7 +964,10 @@ int32_t moe_stage_count(const moe_layer_desc* desc, int32_t n_tokens) {
 const char* moe_stage_name(const moe_layer_desc* desc, int32_t n_tokens, int32_t i) {
   const int n = moe_stage_count(desc, n_tokens);
   if (n <= 0 || i < 0 || i >= n) return nullptr;
-  return n == 1 ? kFlowStageName : kStageNames[i];
+  if (n == 1) return kFlowStageName;
+  Plan p;
+  make_plan(desc, n_tokens, &p);
+  return gemm_path(p) ? kGemmStageNames[i] : kStageNames[i];
 }
 
 int32_t moe_route(const moe_layer_desc* desc, const float* router, const float* x,

@@ -12,8 +12,18 @@ import speculative_verify_router_amd as svr
 # Output tolerance: max |y - y_ref| <= 2e-3 * RMS(y_ref) over the whole
 # [M][H] output (fp32-accumulated outputs against the fp64 oracle).
 Y_TOL = 2e-3
-# Routing weights: fp32 softmax against fp64, absolute.
+# Routing weights: fp32 against fp64, absolute: 1e-6 for the fp32 softmax,
+# plus what the fp32 logits carry.  A logit of magnitude L is a sum whose
+# partial sums round at a few ulp(L) ~ 2^-23 L each; the renormalised
+# softmax passes at most half of a logit error on to any weight.  Four such
+# roundings of the token's largest logit: 2^-22 max|l|.
 W_TOL = 1e-6
+
+
+def w_tolerance(ref) -> np.ndarray:
+    """Per-token tolerance of the routing weights, [M][1]."""
+    lmax = np.max(np.abs(np.atleast_2d(ref["logits"])), axis=1, keepdims=True)
+    return W_TOL + 2.0 ** -22 * lmax
 
 
 def log(msg: str):
@@ -73,4 +83,5 @@ def check_y(y, y_ref, what=""):
 
 def check_routing(ids, w, ref):
     assert np.array_equal(ids, ref["ids"]), f"ids differ:\n{ids}\nvs\n{ref['ids']}"
-    assert np.max(np.abs(w - ref["w"])) <= W_TOL, np.max(np.abs(w - ref["w"]))
+    err = np.abs(w - ref["w"])
+    assert np.all(err <= w_tolerance(ref)), (np.max(err), np.max(w_tolerance(ref)))
