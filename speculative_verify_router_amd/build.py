@@ -37,6 +37,8 @@ def compile_flags(extra=()) -> list:
         "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-shared",
         # No packed-FP32 instructions anywhere in the device code.
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # MFMA results straight into VGPRs (no AGPR round trip).
+        "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-Wno-unused-command-line-argument",
         "-I", os.path.join(ROOT, "include"), "-I", CSRC, *extra,
     ]

@@ -18,11 +18,11 @@
 // 0,4,1,5,2,6,3,7 (the order in which shifts and masks pull the nibbles of
 // a Q4_K dword apart); activations are stored in that order.
 //
-// Q4_K weights enter as the bf16 value 1 + q/16 (exponent of 1, q in the
-// top four mantissa bits: one shift and one AND-OR per pair), so with
-// P = sum (1 + q/16) x over a sub-block and X = sum x,
-//   sum w x = 16 d sc (P - X) - dmin m X = a P - c X,
-//   a = 16 d sc,  c = a + dmin m.
+// Q4_K weights enter as the bf16 value 1 + q/128 (the exponent of 1 with q
+// in the low four mantissa bits: one shift and one bit-field insert per
+// pair), so with P = sum (1 + q/128) x over a sub-block and X = sum x,
+//   sum w x = 128 d sc (P - X) - dmin m X = a P - c X,
+//   a = 128 d sc,  c = a + dmin m.
 // X comes from the same MFMA with an all-ones B operand, in the D layout.
 // Q8_0 weights are the int8 values converted to bf16 (exact), sum w x = d P.
 #pragma once
@@ -146,28 +146,40 @@ struct GemmArgs {
   int row_blocks;    // workgroups per token tile
 };
 
-// Q4_K sub-block i (0..7; a constant once unrolled) of a super-block
-// header h: a = 16 d sc, c = a + dmin m (d16 = 16 d).
-__device__ __forceinline__ void q4k_scale(const uint4& h, int i, float d16, float dmin, float& a,
-                                          float& c) {
-  const uint64_t lo = (uint64_t)h.y | ((uint64_t)h.z << 32);
-  const uint64_t hi = (uint64_t)h.z | ((uint64_t)h.w << 32);
-  const uint32_t sc = (uint32_t)(lo >> (6 * i)) & 63u;
-  const uint32_t m = (uint32_t)(hi >> (16 + 6 * i)) & 63u;
-  a = d16 * (float)sc;
-  c = fmaf(dmin, (float)m, a);
+// Q4_K sub-block i (0..7) of a super-block header h: a = 128 d sc,
+// c = a + dmin m.  The six-bit fields are cut from the 96-bit stream
+// (h.y, h.z, h.w) with 32-bit funnel shifts: 64-bit shifts would need the
+// loaded words in aligned register pairs, and the copies into them would
+// wait for the load.
+__device__ __forceinline__ float2 q4k_scale(const uint4& h, int i) {
+  const float d128 = 128.0f * f16_lo(h.x), dmin = f16_hi(h.x);
+  const int bs = 6 * i, bm = 16 + 6 * i;  // sc at stream bit bs, m at 32 + bm
+  const uint32_t sc =
+      __builtin_amdgcn_alignbit(bs < 32 ? h.z : h.w, bs < 32 ? h.y : h.z, bs & 31) & 63u;
+  const uint32_t m =
+      __builtin_amdgcn_alignbit(h.w, bm < 32 ? h.z : h.w, bm & 31) & 63u;
+  const float a = d128 * (float)sc;
+  return make_float2(a, fmaf(dmin, (float)m, a));
 }
 
 // One Q4_K dword (8 nibbles, weights 8g..8g+7 of a sub-block) -> B operand
-// elements 1 + q/16 in the order 0,4,1,5,2,6,3,7.
-__device__ __forceinline__ u32x4 q4k_operand(uint32_t w) {
-  constexpr uint32_t kMask = 0x00780078u, kOne = 0x3F803F80u;
+// elements 1 + q/128 in the order 0,4,1,5,2,6,3,7.  `one` = 0x3F803F80
+// held in a VGPR the compiler cannot see through (opaque_vgpr), so that
+// each pair is one v_bfi_b32 rather than an AND and an OR with literals.
+__device__ __forceinline__ u32x4 q4k_operand(uint32_t w, uint32_t one) {
+  constexpr uint32_t kMask = 0x000F000Fu;
   u32x4 b;
-  b.x = ((w << 3) & kMask) | kOne;
-  b.y = ((w >> 1) & kMask) | kOne;
-  b.z = ((w >> 5) & kMask) | kOne;
-  b.w = ((w >> 9) & kMask) | kOne;
+  b.x = (w & kMask) | (one & ~kMask);
+  b.y = ((w >> 4) & kMask) | (one & ~kMask);
+  b.z = ((w >> 8) & kMask) | (one & ~kMask);
+  b.w = ((w >> 12) & kMask) | (one & ~kMask);
   return b;
+}
+
+// v, in a VGPR, as a value unknown to the optimiser (emits no instruction).
+__device__ __forceinline__ uint32_t opaque_vgpr(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
 }
 
 // Two Q8_0 dwords (int8 weights 8g..8g+7) -> bf16 B operand elements.
@@ -183,62 +195,104 @@ __device__ __forceinline__ u32x4 q8_operand(uint32_t w0, uint32_t w1) {
   return b;
 }
 
-// Per step (one 32-column sub-block) the operands a wave loads.
+// K is processed in slabs of 8 sub-blocks (256 columns: one Q4_K
+// super-block).  Per slab a workgroup stages in LDS
+//  * the token tile's activations, once for its four waves, as
+//    [step 8][hi, lo][group 4][row 16] x 16 bytes (16 KB), double-buffered;
+//  * each wave's weight rows, loaded as whole 128-byte lines (lane 16 g + n
+//    reads 16 bytes of row n) and read back per step in operand order, as
+//    [matrix][row tile][load j][lane 64] x 16 bytes.
+// Scale data (a Q4_K header, or eight Q8_0 fp16 scales: 16 bytes per row
+// and slab) stays in VGPRs.  The global loads of slab k+1 are issued right
+// after slab k is written to LDS, so waits happen only at slab boundaries.
+constexpr int kSlab = 8;
+constexpr int kActSlabBytes = kSlab * 2 * 4 * 16 * 16;
+
+// 16-byte weight loads per lane, row tile and slab (128 / 256 bytes per row).
+template <int FMT>
+constexpr int slab_loads() { return FMT == kQ4_K ? 2 : 4; }
+
 template <int FMT, int NM, int RTR>
-struct GStep {
-  uint4 ahi, alo;                                   // activations (A operand)
-  uint32_t w[NM][RTR][FMT == kQ8_0 ? 2 : 1];  // weight dwords (B operand)
-  uint32_t d[NM][RTR];                         // Q8_0 fp16 scale bits
+struct Slab {
+  uint4 act[4];                             // this thread's part of the activation slab
+  uint4 q[NM][RTR][slab_loads<FMT>()];      // weight lines
+  uint4 s[NM][RTR];                         // scale data of the lane's row
 };
 
-// Steps of the software pipeline kept in flight.
-constexpr int kGemmRing = 4;
-
-// A wave's work: token tile (first position pos0, cnt tokens) x RTR row
-// tiles of 16 rows from r0, of NM matrices (2: gate and up).  Outputs:
-// gate/up -> h = silu(gate) * up, split; down -> fp32.
 template <int FMT, bool GATEUP, int RTR>
-__device__ __forceinline__ void gemm_wave(const GemmArgs& a, int e, int pos0, int cnt, int r0) {
+struct GemmLds {
+  static constexpr int NM = GATEUP ? 2 : 1;
+  static constexpr int kWaveBytes = NM * RTR * slab_loads<FMT>() * 1024;
+  uint4 act[2][kActSlabBytes / 16];
+  uint4 w[kWavesPerBlock][kWaveBytes / 16];
+  // Per wave: (a, c) of [matrix][row tile][step pair 4][row 16][step % 2].
+  float2 sc[kWavesPerBlock][NM * RTR * kSlab * 16];
+};
+
+// A workgroup's work: token tile (positions pos0.., cnt of them) x four
+// waves of RTR row tiles of 16 rows (wave w: rows r0 + 16 RTR w ..), of NM
+// matrices (2: gate and up).  Outputs: gate/up -> h = silu(gate) * up,
+// split; down -> fp32.
+template <int FMT, bool GATEUP, int RTR>
+__device__ __forceinline__ void gemm_block(const GemmArgs& a, int e, int pos0, int cnt, int rb0,
+                                           GemmLds<FMT, GATEUP, RTR>& L) {
   constexpr int NM = GATEUP ? 2 : 1;
-  const int lane = threadIdx.x & (kWave - 1);
+  constexpr int NQ = slab_loads<FMT>();
+  constexpr uint32_t kSlabRowBytes = FMT == kQ4_K ? 128u : 256u;  // quant bytes per row and slab
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int S = a.K >> 5;  // sub-blocks
+  const int NS = (S + kSlab - 1) / kSlab;
+  const int r0 = rb0 + 16 * RTR * wv;
 
-  // Activation row of this lane's A operand (row n of the tile).  Rows
-  // past the tile repeat its first row: they only feed output rows that are
-  // not stored.
-  const int pos = pos0 + (n < cnt ? n : 0);
-  const int arow = a.act_gather ? a.slots[pos] / a.top_k : pos;
-  const uint32_t aoff = (uint32_t)arow * (uint32_t)a.K * 4u + 32u * (uint32_t)g;
+  // Activations: thread T stages LDS entries T + 256 j (j < 4), i.e. row
+  // n = T % 16 of (step, hi/lo, group) u = T / 16 + 16 j, so that the 64
+  // lanes of a wave write 1 KB of consecutive LDS.  Its source is unit
+  // 8 step + 2 group + hi/lo of row n's 1 KB slab chunk.
+  const int an = tid & 15, au = tid >> 4;
+  const int apos = pos0 + (an < cnt ? an : 0);  // rows past the tile repeat its first row
+  const int arow = a.act_gather ? a.slots[apos] / a.top_k : apos;
   const __amdgpu_buffer_rsrc_t ar = make_rsrc(a.act, (uint32_t)(a.act_rows * a.K * 4));
+  uint32_t aoff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int u = au + 16 * j;  // (step u / 8, hi/lo (u / 4) % 2, group u % 4)
+    aoff[j] = (uint32_t)arow * (uint32_t)a.K * 4u +
+              16u * (uint32_t)(8 * (u >> 3) + 2 * (u & 3) + ((u >> 2) & 1));
+  }
 
   QPlanes P[NM];
   P[0] = expert_planes<FMT>(a.w0, a.total_rows, a.K, (int64_t)e * a.rows, a.rows);
   if (GATEUP) P[NM - 1] = expert_planes<FMT>(a.w1, a.total_rows, a.K, (int64_t)e * a.rows, a.rows);
-  // Byte offsets of this lane's weight row (row r0 + 16 rt + n) in each plane.
   uint32_t qo[RTR], so[RTR];
 #pragma unroll
   for (int rt = 0; rt < RTR; ++rt) {
     const uint32_t r = (uint32_t)(r0 + 16 * rt + n);
-    qo[rt] = r * P[0].qrow + (FMT == kQ8_0 ? 8u : 4u) * (uint32_t)g;
+    qo[rt] = r * P[0].qrow + 16u * (uint32_t)g;
     so[rt] = r * P[0].srow;
   }
 
-  auto load_step = [&](GStep<FMT, NM, RTR>& st, int s) {
-    const uint32_t ao = aoff + 128u * (uint32_t)s;
-    st.ahi = bload16(ar, ao);
-    st.alo = bload16(ar, ao + 16u);
+  auto load_slab = [&](Slab<FMT, NM, RTR>& sl, int k) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sl.act[j] = bload16(ar, aoff[j] + 1024u * (uint32_t)k);
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
       for (int rt = 0; rt < RTR; ++rt) {
+#pragma unroll
+        for (int j = 0; j < NQ; ++j)
+          sl.q[m][rt][j] = bload16(P[m].q, qo[rt] + kSlabRowBytes * (uint32_t)k + 64u * j);
+        // Scale data: 16 bytes per row and slab; a Q4_K header is 16-byte
+        // aligned, Q8_0 rows (K / 16 bytes of scales) need not be, so their
+        // fp16 scales are loaded one by one.
         if constexpr (FMT == kQ4_K) {
-          st.w[m][rt][0] = __builtin_amdgcn_raw_buffer_load_b32(P[m].q, qo[rt] + 16u * s, 0, 0);
+          sl.s[m][rt] = bload16(P[m].s, so[rt] + 16u * (uint32_t)k);
         } else {
-          const uint32_t o = qo[rt] + 32u * s;
-          st.w[m][rt][0] = __builtin_amdgcn_raw_buffer_load_b32(P[m].q, o, 0, 0);
-          st.w[m][rt][1] = __builtin_amdgcn_raw_buffer_load_b32(P[m].q, o + 4u, 0, 0);
-          st.d[m][rt] = bload2(P[m].s, so[rt] + 2u * s);
+          uint32_t h[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) h[i] = bload2(P[m].s, so[rt] + 16u * (uint32_t)k + 2u * i);
+          sl.s[m][rt] = make_uint4(h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16,
+                                   h[6] | h[7] << 16);
         }
       }
   };
@@ -248,73 +302,104 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& a, int e, int pos0, in
   for (int m = 0; m < NM; ++m)
 #pragma unroll
     for (int rt = 0; rt < RTR; ++rt) acc[m][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint32_t one = opaque_vgpr(0x3F803F80u);
   const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  uint4* const wl = L.w[wv];
+  float2* const scl = L.sc[wv];
 
-  GStep<FMT, NM, RTR> ring[kGemmRing];
+  // Slab k: stage it in LDS, issue the loads of slab k + 1 into the
+  // registers it leaves free, compute its eight steps.
+  auto consume = [&](Slab<FMT, NM, RTR>& sl, int k) {
+    uint4* const al = L.act[k & 1];
 #pragma unroll
-  for (int i = 0; i < kGemmRing - 1; ++i) load_step(ring[i], min(i, S - 1));
-
-  // Q4_K super-block headers (16 bytes per 8 sub-blocks) of the lane's
-  // rows: the current one, and the next one loaded a super-block ahead so
-  // that waiting for it never drains the ring.
-  uint4 hd[NM][RTR], hn[NM][RTR];
-  float d16[NM][RTR], dmn[NM][RTR];
-  if constexpr (FMT == kQ4_K) {
+    for (int j = 0; j < 4; ++j) al[tid + 256 * j] = sl.act[j];
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
-      for (int rt = 0; rt < RTR; ++rt) hn[m][rt] = bload16(P[m].s, so[rt]);
-  }
-
-  // Steps come in groups of 8 (one Q4_K super-block; Q8_0 pads the last
-  // group with zero-scale steps).  Ring slot of step s is s % kGemmRing.
-  for (int s0 = 0; s0 < S; s0 += 8) {
-    if constexpr (FMT == kQ4_K) {
-      const uint32_t next = 2u * (uint32_t)min(s0 + 8, S - 8);
+      for (int rt = 0; rt < RTR; ++rt)
 #pragma unroll
-      for (int m = 0; m < NM; ++m)
+        for (int j = 0; j < NQ; ++j) wl[((m * RTR + rt) * NQ + j) * 64 + lane] = sl.q[m][rt][j];
+    // Scales of the slab: the four lanes of a row decode two steps each
+    // (lane 16 g + n: steps 2g, 2g + 1 of row n, one 16-byte store).
 #pragma unroll
-        for (int rt = 0; rt < RTR; ++rt) {
-          hd[m][rt] = hn[m][rt];
-          hn[m][rt] = bload16(P[m].s, so[rt] + next);
-          d16[m][rt] = 16.0f * f16_lo(hd[m][rt].x);
-          dmn[m][rt] = f16_hi(hd[m][rt].x);
-        }
-    }
+    for (int m = 0; m < NM; ++m)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int s = s0 + i;
-      load_step(ring[(i + kGemmRing - 1) % kGemmRing], min(s + kGemmRing - 1, S - 1));
-      const GStep<FMT, NM, RTR>& st = ring[i % kGemmRing];
-      const u32x4 ahi = {st.ahi.x, st.ahi.y, st.ahi.z, st.ahi.w};
-      const u32x4 alo = {st.alo.x, st.alo.y, st.alo.z, st.alo.w};
-      f32x4 X = zero;
-      if constexpr (FMT == kQ4_K) X = mfma_bf16(alo, ones, mfma_bf16(ahi, ones, zero));
-      const bool live = s < S;
+      for (int rt = 0; rt < RTR; ++rt) {
+        float2 ac2[2];
 #pragma unroll
-      for (int m = 0; m < NM; ++m)
-#pragma unroll
-        for (int rt = 0; rt < RTR; ++rt) {
-          u32x4 b;
-          float sa, sc = 0.f;
+        for (int t = 0; t < 2; ++t) {
+          const int i = 2 * g + t;
+          float2 ac;
           if constexpr (FMT == kQ4_K) {
-            b = q4k_operand(st.w[m][rt][0]);
-            q4k_scale(hd[m][rt], i, d16[m][rt], dmn[m][rt], sa, sc);
+            ac = q4k_scale(sl.s[m][rt], i);
           } else {
-            b = q8_operand(st.w[m][rt][0], st.w[m][rt][1]);
-            sa = live ? f16_to_f32(st.d[m][rt]) : 0.f;
+            const uint4 h = sl.s[m][rt];
+            const uint64_t lo = (uint64_t)h.x | ((uint64_t)h.y << 32);
+            const uint64_t hi = (uint64_t)h.z | ((uint64_t)h.w << 32);
+            const uint32_t dw = (uint32_t)((g < 2 ? lo : hi) >> (32 * (g & 1)));  // halves 2g, 2g+1
+            const bool live = kSlab * k + i < S;
+            ac = make_float2(live ? f16_to_f32(t ? dw >> 16 : dw) : 0.f, 0.f);
           }
-          const f32x4 p = mfma_bf16(alo, b, mfma_bf16(ahi, b, zero));
+          ac2[t] = ac;
+        }
+        reinterpret_cast<float4*>(scl)[((m * RTR + rt) * 4 + g) * 16 + n] =
+            make_float4(ac2[0].x, ac2[0].y, ac2[1].x, ac2[1].y);
+      }
+    __syncthreads();
+    if (k + 1 < NS) load_slab(sl, k + 1);
+
+    const uint32_t* wl32 = reinterpret_cast<const uint32_t*>(wl);
+#pragma unroll
+    for (int i = 0; i < kSlab; ++i) {
+      const uint4 h4 = al[((i * 2 + 0) * 4 + g) * 16 + n];
+      const uint4 l4 = al[((i * 2 + 1) * 4 + g) * 16 + n];
+      const u32x4 ahi = {h4.x, h4.y, h4.z, h4.w};
+      const u32x4 alo = {l4.x, l4.y, l4.z, l4.w};
+      u32x4 b[NM][RTR];
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int rt = 0; rt < RTR; ++rt) {
+          const int base = (m * RTR + rt) * NQ;
+          if constexpr (FMT == kQ4_K) {
+            b[m][rt] = q4k_operand(wl32[((base + (i >> 2)) * 64 + (i & 3) * 16 + n) * 4 + g], one);
+          } else {
+            const int u = 2 * i + (g >> 1);
+            const uint2 w = reinterpret_cast<const uint2*>(wl)[((base + (i >> 1)) * 64 + (u & 3) * 16 + n) * 2 + (g & 1)];
+            b[m][rt] = q8_operand(w.x, w.y);
+          }
+        }
+      // hi terms for every row tile first, then lo terms, so that no MFMA
+      // waits on the one just issued.
+      f32x4 p[NM][RTR], X = zero;
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int rt = 0; rt < RTR; ++rt) p[m][rt] = mfma_bf16(ahi, b[m][rt], zero);
+      if constexpr (FMT == kQ4_K) X = mfma_bf16(ahi, ones, zero);
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int rt = 0; rt < RTR; ++rt) p[m][rt] = mfma_bf16(alo, b[m][rt], p[m][rt]);
+      if constexpr (FMT == kQ4_K) X = mfma_bf16(alo, ones, X);
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int rt = 0; rt < RTR; ++rt) {
+          const float2 ac = scl[(((m * RTR + rt) * 4 + (i >> 1)) * 16 + n) * 2 + (i & 1)];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            float v = fmaf(sa, p[j], acc[m][rt][j]);
-            if constexpr (FMT == kQ4_K) v = fmaf(-sc, X[j], v);
+            float v = fmaf(ac.x, p[m][rt][j], acc[m][rt][j]);
+            if constexpr (FMT == kQ4_K) v = fmaf(-ac.y, X[j], v);
             acc[m][rt][j] = v;
           }
         }
     }
-  }
+  };
+  Slab<FMT, NM, RTR> sl;
+  load_slab(sl, 0);
+  for (int k = 0; k < NS; ++k) consume(sl, k);
 
   // Epilogue: lane holds rows r0 + 16 rt + n for tokens 4g + j.
 #pragma unroll
@@ -348,9 +433,11 @@ __device__ __forceinline__ void gemm_wave(const GemmArgs& a, int e, int pos0, in
 // the eight XCDs round-robin; block b takes token tile 8 (b / 8 / row_blocks)
 // + b % 8 and row block (b / 8) % row_blocks, so the row blocks of one token
 // tile share an XCD (and its L2 copy of the tile's activations) and the
-// tiles spread over all XCDs.
+// tiles spread over all XCDs.  Every wave of a workgroup passes the same
+// slab barriers; waves whose rows lie past the expert compute zeros.
 template <int FMT, bool GATEUP, int RTR>
 __global__ __launch_bounds__(kBlock) void k_gemm(GemmArgs a) {
+  __shared__ GemmLds<FMT, GATEUP, RTR> lds;
   const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
   const int tile = (j / a.row_blocks) * 8 + xcd, rb = j % a.row_blocks;
   int e, pos0, cnt;
@@ -365,9 +452,7 @@ __global__ __launch_bounds__(kBlock) void k_gemm(GemmArgs a) {
     cnt = min(16, a.dense_tokens - pos0);
     if (cnt <= 0) return;
   }
-  const int r0 = (rb * kWavesPerBlock + (threadIdx.x >> 6)) * 16 * RTR;
-  if (r0 >= a.rows) return;
-  gemm_wave<FMT, GATEUP, RTR>(a, e, pos0, cnt, r0);
+  gemm_block<FMT, GATEUP, RTR>(a, e, pos0, cnt, rb * kWavesPerBlock * 16 * RTR, lds);
 }
 
 // ---------------------------------------------------------------------------

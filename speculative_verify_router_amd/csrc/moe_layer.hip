@@ -685,23 +685,22 @@ bool gemm_path(const Plan& p) {
   return true;
 }
 
-template <int FMT, bool GU>
-void launch_gemm_t(const GemmArgs& a, int tiles_cap, hipStream_t st) {
-  constexpr int RTR = GU ? kGemmGateUpRtr : kGemmDownRtr;
+template <int FMT, bool GU, int RTR>
+void launch_gemm_t(GemmArgs a, int tiles_cap, hipStream_t st) {
+  const int per = kWavesPerBlock * 16 * RTR;
+  a.row_blocks = (a.rows + per - 1) / per;
   const int t8 = (tiles_cap + 7) & ~7;
-  hipLaunchKernelGGL((k_gemm<FMT, GU, RTR>), dim3((unsigned)(t8 * a.row_blocks)), dim3(kBlock), 0,
-                     st, a);
+  hipLaunchKernelGGL((k_gemm<FMT, GU, RTR>), dim3((unsigned)(t8 * a.row_blocks)), dim3(kBlock),
+                     0, st, a);
 }
 
-void launch_gemm(int dtype, bool gateup, GemmArgs a, int tiles_cap, hipStream_t st) {
-  const int per = kWavesPerBlock * 16 * (gateup ? kGemmGateUpRtr : kGemmDownRtr);
-  a.row_blocks = (a.rows + per - 1) / per;
+void launch_gemm(int dtype, bool gateup, const GemmArgs& a, int tiles_cap, hipStream_t st) {
   if (dtype == MOE_Q4_K) {
-    if (gateup) launch_gemm_t<kQ4_K, true>(a, tiles_cap, st);
-    else launch_gemm_t<kQ4_K, false>(a, tiles_cap, st);
+    if (gateup) launch_gemm_t<kQ4_K, true, kGemmGateUpRtr>(a, tiles_cap, st);
+    else launch_gemm_t<kQ4_K, false, kGemmDownRtr>(a, tiles_cap, st);
   } else {
-    if (gateup) launch_gemm_t<kQ8_0, true>(a, tiles_cap, st);
-    else launch_gemm_t<kQ8_0, false>(a, tiles_cap, st);
+    if (gateup) launch_gemm_t<kQ8_0, true, kGemmGateUpRtr>(a, tiles_cap, st);
+    else launch_gemm_t<kQ8_0, false, kGemmDownRtr>(a, tiles_cap, st);
   }
 }
 

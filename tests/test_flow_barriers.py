@@ -68,6 +68,7 @@ def test_every_wave_passes_each_barrier_once(tmp_path):
     out = tmp_path / "flow_variants.s"
     subprocess.run([HIPCC, "-O3", "-std=c++17", "--offload-arch=gfx950", "--cuda-device-only", "-S",
                     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                    "-mllvm", "-amdgpu-mfma-vgpr-form",
                     "-Wno-unused-command-line-argument", "-I", os.path.join(ROOT, "include"),
                     "-I", CSRC, "-o", str(out), str(src)], check=True, capture_output=True)
     kernels = [(n, b) for n, b in _functions(out.read_text()) if "k_flow" in n]
