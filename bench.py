@@ -10,9 +10,10 @@ router.  Calls rotate over R independent layer instances so that no call
 finds its weights in the 256 MB Infinity Cache left by the previous one.
 
 Prints one JSON line.  `roofline` reports the dominant kernel against the
-8 TB/s HBM peak: for batches of up to four tokens the whole layer is one
-launch (k_flow, every byte of the layer); otherwise the routed gate/up
-stage (k_dual).  Its time comes from HIP events recorded by the library on
+8 TB/s HBM peak: the single-launch layer (k_flow, every byte of the layer)
+when it is selected; otherwise the routed gate/up stage (k_dual, which also
+streams the shared down projection, for up to 16 tokens; the routed gate/up
+grouped GEMM k_gemm for larger batches).  Its time comes from HIP events recorded by the library on
 the launch stream; `cpu_baseline` times the CPU oracle on a
 bounded sample (repeated layer calls, about 12 s) on the host.
 
@@ -37,22 +38,27 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "step35_verify_m4"
-# Dominant stage -> its kernel.  Batches of up to four tokens run the whole
-# layer as one launch (stage "layer"); larger ones in three stages, of which
-# "gateup" moves the most bytes.
+# Dominant stage -> its kernel.  The single-launch path runs the whole layer
+# as one launch (stage "layer"); the staged path (up to 16 tokens) has three
+# stages, the batched path five (its first is "route"); in both "gateup"
+# moves the most bytes.
 KERNEL_OF_STAGE = {"layer": "k_flow", "gateup": "k_dual"}
+BATCHED_KERNEL = "k_gemm"
 
 
 def traffic_file(kernel: str, workload: str) -> str:
-    return os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_counters.json")
+    """Counter summary of `kernel` (a name, or a name with the start of its
+    template arguments, e.g. "k_gemm<2, true") on `workload`."""
+    return os.path.join(ROOT, "profiles", f"{kernel.split('<')[0]}_{workload}_hbm_counters.json")
 
 
 def _bytes_per_row(dtype: str, cols: int) -> float:
     return cols // 32 * 34 if dtype == "q8_0" else cols // 256 * 144
 
 
-def layer_bytes(cfg, distinct: int) -> dict:
-    """Algorithmic HBM bytes of one call: router, distinct experts, shared expert, x, y."""
+def layer_bytes(cfg, distinct: int, batched: bool = False) -> dict:
+    """Algorithmic HBM bytes of one call: router, distinct experts, shared expert, x, y;
+    and of the "gateup" stage of the staged (default) or batched path."""
     H, F, Fs, M, k = cfg.hidden, cfg.ffn, cfg.shared_ffn, cfg.n_tokens, cfg.top_k
     expert = 2 * F * _bytes_per_row(cfg.expert_type, H) + H * _bytes_per_row(cfg.expert_type, F)
     shared = 0
@@ -61,8 +67,10 @@ def layer_bytes(cfg, distinct: int) -> dict:
     router = cfg.n_experts * H * 4
     xy = 2 * M * H * 4
     # Stage "gateup": routed gate/up (x in, h out) and shared down (hs in, s out).
+    # Batched: the routed gate/up GEMM alone (split x in, split h out, both
+    # four bytes per element).
     gateup = distinct * 2 * F * _bytes_per_row(cfg.expert_type, H) + M * H * 4 + M * k * F * 4
-    if Fs:
+    if Fs and not batched:
         gateup += H * _bytes_per_row(cfg.shared_type, Fs) + M * Fs * 4 + M * H * 4
     total = router + distinct * expert + shared + xy
     return dict(total=total, layer=total, gateup=gateup)
@@ -142,11 +150,13 @@ def summarize_counters(fetch_dir: str, write_dir: str, workload: str, copy_bytes
                 acc.setdefault(name, []).append(v)
         return acc
 
-    out = {"kernel": kernel, "workload": workload, "source_hash": source_hash(),
+    out = {"kernel": kernel.split("<")[0], "dispatches": kernel, "workload": workload,
+           "source_hash": source_hash(),
            "copy_bytes": copy_bytes}
     for counter, path in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         acc = per_kernel(path, counter)
-        dom = [v for n, vs in acc.items() if n.startswith(f"void svr::{kernel}<") for v in vs]
+        prefix = f"void svr::{kernel}" if "<" in kernel else f"void svr::{kernel}<"
+        dom = [v for n, vs in acc.items() if n.startswith(prefix) for v in vs]
         # The runtime's device-to-device copy kernel moving copy_bytes
         # (smaller copies of the same kernel are left out).
         cpy = [v for n, vs in acc.items() if "copybuffer" in n.lower()
@@ -249,7 +259,8 @@ def main(argv=None) -> int:
     nst = svr.moe_stage_count(desc, M)
     names = [svr.moe_stage_name(desc, M, j) for j in range(nst)]
     DOMINANT = "layer" if "layer" in names else "gateup"
-    kernel = KERNEL_OF_STAGE[DOMINANT]
+    batched = names[0] == "route"
+    kernel = BATCHED_KERNEL if batched else KERNEL_OF_STAGE[DOMINANT]
     K = args.steps
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(K)]
     for row in evs:  # create the underlying HIP events before the timed region
@@ -286,7 +297,7 @@ def main(argv=None) -> int:
         if args.events == "all":
             stage_ms += [evs[s][j].elapsed_time(evs[s][j + 1]) for j in range(nst)]
         dom_ms += evs[s][dom].elapsed_time(evs[s][dom + 1])
-        dom_bytes += layer_bytes(cfg, distinct[i])[DOMINANT]
+        dom_bytes += layer_bytes(cfg, distinct[i], batched)[DOMINANT]
 
     graph_ms = None
     if args.graph:

@@ -133,8 +133,9 @@ int32_t moe_tensor_bytes(int32_t dtype, int64_t rows, int64_t cols, int64_t* byt
 
 /* Device workspace, in *bytes, that moe_layer_forward and moe_route need for
  * up to max_tokens tokens: 16 KiB of hand-off counters, router logits,
- * routing lists, the SwiGLU activations of every (token, slot) pair and the
- * per-pair expert outputs.  The counter area (the first 16384 bytes) must be
+ * routing lists, the SwiGLU activations of every (token, slot) pair, the
+ * per-pair expert outputs, and for batches above 16 tokens the split
+ * activations and the token-tile list of the grouped GEMMs.  The counter area (the first 16384 bytes) must be
  * zero before the first call that uses the workspace; every call leaves it
  * zero again, so zero-fill a workspace once when it is allocated.  Calls that
  * share a workspace must not overlap in time.  One exception: in the
@@ -168,15 +169,21 @@ int32_t moe_route(const moe_layer_desc* desc, const float* router, const float* 
  * "layer"): a work queue in dependency order
  * (router rows; shared gate/up; routed gate/up per (token, slot) pair;
  * shared down; routed down, each output row tile combined by the last item
- * to finish it).  Other calls run three stages ("route_shared_gateup",
- * "gateup", "down_combine").  moe_stage_count / moe_stage_name say which. */
+ * to finish it).  Other calls of up to 16 tokens run three stages
+ * ("route_shared_gateup", "gateup", "down_combine").  Larger batches (a
+ * prefill micro-batch, "Step-5 Preview GGUF": 512-token micro-batches) run
+ * the expert FFNs as grouped GEMMs on the bf16 matrix cores with exact
+ * integer quants, fp32 scales and activations split into two bf16 terms,
+ * in five stages ("route", "shared_gateup", "gateup", "shared_down",
+ * "down_combine"; the shared stages are empty without a shared expert).
+ * moe_stage_count / moe_stage_name say which. */
 int32_t moe_layer_forward(const moe_layer_desc* desc, const moe_layer_weights* weights,
                           const float* x, int32_t n_tokens, float* y,
                           int32_t* topk_ids, float* topk_w,
                           void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /* Number of stages a moe_layer_forward call with this desc and n_tokens
- * enqueues (1 or 3; the negated status code if desc is invalid), and the
+ * enqueues (1, 3 or 5; the negated status code if desc is invalid), and the
  * name of stage i (static string; NULL if i or desc is invalid). */
 int32_t moe_stage_count(const moe_layer_desc* desc, int32_t n_tokens);
 const char* moe_stage_name(const moe_layer_desc* desc, int32_t n_tokens, int32_t i);

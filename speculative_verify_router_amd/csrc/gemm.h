@@ -203,8 +203,13 @@ __device__ __forceinline__ u32x4 q8_operand(uint32_t w0, uint32_t w1) {
 //    reads 16 bytes of row n) and read back per step in operand order, as
 //    [matrix][row tile][load j][lane 64] x 16 bytes.
 // Scale data (a Q4_K header, or eight Q8_0 fp16 scales: 16 bytes per row
-// and slab) stays in VGPRs.  The global loads of slab k+1 are issued right
-// after slab k is written to LDS, so waits happen only at slab boundaries.
+// and slab) is fetched for eight slabs at a time, one whole 128-byte line
+// per row, lane 16 g + n holding slabs 2g and 2g + 1 of row n; at each slab
+// the lanes of a row take that slab's 16 bytes from the lane holding them.
+// (Fetched slab by slab, the lines would leave L2 before their next 16
+// bytes are needed and be read from memory eight times.)  The global loads
+// of slab k+1 are issued right after slab k is written to LDS, so waits
+// happen only at slab boundaries.
 constexpr int kSlab = 8;
 constexpr int kActSlabBytes = kSlab * 2 * 4 * 16 * 16;
 
@@ -216,8 +221,16 @@ template <int FMT, int NM, int RTR>
 struct Slab {
   uint4 act[4];                             // this thread's part of the activation slab
   uint4 q[NM][RTR][slab_loads<FMT>()];      // weight lines
-  uint4 s[NM][RTR];                         // scale data of the lane's row
 };
+
+// Lane `src`'s value v, for every lane (ds_bpermute, four dwords).
+__device__ __forceinline__ uint4 lane_fetch(int src, const uint4& v) {
+  const int a = src * 4;
+  return make_uint4((uint32_t)__builtin_amdgcn_ds_bpermute(a, (int)v.x),
+                    (uint32_t)__builtin_amdgcn_ds_bpermute(a, (int)v.y),
+                    (uint32_t)__builtin_amdgcn_ds_bpermute(a, (int)v.z),
+                    (uint32_t)__builtin_amdgcn_ds_bpermute(a, (int)v.w));
+}
 
 template <int FMT, bool GATEUP, int RTR>
 struct GemmLds {
@@ -272,6 +285,36 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, int e, int pos0, i
     so[rt] = r * P[0].srow;
   }
 
+  const bool q8_aligned = (a.K & 255) == 0;
+  // Scale data of slabs 8q + 2g (hg0) and 8q + 2g + 1 (hg1) of row n (two
+  // arrays, not one: a select between them must not become an indexed
+  // load from scratch memory).
+  uint4 hg0[NM][RTR], hg1[NM][RTR];
+  auto load_group = [&](int q) {
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int rt = 0; rt < RTR; ++rt)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const uint32_t o = so[rt] + 16u * (uint32_t)min(8 * q + 2 * g + t, NS - 1);
+          // 16-byte aligned for Q4_K and for Q8_0 rows with K % 256 == 0;
+          // other Q8_0 rows (K / 16 bytes of scales) take their eight fp16
+          // scales one by one.
+          uint4 v;
+          if (FMT == kQ4_K || q8_aligned) {
+            v = bload16(P[m].s, o);
+          } else {
+            uint32_t h[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) h[i] = bload2(P[m].s, o + 2u * i);
+            v = make_uint4(h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16,
+                           h[6] | h[7] << 16);
+          }
+          if (t == 0) hg0[m][rt] = v;
+          else hg1[m][rt] = v;
+        }
+  };
   auto load_slab = [&](Slab<FMT, NM, RTR>& sl, int k) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) sl.act[j] = bload16(ar, aoff[j] + 1024u * (uint32_t)k);
@@ -282,18 +325,6 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, int e, int pos0, i
 #pragma unroll
         for (int j = 0; j < NQ; ++j)
           sl.q[m][rt][j] = bload16(P[m].q, qo[rt] + kSlabRowBytes * (uint32_t)k + 64u * j);
-        // Scale data: 16 bytes per row and slab; a Q4_K header is 16-byte
-        // aligned, Q8_0 rows (K / 16 bytes of scales) need not be, so their
-        // fp16 scales are loaded one by one.
-        if constexpr (FMT == kQ4_K) {
-          sl.s[m][rt] = bload16(P[m].s, so[rt] + 16u * (uint32_t)k);
-        } else {
-          uint32_t h[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) h[i] = bload2(P[m].s, so[rt] + 16u * (uint32_t)k + 2u * i);
-          sl.s[m][rt] = make_uint4(h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16,
-                                   h[6] | h[7] << 16);
-        }
       }
   };
 
@@ -322,19 +353,24 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, int e, int pos0, i
         for (int j = 0; j < NQ; ++j) wl[((m * RTR + rt) * NQ + j) * 64 + lane] = sl.q[m][rt][j];
     // Scales of the slab: the four lanes of a row decode two steps each
     // (lane 16 g + n: steps 2g, 2g + 1 of row n, one 16-byte store).
+    const int hsrc = 16 * ((k & 7) >> 1) + n;
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
       for (int rt = 0; rt < RTR; ++rt) {
+        const bool odd = k & 1;
+        const uint4 hv = make_uint4(odd ? hg1[m][rt].x : hg0[m][rt].x, odd ? hg1[m][rt].y : hg0[m][rt].y,
+                                    odd ? hg1[m][rt].z : hg0[m][rt].z, odd ? hg1[m][rt].w : hg0[m][rt].w);
+        const uint4 hk = lane_fetch(hsrc, hv);
         float2 ac2[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const int i = 2 * g + t;
           float2 ac;
           if constexpr (FMT == kQ4_K) {
-            ac = q4k_scale(sl.s[m][rt], i);
+            ac = q4k_scale(hk, i);
           } else {
-            const uint4 h = sl.s[m][rt];
+            const uint4 h = hk;
             const uint64_t lo = (uint64_t)h.x | ((uint64_t)h.y << 32);
             const uint64_t hi = (uint64_t)h.z | ((uint64_t)h.w << 32);
             const uint32_t dw = (uint32_t)((g < 2 ? lo : hi) >> (32 * (g & 1)));  // halves 2g, 2g+1
@@ -347,9 +383,27 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, int e, int pos0, i
             make_float4(ac2[0].x, ac2[0].y, ac2[1].x, ac2[1].y);
       }
     __syncthreads();
-    if (k + 1 < NS) load_slab(sl, k + 1);
+    if (k + 1 < NS) {
+      if ((k & 7) == 7) load_group((k + 1) >> 3);
+      load_slab(sl, k + 1);
+    }
 
     const uint32_t* wl32 = reinterpret_cast<const uint32_t*>(wl);
+    // acc += a P - c X for one step's products (row scale pair ac = (a, c)).
+    f32x4 pp[NM][RTR], Xp;
+    float2 acp[NM][RTR];
+    auto apply = [&](const f32x4 (&pv)[NM][RTR], const f32x4& Xv, const float2 (&acv)[NM][RTR]) {
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int rt = 0; rt < RTR; ++rt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            float v = fmaf(acv[m][rt].x, pv[m][rt][j], acc[m][rt][j]);
+            if constexpr (FMT == kQ4_K) v = fmaf(-acv[m][rt].y, Xv[j], v);
+            acc[m][rt][j] = v;
+          }
+    };
 #pragma unroll
     for (int i = 0; i < kSlab; ++i) {
       const uint4 h4 = al[((i * 2 + 0) * 4 + g) * 16 + n];
@@ -383,21 +437,21 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, int e, int pos0, i
 #pragma unroll
         for (int rt = 0; rt < RTR; ++rt) p[m][rt] = mfma_bf16(alo, b[m][rt], p[m][rt]);
       if constexpr (FMT == kQ4_K) X = mfma_bf16(alo, ones, X);
+      // Scale the previous step's products while this step's MFMAs run.
+      if (i > 0) apply(pp, Xp, acp);
 #pragma unroll
       for (int m = 0; m < NM; ++m)
 #pragma unroll
         for (int rt = 0; rt < RTR; ++rt) {
-          const float2 ac = scl[(((m * RTR + rt) * 4 + (i >> 1)) * 16 + n) * 2 + (i & 1)];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            float v = fmaf(ac.x, p[m][rt][j], acc[m][rt][j]);
-            if constexpr (FMT == kQ4_K) v = fmaf(-ac.y, X[j], v);
-            acc[m][rt][j] = v;
-          }
+          pp[m][rt] = p[m][rt];
+          acp[m][rt] = scl[(((m * RTR + rt) * 4 + (i >> 1)) * 16 + n) * 2 + (i & 1)];
         }
+      Xp = X;
     }
+    apply(pp, Xp, acp);
   };
   Slab<FMT, NM, RTR> sl;
+  load_group(0);
   load_slab(sl, 0);
   for (int k = 0; k < NS; ++k) consume(sl, k);
 
@@ -475,14 +529,30 @@ __global__ __launch_bounds__(kBlock) void k_router_mfma(const float* __restrict_
   // Rows past M or E read as zero (offsets past the resources).
   const uint32_t xo = (t0 + n < M) ? (uint32_t)(t0 + n) * H * 4u : 0xFFFFFFF0u;
   const uint32_t wo = (e0 + n < E) ? (uint32_t)(e0 + n) * H * 4u : 0xFFFFFFF0u;
-  const int kq = H / kWavesPerBlock;  // H % 64 == 0
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int k = wv * kq; k < (wv + 1) * kq; k += 16) {
-    const uint32_t ko = 4u * (uint32_t)(k + 4 * g);
-    const f32x4 av = __builtin_amdgcn_raw_buffer_load_b128(xr, xo == 0xFFFFFFF0u ? xo : xo + ko, 0, 0);
-    const f32x4 bv = __builtin_amdgcn_raw_buffer_load_b128(wrr, wo == 0xFFFFFFF0u ? wo : wo + ko, 0, 0);
+  const int kq = H / kWavesPerBlock;  // H % 64 == 0: whole groups of 16 columns
+  const int kb = wv * kq, ke = kb + kq;
+  // Loads run kRing groups of 16 columns ahead of the MFMAs (the last
+  // groups re-read the wave's final group; those values are never used).
+  constexpr int kRing = 4;
+  auto load = [&](int k, f32x4& av, f32x4& bv) {
+    const uint32_t ko = 4u * (uint32_t)(min(k, ke - 16) + 4 * g);
+    av = __builtin_amdgcn_raw_buffer_load_b128(xr, xo == 0xFFFFFFF0u ? xo : xo + ko, 0, 0);
+    bv = __builtin_amdgcn_raw_buffer_load_b128(wrr, wo == 0xFFFFFFF0u ? wo : wo + ko, 0, 0);
+  };
+  f32x4 av[kRing], bv[kRing];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j], bv[j], acc, 0, 0, 0);
+  for (int u = 0; u < kRing; ++u) load(kb + 16 * u, av[u], bv[u]);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int k = kb; k < ke; k += 16 * kRing) {
+#pragma unroll
+    for (int u = 0; u < kRing; ++u) {
+      if (k + 16 * u < ke) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u][j], bv[u][j], acc, 0, 0, 0);
+      }
+      load(k + 16 * (u + kRing), av[u], bv[u]);
+    }
   }
   if (wv > 0) s_part[wv - 1][lane] = acc;
   __syncthreads();

@@ -520,7 +520,10 @@ void enqueue_route_plain(const Plan& p, const float* router, const float* x, con
   enqueue_logits(p, router, x, b.logits, st);
   hipLaunchKernelGGL(k_topk, dim3((p.M + kWavesPerBlock - 1) / kWavesPerBlock), dim3(kBlock), 0,
                      st, b.logits, b.ids, b.w, p.E, p.k, p.M);
-  hipLaunchKernelGGL(k_bucket, dim3(1), dim3(kBlock), 0, st, b.ids, p.M * p.k, p.E, bo);
+  if (p.M * p.k > 256)
+    hipLaunchKernelGGL(k_bucket_wide, dim3(1), dim3(kWideBlock), 0, st, b.ids, p.M * p.k, p.E, bo);
+  else
+    hipLaunchKernelGGL(k_bucket, dim3(1), dim3(kBlock), 0, st, b.ids, p.M * p.k, p.E, bo);
 }
 
 FfnArgs shared_gateup_args(const Plan& p, const moe_layer_weights* wt, const float* x,
@@ -674,7 +677,12 @@ bool flow_args(const Plan& p, const moe_layer_weights* wt, const float* x, float
 // ---- Batched path: grouped GEMMs on the matrix cores.
 constexpr int kGemmGateUpRtr = 2;  // row tiles of 16 per wave and matrix
 constexpr int kGemmDownRtr = 4;
-const char* const kGemmStageNames[kNumStages] = {"route", "gateup", "down_combine"};
+constexpr int kGemmQ8Rtr = 1;
+// Stages of the batched path; the shared expert's GEMMs are stages of their
+// own (empty without one), so that "gateup" is the routed gate/up GEMM alone.
+constexpr int kGemmStages = 5;
+const char* const kGemmStageNames[kGemmStages] = {"route", "shared_gateup", "gateup",
+                                                   "shared_down", "down_combine"};
 
 bool gemm_path(const Plan& p) {
   if (p.M <= kFusedMaxTokens) return false;
@@ -690,8 +698,8 @@ void launch_gemm_t(GemmArgs a, int tiles_cap, hipStream_t st) {
   const int per = kWavesPerBlock * 16 * RTR;
   a.row_blocks = (a.rows + per - 1) / per;
   const int t8 = (tiles_cap + 7) & ~7;
-  hipLaunchKernelGGL((k_gemm<FMT, GU, RTR>), dim3((unsigned)(t8 * a.row_blocks)), dim3(kBlock),
-                     0, st, a);
+  hipLaunchKernelGGL((k_gemm<FMT, GU, RTR>), dim3((unsigned)(t8 * a.row_blocks)), dim3(kBlock), 0,
+                     st, a);
 }
 
 void launch_gemm(int dtype, bool gateup, const GemmArgs& a, int tiles_cap, hipStream_t st) {
@@ -699,8 +707,10 @@ void launch_gemm(int dtype, bool gateup, const GemmArgs& a, int tiles_cap, hipSt
     if (gateup) launch_gemm_t<kQ4_K, true, kGemmGateUpRtr>(a, tiles_cap, st);
     else launch_gemm_t<kQ4_K, false, kGemmDownRtr>(a, tiles_cap, st);
   } else {
-    if (gateup) launch_gemm_t<kQ8_0, true, kGemmGateUpRtr>(a, tiles_cap, st);
-    else launch_gemm_t<kQ8_0, false, kGemmDownRtr>(a, tiles_cap, st);
+    // Q8_0 weight slabs are twice as long: fewer row tiles per wave keep
+    // two workgroups per CU.
+    if (gateup) launch_gemm_t<kQ8_0, true, kGemmQ8Rtr>(a, tiles_cap, st);
+    else launch_gemm_t<kQ8_0, false, kGemmQ8Rtr>(a, tiles_cap, st);
   }
 }
 
@@ -733,6 +743,7 @@ void forward_gemm(const Plan& p, const moe_layer_weights* wt, const float* x, fl
     a.dense_tokens = p.M;
     launch_gemm(p.st, true, a, dense_tiles, st);
   }
+  mark(ev, 2, st);
   {
     GemmArgs a{};
     a.w0 = (const uint8_t*)wt->gate;
@@ -751,7 +762,7 @@ void forward_gemm(const Plan& p, const moe_layer_weights* wt, const float* x, fl
     launch_gemm(p.et, true, a, p.tiles_cap, st);
   }
 
-  mark(ev, 2, st);
+  mark(ev, 3, st);
   if (shared) {
     GemmArgs a{};
     a.w0 = (const uint8_t*)wt->shared_down;
@@ -764,6 +775,7 @@ void forward_gemm(const Plan& p, const moe_layer_weights* wt, const float* x, fl
     a.dense_tokens = p.M;
     launch_gemm(p.st, false, a, dense_tiles, st);
   }
+  mark(ev, 4, st);
   {
     GemmArgs a{};
     a.w0 = (const uint8_t*)wt->down;
@@ -783,7 +795,7 @@ void forward_gemm(const Plan& p, const moe_layer_weights* wt, const float* x, fl
   const int64_t n4 = (int64_t)p.M * (p.H / 4);
   hipLaunchKernelGGL(k_combine, dim3((unsigned)((n4 + kBlock - 1) / kBlock)), dim3(kBlock), 0, st,
                      b.o, shared ? b.s : nullptr, b.w, y, p.M, p.H, p.k);
-  mark(ev, 3, st);
+  mark(ev, 5, st);
 }
 
 int forward_impl(const moe_layer_desc* desc, const moe_layer_weights* wt, const float* x,
@@ -795,7 +807,7 @@ int forward_impl(const moe_layer_desc* desc, const moe_layer_weights* wt, const 
   if (rc != MOE_OK) return rc;
   const Buffers nob{};
   const bool flow = flow_args(p, wt, x, y, nob, nullptr);
-  const int n_stages = flow ? 1 : kNumStages;
+  const int n_stages = flow ? 1 : gemm_path(p) ? kGemmStages : kNumStages;
   if (events && n_events != n_stages + 1) return MOE_ERR_ARG;
   hipStream_t st = (hipStream_t)hip_stream;
   hipEvent_t* ev = events ? (hipEvent_t*)events : nullptr;
@@ -957,7 +969,8 @@ int32_t moe_stage_count(const moe_layer_desc* desc, int32_t n_tokens) {
   const int rc = make_plan(desc, n_tokens, &p);
   if (rc != MOE_OK) return -rc;
   const Buffers nob{};
-  return flow_args(p, nullptr, nullptr, nullptr, nob, nullptr) ? 1 : kNumStages;
+  if (flow_args(p, nullptr, nullptr, nullptr, nob, nullptr)) return 1;
+  return gemm_path(p) ? kGemmStages : kNumStages;
 }
 
 const char* moe_stage_name(const moe_layer_desc* desc, int32_t n_tokens, int32_t i) {

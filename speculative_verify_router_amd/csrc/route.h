@@ -331,4 +331,85 @@ __global__ __launch_bounds__(kBlock) void k_bucket(const int32_t* __restrict__ i
   bucket_block(ids, n_pairs, E, o);
 }
 
+// The same outputs for large batches, by one workgroup of 16 waves: wave w
+// ranks its own contiguous chunk of pairs, starting each expert's cursor at
+// the expert's offset plus the pairs of that expert in earlier chunks.
+constexpr int kWideWaves = 16;
+constexpr int kWideBlock = kWideWaves * kWave;
+
+__global__ __launch_bounds__(kWideBlock) void k_bucket_wide(const int32_t* __restrict__ ids,
+                                                            int n_pairs, int E, BucketOut o) {
+  __shared__ int32_t s_hist[kWideWaves][kMaxExperts];  // per-chunk counts, then cursors
+  __shared__ int32_t s_wc[kWideWaves], s_wa[kWideWaves];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid >> 6;
+  for (int i = tid; i < kWideWaves * kMaxExperts; i += kWideBlock) s_hist[i / kMaxExperts][i % kMaxExperts] = 0;
+  const int chunk = (n_pairs + kWideWaves * kWave - 1) / (kWideWaves * kWave) * kWave;
+  const int c0 = min(wv * chunk, n_pairs), c1 = min(c0 + chunk, n_pairs);
+  __syncthreads();
+  for (int p = c0 + lane; p < c1; p += kWave) atomicAdd(&s_hist[wv][ids[p]], 1);
+  __syncthreads();
+  // Thread e: expert e's count, and its per-chunk counts turned into
+  // exclusive prefixes over the chunks.
+  int cnt = 0;
+  if (tid < E) {
+    for (int w = 0; w < kWideWaves; ++w) {
+      const int h = s_hist[w][tid];
+      s_hist[w][tid] = cnt;
+      cnt += h;
+    }
+  }
+  const int act = cnt > 0;
+  int cinc = cnt, ainc = act;
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int oc = __shfl_up(cinc, off, kWave);
+    const int oa = __shfl_up(ainc, off, kWave);
+    if (lane >= off) {
+      cinc += oc;
+      ainc += oa;
+    }
+  }
+  if (lane == kWave - 1) {
+    s_wc[wv] = cinc;
+    s_wa[wv] = ainc;
+  }
+  if (tid < E && o.active) o.active[tid] = -1;
+  __syncthreads();
+  int cbase = 0, abase = 0;
+  for (int w = 0; w < wv; ++w) {
+    cbase += s_wc[w];
+    abase += s_wa[w];
+  }
+  const int off = cbase + cinc - cnt, aex = abase + ainc - act;
+  if (tid < E) {
+    if (o.counts) o.counts[tid] = cnt;
+    if (o.offsets) o.offsets[tid] = off;
+    if (o.active && act) o.active[aex] = tid;
+    for (int w = 0; w < kWideWaves; ++w) s_hist[w][tid] += off;
+  }
+  if (tid == E - 1) {
+    if (o.offsets) o.offsets[E] = off + cnt;
+    if (o.n_active) *o.n_active = aex + act;
+  }
+  __syncthreads();
+  if (!o.slots) return;
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  for (int p0 = c0; p0 < c1; p0 += kWave) {
+    const int p = p0 + lane;
+    const bool valid = p < c1;
+    const int e = valid ? ids[p] : -1;
+    uint64_t same = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = valid && ((e >> b) & 1);
+      const uint64_t bal = __ballot(bit);
+      same &= bit ? bal : ~bal;
+    }
+    if (valid) o.slots[s_hist[wv][e] + __popcll(same & below)] = p;
+    __builtin_amdgcn_wave_barrier();
+    if (valid && (same & below) == 0) s_hist[wv][e] += __popcll(same);
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
 }  // namespace svr

@@ -52,7 +52,8 @@ def test_stage_lists_follow_the_launch_path():
         assert _stage_names(d, M) == ["route_shared_gateup", "gateup", "down_combine"]
     # Batches above 16 tokens: the grouped-GEMM path.
     for M in (17, 512):
-        assert _stage_names(d, M) == ["route", "gateup", "down_combine"]
+        assert _stage_names(d, M) == ["route", "shared_gateup", "gateup", "shared_down",
+                                      "down_combine"]
     # Shapes without a single-launch instantiation take the staged path.
     odd = svr.LayerDesc(640, 5, 2, 96, 160, "q8_0", "q8_0", single_launch=True)
     assert _stage_names(odd, 2) == ["route_shared_gateup", "gateup", "down_combine"]

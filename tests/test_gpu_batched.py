@@ -81,13 +81,14 @@ def test_repeatable_and_timed():
     cfg = small_config(hidden=512, n_experts=16, top_k=4, ffn=256, shared_ffn=96,
                        expert_type="q4_k", n_tokens=50, router_std=0.2, seed_index=730)
     d = desc_of(cfg)
-    assert svr.moe_stage_count(d, 50) == 3
-    assert [svr.moe_stage_name(d, 50, i) for i in range(3)] == ["route", "gateup", "down_combine"]
+    assert svr.moe_stage_count(d, 50) == 5
+    assert [svr.moe_stage_name(d, 50, i) for i in range(5)] == [
+        "route", "shared_gateup", "gateup", "shared_down", "down_combine"]
     inp, x, w, y, ref = _case(cfg)
     y2, _, _ = gpu_forward(cfg, w, x)
     assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
     # Timed call: same result, one event per stage boundary.
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
     for e in ev:
         e.record()
     torch.cuda.synchronize()
@@ -95,7 +96,7 @@ def test_repeatable_and_timed():
     svr.moe_layer_forward_timed(d, w, dev(x), yt, [e.cuda_event for e in ev])
     torch.cuda.synchronize()
     assert np.array_equal(yt.cpu().numpy().view(np.uint32), y.view(np.uint32))
-    assert all(ev[i].elapsed_time(ev[i + 1]) >= 0 for i in range(3))
+    assert all(ev[i].elapsed_time(ev[i + 1]) >= 0 for i in range(5))
 
 
 def test_route_lists_of_a_batch():
