@@ -172,6 +172,107 @@ def summarize_counters(fetch_dir: str, write_dir: str, workload: str, copy_bytes
     return out
 
 
+def accept_bytes(rows: int, vocab: int, h_dim: int) -> int:
+    """Algorithmic HBM bytes of one verify/accept call: the logits, the
+    drafts, one verify row read and written as pending_h, the outputs."""
+    return rows * vocab * 4 + (rows - 1) * 4 + 2 * h_dim * 4 + (2 * rows + 1) * 4
+
+
+def cpu_baseline_accept(batch) -> dict:
+    """The verify/accept oracle as it stands, repeated on one batch for about 10 s."""
+    from oracle import accept_oracle as ao
+    calls, t0 = 0, time.perf_counter()
+    while True:
+        ao.verify_accept(batch.logits, batch.drafts, batch.verify_h)
+        calls += 1
+        dt = time.perf_counter() - t0
+        if dt >= 10.0:
+            break
+    M, V = batch.logits.shape
+    return {"value": calls / dt, "unit": "batches/s", "cores": 1, "kind": "oracle",
+            "sample": f"{calls} oracle calls on one verify batch ({M} rows x {V} logits, "
+                      f"NumPy on one thread), {dt:.1f} s"}
+
+
+def bench_accept(args) -> int:
+    """Greedy verify/accept of a verify batch (moe_verify_accept): batches/s.
+
+    Calls rotate over enough seeded batches (about 330 MB of logits) that no
+    call finds its logits in the 256 MB Infinity Cache; every timed call is
+    bracketed by HIP events on the launch stream."""
+    import torch
+    import speculative_verify_router_amd as svr
+    import synth
+
+    w = synth.ACCEPT_WORKLOADS[args.workload]
+    M, V, Hd = w["rows"], w["vocab"], w["h_dim"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    per = M * V * 4
+    R = max(args.instances, (330 << 20) // per + 1)
+    batches, host0 = [], None
+    for i in range(R):
+        b = synth.draw_verify_batch(M, V, Hd, i % M, seed=i)
+        up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+        batches.append((up(b.logits), up(b.drafts), up(b.verify_h)))
+        if i == 0:
+            host0 = b
+    print(f"# {R} verify batches resident", file=sys.stderr, flush=True)
+    ws = svr.accept_workspace(M, V, dev)
+    tok = torch.empty(M, dtype=torch.int32, device=dev)
+    acc = torch.empty(M, dtype=torch.int32, device=dev)
+    n = torch.empty(1, dtype=torch.int32, device=dev)
+    pend = torch.empty(Hd, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def call(i):
+        lg, dr, vh = batches[i % R]
+        svr.moe_verify_accept(lg, dr, tok, acc, n, vh, pend, ws=ws, stream=stream)
+
+    for s in range(max(args.warmup, 1)):
+        call(s)
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        evs[s][0].record(stream)
+        call(s)
+        evs[s][1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ev_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    nbytes = accept_bytes(M, V, Hd)
+    achieved = nbytes / (ev_ms * 1e-3) / 1e9
+    out = {
+        "metric": f"greedy MTP verify/accept batches/s (M={M} rows, {V}-column logits), 1 MI355X",
+        "value": round(K / elapsed, 1),
+        "unit": "batches/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / K, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "rows": M, "vocab": V, "h_dim": Hd,
+                   "batches_rotated": R},
+        "roofline": {
+            "kernel": "k_accept", "bound": "hbm", "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic_for("k_accept", args.workload), "bytes_per_launch": nbytes,
+            "avg_launch_us": round(ev_ms * 1e3, 3), "timed_launches": K,
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_accept(host0)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -215,6 +316,8 @@ def main(argv=None) -> int:
     import speculative_verify_router_amd as svr
     import synth
 
+    if args.workload in synth.ACCEPT_WORKLOADS:
+        return bench_accept(args)
     cfg = synth.CONFIGS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

@@ -3,18 +3,22 @@
 One routed-MoE FFN block (F32 softmax top-k router, Q4_K / Q8_0 experts,
 SwiGLU, a shared expert and a weighted combine) applied to the verify batch
 of MTP speculative decoding, implemented as hand-written HIP kernels behind
-the C ABI of ``include/moe_layer.h``.  This package is the thin Python
+the C ABI of ``include/moe_layer.h``, plus greedy MTP verify/accept
+(``include/moe_accept.h``).  This package is the thin Python
 binding of that ABI (``_binding``) and the build helper (``build``).
 """
 
 from ._binding import (  # noqa: F401
+    ACCEPT_MAX_ROWS,
     C_SYMBOLS,
     LIB_PATH,
     LayerDesc,
     LayerWeights,
     MoeError,
     PreparedForward,
+    accept_workspace,
     lib,
+    moe_accept_workspace_bytes,
     moe_dequant_rows,
     moe_layer_forward,
     moe_layer_forward_timed,
@@ -23,6 +27,7 @@ from ._binding import (  # noqa: F401
     moe_stage_name,
     moe_strerror,
     moe_tensor_bytes,
+    moe_verify_accept,
     moe_version,
     moe_workspace_bytes,
     workspace,

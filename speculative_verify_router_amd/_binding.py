@@ -105,6 +105,8 @@ def lib():
             "moe_stage_count": (i32, [D, i32]),
             "moe_stage_name": (ctypes.c_char_p, [D, i32, i32]),
             "moe_dequant_rows": (i32, [i32, vp, i64, i32, i64, i64, vp, vp]),
+            "moe_accept_workspace_bytes": (i32, [i32, i64, ctypes.POINTER(sz)]),
+            "moe_verify_accept": (i32, [vp, i32, i64, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -117,7 +119,8 @@ def lib():
 # Exported names of the C ABI (the header declares exactly these).
 C_SYMBOLS = ("moe_version", "moe_strerror", "moe_tensor_bytes", "moe_workspace_bytes",
              "moe_route", "moe_layer_forward", "moe_layer_forward_timed", "moe_stage_count",
-             "moe_stage_name", "moe_dequant_rows")
+             "moe_stage_name", "moe_dequant_rows", "moe_accept_workspace_bytes",
+             "moe_verify_accept")
 
 
 def _ptr(t: Optional[torch.Tensor], dtype) -> Optional[int]:
@@ -279,3 +282,44 @@ def moe_dequant_rows(dtype: str, tensor: torch.Tensor, rows: int, cols: int, row
     st = lib().moe_dequant_rows(_DTYPES[dtype], _ptr(tensor, None), rows, cols, row_start,
                                 row_count, _ptr(out, torch.float32), _stream(stream))
     _check(st, "moe_dequant_rows")
+
+
+# include/moe_accept.h: greedy verify/accept of an MTP verify batch.
+ACCEPT_MAX_ROWS = 64
+
+
+def moe_accept_workspace_bytes(max_rows: int, vocab: int) -> int:
+    out = ctypes.c_size_t()
+    _check(lib().moe_accept_workspace_bytes(max_rows, vocab, ctypes.byref(out)),
+           "moe_accept_workspace_bytes")
+    return out.value
+
+
+def accept_workspace(max_rows: int, vocab: int, device="cuda") -> torch.Tensor:
+    """A zero-filled device workspace for moe_verify_accept (its counter line
+    must start at zero; calls keep it so)."""
+    return torch.zeros(moe_accept_workspace_bytes(max_rows, vocab), dtype=torch.uint8,
+                       device=device)
+
+
+def moe_verify_accept(logits: torch.Tensor, drafts: Optional[torch.Tensor], tokens: torch.Tensor,
+                      accepted: torch.Tensor, n_accepted: torch.Tensor,
+                      verify_h: Optional[torch.Tensor] = None,
+                      pending_h: Optional[torch.Tensor] = None, ws: torch.Tensor = None,
+                      stream=None, n_rows: Optional[int] = None, vocab: Optional[int] = None):
+    """logits [M][V] float32; drafts [M-1] int32 (None for M == 1); tokens,
+    accepted [M] and n_accepted [1] int32 outputs; verify_h [M][h] and
+    pending_h [h] float32, both or neither.  ``n_rows``/``vocab`` override
+    the shape read from ``logits`` (for error-path tests)."""
+    M = logits.shape[0] if n_rows is None else n_rows
+    V = logits.shape[-1] if vocab is None else vocab
+    if ws is None:
+        ws = accept_workspace(max(M, 1), max(V, 1), logits.device)
+    h_dim = 0 if verify_h is None else verify_h.shape[-1]
+    i32 = torch.int32
+    st = lib().moe_verify_accept(_ptr(logits, torch.float32), M, V, _ptr(drafts, i32),
+                                 _ptr(verify_h, torch.float32), h_dim, _ptr(tokens, i32),
+                                 _ptr(accepted, i32), _ptr(n_accepted, i32),
+                                 _ptr(pending_h, torch.float32), _ptr(ws, torch.uint8), ws.numel(),
+                                 _stream(stream))
+    _check(st, "moe_verify_accept")

@@ -18,9 +18,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libsvr_moe.so")
-SOURCES = [os.path.join(CSRC, "moe_layer.hip")]
-HEADERS = [os.path.join(CSRC, f) for f in ("common.h", "quant.h", "route.h", "ffn.h", "phases.h", "misc.h")] + [
-    os.path.join(ROOT, "include", "moe_layer.h")]
+SOURCES = [os.path.join(CSRC, "moe_layer.hip"), os.path.join(CSRC, "accept.hip")]
+HEADERS = [os.path.join(CSRC, f) for f in ("common.h", "quant.h", "route.h", "ffn.h", "phases.h", "misc.h",
+                                           "flow.h", "gemm.h")] + [
+    os.path.join(ROOT, "include", h) for h in ("moe_layer.h", "moe_accept.h")]
 
 ARCH = "gfx950"
 

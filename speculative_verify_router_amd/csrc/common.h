@@ -116,6 +116,18 @@ __device__ __forceinline__ float silu(float g) {
   return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
 }
 
+// Order-preserving 32-bit key of a float: a larger value gives a larger
+// key; -0 maps to +0's key and NaN to -inf's.  Every finite or infinite
+// value has a key of at least 0x007FFFFF, so 0 is below all of them.
+__device__ __forceinline__ uint32_t order_key(float v) {
+  v = (v != v) ? -INFINITY : v + 0.0f;
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __builtin_bit_cast(float, (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
 // Buffer resource over [base, base + bytes): 16-byte loads with 32-bit
 // offsets; reads past `bytes` return zero.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

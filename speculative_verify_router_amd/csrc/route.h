@@ -133,14 +133,6 @@ __global__ __launch_bounds__(kBlock) void k_router_logits(const float* __restric
 // winner, marks it taken and refreshes its candidate.  Then
 // w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t order_key(float v) {
-  v = (v != v) ? -INFINITY : v + 0.0f;
-  const uint32_t u = __builtin_bit_cast(uint32_t, v);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float key_value(uint32_t k) {
-  return __builtin_bit_cast(float, (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
-}
 
 template <bool COHERENT, int NV>
 __device__ __forceinline__ void topk_token_nv(const float* __restrict__ row,

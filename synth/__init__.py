@@ -4,7 +4,8 @@ This package draws router weights, activations and block-quantised expert
 tensors from fixed seeds and packs them into the byte layouts that
 ``include/moe_layer.h`` documents.  It holds none of the layer's arithmetic
 (no routing, no dequantisation, no matrix products); the CPU oracle and the
-HIP library both read the bytes it writes.
+HIP library both read the bytes it writes.  ``verify`` draws the seeded
+verify batches (logits, drafts, hidden-state rows) of greedy verify/accept.
 """
 
 from .layers import (  # noqa: F401
@@ -20,3 +21,4 @@ from .layers import (  # noqa: F401
     quantize_q8_0,
     tensor_bytes,
 )
+from .verify import ACCEPT_WORKLOADS, VerifyBatch, draw_verify_batch  # noqa: F401,E402

@@ -12,14 +12,16 @@ import speculative_verify_router_amd as svr
 from speculative_verify_router_amd import _binding as B
 import synth
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
-                      "moe_layer.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
 
 
 def _declared():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    names = set()
+    for h in sorted(os.listdir(INCLUDE)):
+        if h.endswith(".h"):
+            text = re.sub(r"/\*.*?\*/", "", open(os.path.join(INCLUDE, h)).read(), flags=re.S)
+            names |= set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_the_binding_symbols():
@@ -194,3 +196,48 @@ def test_unknown_flag_bits_are_rejected():
     assert svr.lib().moe_workspace_bytes(ctypes.byref(d), 4, ctypes.byref(out)) == B.ERR_ARG
     d.flags = B.SINGLE_LAUNCH
     assert svr.lib().moe_workspace_bytes(ctypes.byref(d), 4, ctypes.byref(out)) == B.OK
+
+
+# --- include/moe_accept.h ---------------------------------------------------
+
+
+def test_accept_workspace_sizes():
+    small = svr.moe_accept_workspace_bytes(4, 1000)
+    big = svr.moe_accept_workspace_bytes(4, 131072)
+    assert 256 < small <= big and big % 256 == 0
+    assert svr.moe_accept_workspace_bytes(64, 1 << 30) >= svr.moe_accept_workspace_bytes(4, 1 << 30)
+    L = svr.lib()
+    out = ctypes.c_size_t()
+    assert L.moe_accept_workspace_bytes(0, 10, ctypes.byref(out)) == B.ERR_SHAPE
+    assert L.moe_accept_workspace_bytes(65, 10, ctypes.byref(out)) == B.ERR_SHAPE
+    assert L.moe_accept_workspace_bytes(4, 0, ctypes.byref(out)) == B.ERR_SHAPE
+    assert L.moe_accept_workspace_bytes(4, (1 << 30) + 1, ctypes.byref(out)) == B.ERR_SHAPE
+    assert L.moe_accept_workspace_bytes(4, 10, None) == B.ERR_NULL
+
+
+def _accept(logits=FAKE, M=4, V=131072, drafts=FAKE, vh=FAKE, hd=4096, tokens=FAKE, acc=FAKE,
+            n=FAKE, pend=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    return svr.lib().moe_verify_accept(logits, M, V, drafts, vh, hd, tokens, acc, n, pend, ws,
+                                       ws_bytes, None)
+
+
+def test_accept_error_paths():
+    need = svr.moe_accept_workspace_bytes(4, 131072)
+    assert _accept(ws_bytes=need - 1) == B.ERR_WORKSPACE
+    assert _accept(logits=None) == B.ERR_NULL
+    assert _accept(tokens=None) == B.ERR_NULL
+    assert _accept(acc=None) == B.ERR_NULL
+    assert _accept(n=None) == B.ERR_NULL
+    assert _accept(ws=None) == B.ERR_NULL
+    assert _accept(drafts=None) == B.ERR_NULL            # drafts needed with more than one row
+    assert _accept(pend=None) == B.ERR_NULL              # verify_h without pending_h
+    assert _accept(vh=None, hd=16) == B.ERR_NULL         # pending_h without verify_h
+    assert _accept(vh=None, pend=None, hd=16) == B.ERR_SHAPE
+    assert _accept(M=-1) == B.ERR_SHAPE
+    assert _accept(M=65) == B.ERR_SHAPE
+    assert _accept(V=0) == B.ERR_SHAPE
+    assert _accept(V=(1 << 30) + 1) == B.ERR_SHAPE
+    assert _accept(hd=-1) == B.ERR_SHAPE
+    assert _accept(ws=FAKE + 16) == B.ERR_ARG            # misaligned workspace
+    assert _accept(logits=FAKE + 2) == B.ERR_ARG         # logits not 4-byte aligned
+    assert _accept(M=0, logits=None, ws=None) == B.OK    # empty batch: nothing enqueued
