@@ -114,13 +114,19 @@ __device__ __forceinline__ void compute_stage(const Stage<FMT, CPL, GATEUP>& s,
     const int sub = cc[ci] & 7;  // Q4_K sub-block of this chunk
     const ChunkScale k0 = decode_scale(s.c0[ci], sub);
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
-      acc0[t] = fmaf(k0.a, chunk_dot(s.c0[ci], xs[t][ci]), fmaf(-k0.b, xs[t][ci].sum, acc0[t]));
+    for (int t = 0; t < NT; ++t) {
+      const float v = chunk_dot(s.c0[ci], xs[t][ci]) * xs[t][ci].s;
+      acc0[t] = FMT == kQ8_0 ? fmaf(k0.a, v, acc0[t])
+                             : fmaf(k0.a, v, fmaf(-k0.b, xs[t][ci].sum, acc0[t]));
+    }
     if (GATEUP) {
       const ChunkScale k1 = decode_scale(s.c1[ci], sub);
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
-        acc1[t] = fmaf(k1.a, chunk_dot(s.c1[ci], xs[t][ci]), fmaf(-k1.b, xs[t][ci].sum, acc1[t]));
+      for (int t = 0; t < NT; ++t) {
+        const float v = chunk_dot(s.c1[ci], xs[t][ci]) * xs[t][ci].s;
+        acc1[t] = FMT == kQ8_0 ? fmaf(k1.a, v, acc1[t])
+                               : fmaf(k1.a, v, fmaf(-k1.b, xs[t][ci].sum, acc1[t]));
+      }
     }
   }
 #pragma unroll

@@ -220,19 +220,22 @@ void size_role(FfnArgs& a, int dtype, int slots, int64_t blocks) {
   a.units_per_block = (int)upb;
 }
 
-// Shared-expert tiles sized by the bytes each wave streams: a wave's token
-// group of 4 / M waves shares a tile's rows (see ffn_tile_tokens).
-constexpr double kSharedWaveBytes = 24.0 * 1024.0;
-void size_shared_tiles(FfnArgs& a, int dtype, bool gateup, double wave_bytes) {
+// Shared-expert tiles of phase 1: the workgroup slots of one resident round
+// that the router rows leave free (at least a quarter of the round), each
+// taking an equal share of the rows.  A wave's token group of 4 / M waves
+// shares a tile's rows (see ffn_tile_tokens), so a tile is a whole number
+// of that group's steps.
+void size_shared_tiles(FfnArgs& a, int dtype, int64_t blocks) {
   FfnShape s;
   ffn_shape(dtype, a.K, &s);
   a.lpr = s.lpr;
   const int G = kWave / s.lpr;
   const int rg = a.n_tokens < kWavesPerBlock ? kWavesPerBlock / a.n_tokens : 1;
-  const double rb = (gateup ? 2.0 : 1.0) * (dtype == MOE_Q8_0 ? a.K / 32 * 34.0 : a.K / 256 * 144.0);
-  int rows = (int)(wave_bytes * rg / rb) / (rg * G) * (rg * G);
-  if (rows < rg * G) rows = rg * G;
-  a.units_per_block = rows;
+  const int unit = rg * G;
+  if (blocks < 1) blocks = 1;
+  int64_t rows = (a.rows_per_expert + blocks - 1) / blocks;
+  rows = (rows + unit - 1) / unit * unit;
+  a.units_per_block = (int)rows;
 }
 
 int tiles_of(const FfnArgs& a) {
@@ -277,16 +280,16 @@ constexpr int key(int fmt, int code) { return fmt * 65536 + code; }
 int exact_key(int dtype, const FfnShape& s) { return key(qfmt(dtype), shape_code(s.cpl, s.lpr)); }
 int generic_key(int dtype, const FfnShape& s) { return key(qfmt(dtype), shape_code(s.cpl, 0)); }
 
-// Phase 1: router rows (NC float4 per lane) + shared gate/up in small tiles
-// (about kSharedWaveBytes per wave), which also fill the slots the router
-// workgroups free.
+// Phase 1: router rows (NC float4 per lane) + shared gate/up tiles in the
+// rest of one resident round.
 template <int NC>
 bool launch_phase1_nc(int skey, hipStream_t st, const RouteArgs& r, FfnArgs s, int sdtype) {
   switch (skey) {
 #define SVR_P1(F, C, L)                                                                  \
   case key(F, shape_code(C, L)): {                                                       \
     auto k = k_phase1<NC, F, shape_code(C, L)>;                                          \
-    size_shared_tiles(s, sdtype, true, kSharedWaveBytes);                               \
+    const int64_t cap = resident_blocks(k);                                              \
+    size_shared_tiles(s, sdtype, std::max<int64_t>(cap - r.n_router_blocks, cap / 4));  \
     hipLaunchKernelGGL(k, dim3(r.n_router_blocks + tiles_of(s)), dim3(kBlock), 0, st, r, s); \
     return true;                                                                         \
   }
@@ -365,19 +368,49 @@ bool launch_dual(int adtype, const FfnShape& as, int bdtype, const FfnShape& bs,
          launch_dual_keys(generic_key(adtype, as), generic_key(bdtype, bs), st, a, b, d);
 }
 
+// Phase 3 with pair slots: one workgroup per (token, row tile), one
+// resident round of them (the rows of a tile a whole number of wave steps,
+// at most one per thread).
+template <int F, int S>
+bool launch_down_tok_t(hipStream_t st, FfnArgs a, const CombineArgs& c, int dtype) {
+  auto k = k_down_tok<F, S>;
+  FfnShape s;
+  ffn_shape(dtype, a.K, &s);
+  a.lpr = s.lpr;
+  const int G = kWave / s.lpr;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kDownTokThreads, 0) != hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  int64_t tiles = (int64_t)per_cu * device_cus() / (c.M > 0 ? c.M : 1);
+  if (tiles < 1) tiles = 1;
+  int64_t upb = (a.rows_per_expert + tiles - 1) / tiles;
+  upb = (upb + G - 1) / G * G;
+  if (upb > kDownTokRows) upb = kDownTokRows / G * G;
+  a.units_per_block = (int)upb;
+  const int nt = (a.rows_per_expert + a.units_per_block - 1) / a.units_per_block;
+  hipLaunchKernelGGL(k, dim3((unsigned)(nt * c.M)), dim3(kDownTokThreads), 0, st, a, c, nt);
+  return true;
+}
+
+bool launch_down_tok(int dtype, const FfnShape& ds, hipStream_t st, const FfnArgs& a,
+                     const CombineArgs& c) {
+#define SVR_DT(F, C, L) \
+  if (key(F, shape_code(C, L)) == kk) return launch_down_tok_t<F, shape_code(C, L)>(st, a, c, dtype);
+  for (int kk : {exact_key(dtype, ds), generic_key(dtype, ds)}) {
+    SVR_DT(kQ4_K, 3, 16) SVR_DT(kQ8_0, 5, 16) SVR_DT(kQ8_0, 3, 32)
+    SVR_DT(kQ4_K, 1, 0) SVR_DT(kQ4_K, 2, 0) SVR_DT(kQ4_K, 3, 0) SVR_DT(kQ8_0, 1, 0)
+    SVR_DT(kQ8_0, 2, 0) SVR_DT(kQ8_0, 3, 0) SVR_DT(kQ8_0, 4, 0) SVR_DT(kQ8_0, 5, 0)
+    SVR_DT(kQ8_0, 6, 0)
+  }
+#undef SVR_DT
+  return false;
+}
+
 // Phase 3: routed down + combine, one resident round of row tiles x slots.
 template <int F, int S>
 bool launch_down_combine_t(hipStream_t st, FfnArgs a, const CombineArgs& c, int dtype, int slots) {
-  const bool pair_lds = a.pair_expert != nullptr;
-  if (pair_lds) {
-    auto k = k_down_combine<F, S, true>;
-    size_role(a, dtype, slots, resident_blocks(k));
-    if (tiles_of(a) <= kMaxTiles && a.units_per_block <= kDownLdsRows) {
-      hipLaunchKernelGGL(k, dim3(tiles_of(a), slots), dim3(kBlock), 0, st, a, c);
-      return true;
-    }
-  }
-  auto k = k_down_combine<F, S, false>;
+  auto k = k_down_combine<F, S>;
   size_role(a, dtype, slots, resident_blocks(k));
   const int tiles = tiles_of(a);
   if (tiles > kMaxTiles) return false;
@@ -907,7 +940,9 @@ int forward_impl(const moe_layer_desc* desc, const moe_layer_weights* wt, const 
     FfnShape ds;
     ffn_shape(p.et, p.F, &ds);
     CombineArgs c{b.o, shared ? b.s : nullptr, b.w, y, p.M, p.H, p.k, b.ctr};
-    if (!launch_down_combine(p.et, ds, st, rd, c, slots_max)) {
+    if (pairs && launch_down_tok(p.et, ds, st, rd, c)) {
+      // one workgroup per (token, row tile), combined in LDS
+    } else if (!launch_down_combine(p.et, ds, st, rd, c, slots_max)) {
       rd.coherent_out = 0;
       if (!launch_ffn(p.et, false, rd, slots_max, st)) return MOE_ERR_SHAPE;
       const int64_t n4 = (int64_t)p.M * (p.H / 4);

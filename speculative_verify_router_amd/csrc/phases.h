@@ -134,32 +134,62 @@ struct CombineArgs {
 };
 
 // Phase 3: routed down tiles, then the combine of each finished row tile.
-// PAIR_LDS (per-pair slots): the tile's outputs are gathered in LDS and
-// written out as one contiguous range after the row loop, so that no store
-// sits between the row loop's loads and their waits.
-constexpr int kDownLdsRows = 2048;
 // Ring depth of the routed down rows: a one-matrix row of a few hundred
 // bytes per lane group needs several steps in flight to cover the latency.
 constexpr int kDownNst = 4;
 
-template <int FMT, int S, bool PAIR_LDS>
+// Phase 3 for pair slots (up to four tokens): one workgroup of eight waves
+// per (token, row tile).  In each pass of eight slots, wave w streams the
+// tile's rows of the expert of pair (t, j0 + w) against that pair's h and
+// leaves them in LDS; after a barrier each thread owns one row and adds
+// the pass's slots in order onto y[t][r] = s[t][r] + sum_j w[t][j] o_j[r].
+// The combine needs no counters and no reads past L2: routing, h and s all
+// come from earlier launches.
+constexpr int kDownTokWaves = 8;
+constexpr int kDownTokThreads = kDownTokWaves * kWave;
+constexpr int kDownTokRows = kDownTokThreads;  // rows of a tile, one per thread
+
+template <int FMT, int S>
+__global__ __launch_bounds__(kDownTokThreads) void k_down_tok(FfnArgs a, CombineArgs c,
+                                                              int tiles) {
+  constexpr int CPL = shape_cpl(S), LPR = shape_lpr(S);
+  __shared__ float s_o[kDownTokWaves * kDownTokRows];
+  const int t = blockIdx.x / tiles, tile = blockIdx.x - t * tiles;
+  const int wv = threadIdx.x >> 6;
+  const int ub = tile * a.units_per_block;
+  const int ue = min(ub + a.units_per_block, a.rows_per_expert);
+  const int r = ub + (int)threadIdx.x;  // the row this thread combines
+  const bool own = r < ue;
+  float acc = 0.f;
+  if (own && c.s) acc = c.s[(int64_t)t * c.H + r];
+  const int G = kWave / (LPR ? LPR : a.lpr);
+  for (int j0 = 0; j0 < c.k; j0 += kDownTokWaves) {
+    const int j = j0 + wv;
+    if (j < c.k) {  // wave-uniform
+      const int p = t * c.k + j;
+      const int ids1[1] = {p}, slot1[1] = {wv};
+      ffn_pass<FMT, CPL, 1, false, kDownNst, true, LPR>(
+          a, a.pair_expert[p], ids1, ub, G, ue, LdsOut{s_o, ub, kDownTokRows}, slot1);
+    }
+    __syncthreads();
+    if (own) {
+      const int nj = min(kDownTokWaves, c.k - j0);
+      for (int w = 0; w < nj; ++w)
+        acc = fmaf(c.w[(int64_t)t * c.k + j0 + w], s_o[w * kDownTokRows + (r - ub)], acc);
+    }
+    __syncthreads();  // s_o is refilled by the next pass
+  }
+  if (own) c.y[(int64_t)t * c.H + r] = acc;
+}
+
+template <int FMT, int S>
 __global__ __launch_bounds__(kBlock) void k_down_combine(FfnArgs a, CombineArgs c) {
   constexpr int CPL = shape_cpl(S), LPR = shape_lpr(S);
   __shared__ int s_last;
-  __shared__ float s_out[PAIR_LDS ? kDownLdsRows : 1];
   const int tile = blockIdx.x, slot = blockIdx.y;
   const int n_act = a.pair_expert ? a.n_pairs : *a.n_active;
   if (slot >= n_act) return;  // block-uniform; these blocks never count
-  if constexpr (PAIR_LDS) {
-    ffn_tile_pair<FMT, CPL, false, kDownNst, true, LPR>(a, slot, tile, s_out);
-    __syncthreads();
-    const int ub = tile * a.units_per_block;
-    const int ue = min(ub + a.units_per_block, a.rows_per_expert);
-    float* o = a.out + (int64_t)slot * a.rows_per_expert;
-    for (int r = ub + threadIdx.x; r < ue; r += kBlock) store_shared(o + r, s_out[r - ub]);
-  } else {
-    ffn_tile<FMT, CPL, false, LPR>(a, slot, tile);  // o rows stored with store_shared
-  }
+  ffn_tile<FMT, CPL, false, LPR>(a, slot, tile);  // o rows stored with store_shared
   wait_stores();
   __syncthreads();
   if (threadIdx.x == 0) s_last = arrive(&c.ctr->tile_done[tile]) == (unsigned)(n_act - 1);

@@ -1,5 +1,5 @@
 // Planar Q8_0 / Q4_K blocks: 16-byte chunk loads, scale decoding and the
-// fused dequantise-and-dot of one chunk against fp32 activations.
+// fused dequantise-and-dot of one chunk against 16-bit activations.
 //
 // Formats (include/moe_layer.h): Q8_0 blocks of 32 int8 with an fp16 scale
 // d, w = d*q; Q4_K super-blocks of 256 with fp16 d, dmin and per-32 6-bit
@@ -7,17 +7,13 @@
 // Flash Mixed-Quant GGUF" name these tensor types; their bit layouts are
 // this library's).
 //
-// Dot product.  A quant nibble or biased byte placed in the low bits of an
-// fp16 half is the subnormal q * 2^-24 exactly, so one AND turns two
-// weights into two fp16 operands, and v_fma_mix_f32 multiplies each by an
-// fp32 activation and accumulates in fp32.  The 2^24 goes into the scale.
-//  * Q4_K dword (8 nibbles, weights 2b / 2b+1 in the low / high nibble of
-//    byte b): mask 0x000F000F -> (w0, w4), 0x00F000F0 -> 16*(w1, w5), and
-//    the same after >> 8 -> (w2, w6), 16*(w3, w7).  Odd activations are held
-//    pre-scaled by 1/16 (exact).
-//  * Q8_0 dword: XOR 0x80808080 biases int8 to q+128 in 0..255; mask
-//    0x00FF00FF -> (b0, b2), after >> 8 -> (b1, b3).  sum((q+128) x) minus
-//    128 sum(x) recovers sum(q x).
+// Dot product.  The weights' integer quants go into v_dot4_i32_i8 as they
+// are: a Q8_0 quant dword is four int8 weights; a Q4_K dword (8 nibbles,
+// weights 2b / 2b+1 in the low / high nibble of byte b) gives the even
+// weights with one AND and the odd ones with a shift and an AND.  The
+// activations enter as 16-bit integers in two int8 limbs (XSlice below),
+// so each chunk's dot product is exact in int32 and the block scales are
+// applied once per chunk in fp32.
 #pragma once
 
 #include "common.h"
@@ -84,29 +80,96 @@ __device__ __forceinline__ void load_chunk(Chunk<kQ4_K>& ch, const QPlanes& p, u
   ch.h = bload16(p.s, so + 16u * (c >> 3));
 }
 
-// Activations of one chunk position for one token.
+// Activations of one chunk position for one token, as 16-bit integers.
+//
+// A lane quantises each of its chunk slices of activations when it loads
+// them: q_i = rint(x_i / s) with s = max|x| / 32639 over the slice (32
+// values for Q4_K, 16 for Q8_0), split q = 256 hi + lo with hi, lo in
+// int8, and packed in the byte order of the chunk's quant dwords.  Then
+// v_dot4_i32_i8 multiplies four weights by four limbs and accumulates
+// exactly in int32, and sum_i w_i x_i = (dot_hi * 256 + dot_lo) * s * scale.
+// The rounding to 16 bits relative to the slice maximum is the only
+// approximation (relative error at most 2^-16 of the slice maximum per
+// value).  The rounding uses the float trick: x / s + (1.5 * 2^23 + 128)
+// rounds x / s to the nearest integer in the low mantissa bits, whose
+// byte 1 is then hi and byte 0 xor 0x80 is lo.
 template <int FMT>
-struct XSlice {
-  float v[QTraits<FMT>::kWpc];
-  float sum;  // Q8_0: 128 * sum(x); Q4_K: sum(x)
+struct XSlice;
+template <>
+struct XSlice<kQ4_K> {
+  // h[2k] / l[2k]: limbs of weights 8k, 8k+2, 8k+4, 8k+6 (the low nibbles of
+  // quant dword k); h[2k+1] / l[2k+1]: weights 8k+1, 8k+3, 8k+5, 8k+7.
+  uint32_t h[8], l[8];
+  float s;    // the slice's scale
+  float sum;  // sum of the quantised activations, for the min term
 };
+template <>
+struct XSlice<kQ8_0> {
+  uint32_t h[4], l[4];  // dword k: limbs of weights 4k..4k+3 (byte order)
+  float s;
+  float sum;  // unused
+};
+
+constexpr float kQ16Max = 32639.0f;     // |q| bound: hi = (q + 128) >> 8 stays in int8
+constexpr float kQ16Magic = 12583040.0f;  // 1.5 * 2^23 + 128
+constexpr uint32_t kQ16MagicBits = 0x4B400080u;
+
+// Limbs of four rounded values (bits of x / s + kQ16Magic): hi = byte 1,
+// lo = byte 0 xor 0x80, packed in the order a, b, c, d.
+__device__ __forceinline__ void limbs4(float a, float b, float c, float d, uint32_t& hi,
+                                       uint32_t& lo) {
+  const uint32_t ab = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, b),
+                                            __builtin_bit_cast(uint32_t, a), 0x05010400u);
+  const uint32_t cd = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, d),
+                                            __builtin_bit_cast(uint32_t, c), 0x05010400u);
+  lo = __builtin_amdgcn_perm(cd, ab, 0x05040100u) ^ 0x80808080u;
+  hi = __builtin_amdgcn_perm(cd, ab, 0x07060302u);
+}
+
+// Quantise N values (N = 32 for Q4_K, 16 for Q8_0) in slice order.
+template <int FMT, int N>
+__device__ __forceinline__ void quantize_slice(XSlice<FMT>& xs, const float (&v)[N]) {
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < N; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const float inv = amax > 0.f ? kQ16Max * __builtin_amdgcn_rcpf(amax) : 0.f;
+  xs.s = amax > 0.f ? __builtin_amdgcn_rcpf(inv) : 0.f;
+  float y[N];
+  uint32_t bsum = 0;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    y[i] = fmaf(v[i], inv, kQ16Magic);
+    bsum += __builtin_bit_cast(uint32_t, y[i]);
+  }
+  if constexpr (FMT == kQ4_K) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float* g = y + 8 * k;
+      limbs4(g[0], g[2], g[4], g[6], xs.h[2 * k], xs.l[2 * k]);
+      limbs4(g[1], g[3], g[5], g[7], xs.h[2 * k + 1], xs.l[2 * k + 1]);
+    }
+    xs.sum = xs.s * (float)(int32_t)(bsum - (uint32_t)N * kQ16MagicBits);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) limbs4(y[4 * k], y[4 * k + 1], y[4 * k + 2], y[4 * k + 3], xs.h[k], xs.l[k]);
+    xs.sum = 0.f;
+  }
+}
 
 template <int FMT>
 __device__ __forceinline__ void load_x(XSlice<FMT>& xs, const float* row, int c) {
   constexpr int W = QTraits<FMT>::kWpc;
   const float* p = row + W * c;
-  float s = 0.f;
+  float v[W];
 #pragma unroll
   for (int i = 0; i < W / 4; ++i) {
     const float4 a = ldf4(p + 4 * i);
-    s += (a.x + a.y) + (a.z + a.w);
-    const float odd = (FMT == kQ4_K) ? 0.0625f : 1.0f;
-    xs.v[4 * i + 0] = a.x;
-    xs.v[4 * i + 1] = a.y * odd;
-    xs.v[4 * i + 2] = a.z;
-    xs.v[4 * i + 3] = a.w * odd;
+    v[4 * i + 0] = a.x;
+    v[4 * i + 1] = a.y;
+    v[4 * i + 2] = a.z;
+    v[4 * i + 3] = a.w;
   }
-  xs.sum = (FMT == kQ8_0) ? 128.f * s : s;
+  quantize_slice<FMT, W>(xs, v);
 }
 
 // load_x for activations another workgroup of this launch wrote with
@@ -118,84 +181,74 @@ __device__ __forceinline__ void load_x_shared(XSlice<FMT>& xs, const float* base
   constexpr int W = QTraits<FMT>::kWpc;
   const __amdgpu_buffer_rsrc_t r = make_rsrc(base, 0x7FFFFFF0u);
   const uint32_t off = 4u * (uint32_t)(row_off + W * c);
-  float s = 0.f;
+  float v[W];
 #pragma unroll
   for (int i = 0; i < W / 4; ++i) {
     const f32x4 a = bload16_shared(r, off + 16u * i);
-    s += (a.x + a.y) + (a.z + a.w);
-    const float odd = (FMT == kQ4_K) ? 0.0625f : 1.0f;
-    xs.v[4 * i + 0] = a.x;
-    xs.v[4 * i + 1] = a.y * odd;
-    xs.v[4 * i + 2] = a.z;
-    xs.v[4 * i + 3] = a.w * odd;
+    v[4 * i + 0] = a.x;
+    v[4 * i + 1] = a.y;
+    v[4 * i + 2] = a.z;
+    v[4 * i + 3] = a.w;
   }
-  xs.sum = (FMT == kQ8_0) ? 128.f * s : s;
+  quantize_slice<FMT, W>(xs, v);
 }
 
 template <int FMT>
 __device__ __forceinline__ void zero_x(XSlice<FMT>& xs) {
+  constexpr int D = FMT == kQ4_K ? 8 : 4;
 #pragma unroll
-  for (int i = 0; i < QTraits<FMT>::kWpc; ++i) xs.v[i] = 0.f;
+  for (int i = 0; i < D; ++i) xs.h[i] = xs.l[i] = 0u;
+  xs.s = 0.f;
   xs.sum = 0.f;
 }
 
-// acc += a * dot - b * xs.sum for one chunk: the chunk's contribution.
+// acc += a * dot - b * xs.sum for one chunk: the chunk's contribution,
+// with dot = sum_i q_i x16_i and a carrying the activation scale.
 struct ChunkScale {
   float a, b;
 };
 
 __device__ __forceinline__ ChunkScale decode_scale(const Chunk<kQ8_0>& ch, int /*sub*/) {
-  const float d = f16_to_f32(ch.d);
-  return {d * 16777216.0f, d};
+  return {f16_to_f32(ch.d), 0.f};
 }
 
+// Sub-block `sub` of a Q4_K header: a = d sc, b = dmin m.  The six-bit
+// fields are cut from the 96-bit stream (h.y, h.z, h.w) with 32-bit funnel
+// shifts; `sub` is fixed per lane, so the word choices are lane constants.
 __device__ __forceinline__ ChunkScale decode_scale(const Chunk<kQ4_K>& ch, int sub) {
-  const float d = f16_lo(ch.h.x);
-  const float dmin = f16_hi(ch.h.x);
-  const uint64_t lo = (uint64_t)ch.h.y | ((uint64_t)ch.h.z << 32);  // stream bits 0..63
-  const uint64_t hi = (uint64_t)ch.h.z | ((uint64_t)ch.h.w << 32);  // stream bits 32..95
-  const uint32_t sc = (uint32_t)(lo >> (6 * sub)) & 63u;
-  const uint32_t m = (uint32_t)(hi >> (16 + 6 * sub)) & 63u;
-  return {d * 16777216.0f * (float)sc, dmin * (float)m};
+  const uint4& h = ch.h;
+  const int bs = 6 * sub, bm = 16 + 6 * sub;  // sc at stream bit bs, m at stream bit 32 + bm
+  const uint32_t sc =
+      __builtin_amdgcn_alignbit(bs < 32 ? h.z : h.w, bs < 32 ? h.y : h.z, bs & 31) & 63u;
+  const uint32_t m = __builtin_amdgcn_alignbit(h.w, bm < 32 ? h.z : h.w, bm & 31) & 63u;
+  return {f16_lo(h.x) * (float)sc, f16_hi(h.x) * (float)m};
 }
 
-// sum_i q'_i * 2^-24 * x_i over the chunk.
+// sum_i q_i x16_i over the chunk (exact in int32; converted with at most one
+// rounding).
 __device__ __forceinline__ float chunk_dot(const Chunk<kQ8_0>& ch, const XSlice<kQ8_0>& xs) {
   const uint32_t w[4] = {ch.q.x, ch.q.y, ch.q.z, ch.q.w};
-  float s0 = 0.f, s1 = 0.f;
+  int ah = 0, al = 0;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const uint32_t u = w[k] ^ 0x80808080u;
-    const uint32_t m0 = u & 0x00FF00FFu;
-    const uint32_t m1 = (u >> 8) & 0x00FF00FFu;
-    s0 = fmaf(f16_lo(m0), xs.v[4 * k + 0], s0);
-    s1 = fmaf(f16_hi(m0), xs.v[4 * k + 2], s1);
-    s0 = fmaf(f16_lo(m1), xs.v[4 * k + 1], s0);
-    s1 = fmaf(f16_hi(m1), xs.v[4 * k + 3], s1);
+    ah = __builtin_amdgcn_sdot4((int)w[k], (int)xs.h[k], ah, false);
+    al = __builtin_amdgcn_sdot4((int)w[k], (int)xs.l[k], al, false);
   }
-  return s0 + s1;
+  return fmaf((float)ah, 256.0f, (float)al);
 }
 
 __device__ __forceinline__ float chunk_dot(const Chunk<kQ4_K>& ch, const XSlice<kQ4_K>& xs) {
   const uint32_t w[4] = {ch.q.x, ch.q.y, ch.q.z, ch.q.w};
-  float s0 = 0.f, s1 = 0.f;
+  int ah = 0, al = 0;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const uint32_t m0 = w[k] & 0x000F000Fu;
-    const uint32_t m1 = w[k] & 0x00F000F0u;
-    const uint32_t sh = w[k] >> 8;
-    const uint32_t m2 = sh & 0x000F000Fu;
-    const uint32_t m3 = sh & 0x00F000F0u;
-    s0 = fmaf(f16_lo(m0), xs.v[8 * k + 0], s0);
-    s1 = fmaf(f16_hi(m0), xs.v[8 * k + 4], s1);
-    s0 = fmaf(f16_lo(m1), xs.v[8 * k + 1], s0);
-    s1 = fmaf(f16_hi(m1), xs.v[8 * k + 5], s1);
-    s0 = fmaf(f16_lo(m2), xs.v[8 * k + 2], s0);
-    s1 = fmaf(f16_hi(m2), xs.v[8 * k + 6], s1);
-    s0 = fmaf(f16_lo(m3), xs.v[8 * k + 3], s0);
-    s1 = fmaf(f16_hi(m3), xs.v[8 * k + 7], s1);
+    const int e = (int)(w[k] & 0x0F0F0F0Fu), o = (int)((w[k] >> 4) & 0x0F0F0F0Fu);
+    ah = __builtin_amdgcn_sdot4(e, (int)xs.h[2 * k], ah, false);
+    ah = __builtin_amdgcn_sdot4(o, (int)xs.h[2 * k + 1], ah, false);
+    al = __builtin_amdgcn_sdot4(e, (int)xs.l[2 * k], al, false);
+    al = __builtin_amdgcn_sdot4(o, (int)xs.l[2 * k + 1], al, false);
   }
-  return s0 + s1;
+  return (float)(ah * 256 + al);  // |.| < 2^24: exact
 }
 
 }  // namespace svr
