@@ -63,23 +63,25 @@ __device__ __forceinline__ float wave_sum(float v) {
       float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, group_sum_last(v, kWave)), kWave - 1));
 }
 
-// Maximum / minimum of a u32 over the wave, returned to every lane.
+// Maximum / minimum of a u32 over the wave, returned to every lane.  Lanes
+// without a DPP source take the operation's identity (0 for max, ~0 for
+// min), which lets each step fold into one DPP-modified max / min.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  v = max(v, dpp_u<kDppShr1>(v, v));
-  v = max(v, dpp_u<kDppShr2>(v, v));
-  v = max(v, dpp_u<kDppShr4>(v, v));
-  v = max(v, dpp_u<kDppShr8>(v, v));
-  v = max(v, dpp_u<kDppBcast15, 0xA>(v, v));
-  v = max(v, dpp_u<kDppBcast31, 0xC>(v, v));
+  v = max(v, dpp_u<kDppShr1>(0u, v));
+  v = max(v, dpp_u<kDppShr2>(0u, v));
+  v = max(v, dpp_u<kDppShr4>(0u, v));
+  v = max(v, dpp_u<kDppShr8>(0u, v));
+  v = max(v, dpp_u<kDppBcast15, 0xA>(0u, v));
+  v = max(v, dpp_u<kDppBcast31, 0xC>(0u, v));
   return (uint32_t)__builtin_amdgcn_readlane((int)v, kWave - 1);
 }
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-  v = min(v, dpp_u<kDppShr1>(v, v));
-  v = min(v, dpp_u<kDppShr2>(v, v));
-  v = min(v, dpp_u<kDppShr4>(v, v));
-  v = min(v, dpp_u<kDppShr8>(v, v));
-  v = min(v, dpp_u<kDppBcast15, 0xA>(v, v));
-  v = min(v, dpp_u<kDppBcast31, 0xC>(v, v));
+  v = min(v, dpp_u<kDppShr1>(~0u, v));
+  v = min(v, dpp_u<kDppShr2>(~0u, v));
+  v = min(v, dpp_u<kDppShr4>(~0u, v));
+  v = min(v, dpp_u<kDppShr8>(~0u, v));
+  v = min(v, dpp_u<kDppBcast15, 0xA>(~0u, v));
+  v = min(v, dpp_u<kDppBcast31, 0xC>(~0u, v));
   return (uint32_t)__builtin_amdgcn_readlane((int)v, kWave - 1);
 }
 

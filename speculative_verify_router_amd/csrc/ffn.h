@@ -64,10 +64,17 @@ constexpr int tp_for(int fmt, int cpl) {
   return (cpl * (fmt == kQ8_0 ? 16 : 32) <= 16) ? 4 : (cpl * (fmt == kQ8_0 ? 16 : 32) <= 32) ? 2 : 1;
 }
 
-// Ring depth: three stages while the in-flight chunks of the ring stay
-// within about 100 VGPRs, else two.
+// Ring depth: as many stages (2 to 5) as fit in about kRingVgprs VGPRs of
+// in-flight chunks.
+#ifndef SVR_RING_VGPRS
+#define SVR_RING_VGPRS 100
+#endif
+constexpr int kRingVgprs = SVR_RING_VGPRS;
 constexpr int nst_for(int fmt, int cpl, bool gateup) {
-  return (cpl * (gateup ? 2 : 1) * (fmt == kQ8_0 ? 5 : 8) * 3 <= 100) ? 3 : 2;
+  return (cpl * (gateup ? 2 : 1) * (fmt == kQ8_0 ? 5 : 8) * 5 <= kRingVgprs)   ? 5
+         : (cpl * (gateup ? 2 : 1) * (fmt == kQ8_0 ? 5 : 8) * 4 <= kRingVgprs) ? 4
+         : (cpl * (gateup ? 2 : 1) * (fmt == kQ8_0 ? 5 : 8) * 3 <= kRingVgprs) ? 3
+                                                                                : 2;
 }
 
 template <int FMT, int CPL, bool GATEUP>

@@ -136,7 +136,10 @@ struct CombineArgs {
 // Phase 3: routed down tiles, then the combine of each finished row tile.
 // Ring depth of the routed down rows: a one-matrix row of a few hundred
 // bytes per lane group needs several steps in flight to cover the latency.
-constexpr int kDownNst = 4;
+#ifndef SVR_DOWN_NST
+#define SVR_DOWN_NST 4
+#endif
+constexpr int kDownNst = SVR_DOWN_NST;
 
 // Phase 3 for pair slots (up to four tokens): one workgroup of eight waves
 // per (token, row tile).  In each pass of eight slots, wave w streams the

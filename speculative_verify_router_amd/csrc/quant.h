@@ -213,15 +213,37 @@ __device__ __forceinline__ ChunkScale decode_scale(const Chunk<kQ8_0>& ch, int /
 }
 
 // Sub-block `sub` of a Q4_K header: a = d sc, b = dmin m.  The six-bit
-// fields are cut from the 96-bit stream (h.y, h.z, h.w) with 32-bit funnel
-// shifts; `sub` is fixed per lane, so the word choices are lane constants.
-__device__ __forceinline__ ChunkScale decode_scale(const Chunk<kQ4_K>& ch, int sub) {
+// field at stream bit f (sc: f = 6 sub, m: f = 48 + 6 sub) lies in stream
+// bytes f/8 and f/8 + 1; a byte permute with a lane-constant selector
+// gathers those two bytes (sc from words y, z; m from z, w) and a
+// bit-field extract takes the six bits.  `sub` is fixed per lane, so the
+// selectors and offsets are computed once.
+struct Q4kSel {
+  uint32_t ssel, msel;  // v_perm selectors: the two bytes into bits 0..15
+  uint32_t soff, moff;  // bit offsets of the fields in them
+};
+__device__ __forceinline__ Q4kSel q4k_sel(int sub) {
+  // v_perm byte numbering: 0..3 = second operand (lower word), 4..7 = first.
+  const int sb = (6 * sub) >> 3;            // stream byte of sc, in (y, z) = bytes 0..7
+  const int mb = ((48 + 6 * sub) >> 3) - 4;  // stream byte of m, in (z, w) = bytes 0..7
+  Q4kSel q;
+  q.ssel = (uint32_t)sb | ((uint32_t)(sb + 1) << 8) | 0x0C0C0000u;  // 0x0C: zero byte
+  // The last m field (stream bits 90..95) sits wholly in byte mb = 7.
+  q.msel = (uint32_t)mb | ((uint32_t)(mb < 7 ? mb + 1 : 7) << 8) | 0x0C0C0000u;
+  q.soff = (uint32_t)((6 * sub) & 7);
+  q.moff = (uint32_t)((48 + 6 * sub) & 7);
+  return q;
+}
+__device__ __forceinline__ ChunkScale decode_scale(const Chunk<kQ4_K>& ch, const Q4kSel& q) {
   const uint4& h = ch.h;
-  const int bs = 6 * sub, bm = 16 + 6 * sub;  // sc at stream bit bs, m at stream bit 32 + bm
-  const uint32_t sc =
-      __builtin_amdgcn_alignbit(bs < 32 ? h.z : h.w, bs < 32 ? h.y : h.z, bs & 31) & 63u;
-  const uint32_t m = __builtin_amdgcn_alignbit(h.w, bm < 32 ? h.z : h.w, bm & 31) & 63u;
-  return {f16_lo(h.x) * (float)sc, f16_hi(h.x) * (float)m};
+  const uint32_t sc = __builtin_amdgcn_ubfe(__builtin_amdgcn_perm(h.z, h.y, q.ssel), q.soff, 6);
+  const uint32_t m = __builtin_amdgcn_ubfe(__builtin_amdgcn_perm(h.w, h.z, q.msel), q.moff, 6);
+  // fma with a zero addend rather than a product, so that each fp16 field
+  // enters a mixed-precision FMA without a separate conversion.
+  return {fmaf(f16_lo(h.x), (float)sc, 0.0f), fmaf(f16_hi(h.x), (float)m, 0.0f)};
+}
+__device__ __forceinline__ ChunkScale decode_scale(const Chunk<kQ4_K>& ch, int sub) {
+  return decode_scale(ch, q4k_sel(sub));
 }
 
 // sum_i q_i x16_i over the chunk (exact in int32; converted with at most one

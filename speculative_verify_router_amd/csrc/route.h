@@ -201,11 +201,16 @@ __device__ __forceinline__ void topk_token_nv(const float* __restrict__ row,
   }
 }
 
-// NV keys per lane: 8 for up to 512 experts, 16 for up to 1024.
+// NV keys per lane, the fewest that hold E: 5 for up to 320 experts (the
+// Step-3.5-Flash shape, 288), 6 for up to 384 (Step-5, 352), then 8 and 16.
 template <bool COHERENT>
 __device__ __forceinline__ void topk_token(const float* __restrict__ row, int32_t* __restrict__ ids,
                                            float* __restrict__ wts, int E, int k) {
-  if (E <= 8 * kWave)
+  if (E <= 5 * kWave)
+    topk_token_nv<COHERENT, 5>(row, ids, wts, E, k);
+  else if (E <= 6 * kWave)
+    topk_token_nv<COHERENT, 6>(row, ids, wts, E, k);
+  else if (E <= 8 * kWave)
     topk_token_nv<COHERENT, 8>(row, ids, wts, E, k);
   else
     topk_token_nv<COHERENT, kMaxExperts / kWave>(row, ids, wts, E, k);
