@@ -18,13 +18,24 @@
 namespace svr {
 
 constexpr int kMaxTiles = 1008;  // combine counters available in the workspace
+// Router workgroups arrive in groups (workgroup index mod kRouterGroups),
+// each group on its own 256-byte line; the last of a group arrives on
+// router_done.  One counter bumped by every router workgroup serialises
+// hundreds of atomics on one address.
+constexpr int kRouterGroups = 16;
+
+struct alignas(256) CounterLine {
+  unsigned v;
+  unsigned pad[63];
+};
 
 struct Counters {
   unsigned router_done;
   unsigned pad[15];
   unsigned tile_done[kMaxTiles];
+  CounterLine router_group[kRouterGroups];
 };
-static_assert(sizeof(Counters) == 4096, "counter page");
+static_assert(sizeof(Counters) == 8192 && sizeof(Counters) <= kCounterBytes, "counter pages");
 
 struct RouteArgs {
   const float* router;
@@ -46,7 +57,19 @@ __device__ __forceinline__ void router_part(const RouteArgs& r, int blk) {
   router_row_block<NC>(r.router, r.x, r.logits, r.H, r.E, r.M, blk);
   wait_stores();
   __syncthreads();
-  if (threadIdx.x == 0) s_last = arrive(&r.ctr->router_done) == (unsigned)(r.n_router_blocks - 1);
+  if (threadIdx.x == 0) {
+    const int g = blk % kRouterGroups;
+    const int n_g = (r.n_router_blocks - g + kRouterGroups - 1) / kRouterGroups;
+    int last = 0;
+    if (arrive(&r.ctr->router_group[g].v) == (unsigned)(n_g - 1)) {
+      // Every workgroup of group g has arrived: reset its line for the next
+      // call, then arrive as the group on router_done.
+      __hip_atomic_store(&r.ctr->router_group[g].v, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int n_groups = min(kRouterGroups, r.n_router_blocks);
+      last = arrive(&r.ctr->router_done) == (unsigned)(n_groups - 1);
+    }
+    s_last = last;
+  }
   __syncthreads();
   if (!s_last) return;
   // Logits of the other workgroups are read with load_shared (coherent).
