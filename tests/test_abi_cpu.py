@@ -164,9 +164,11 @@ def test_forward_error_paths():
 def test_forward_timed_checks_the_event_count():
     L = svr.lib()
     d, w = _desc().c(), _fake_weights()
-    evs = (ctypes.c_void_p * 3)(1, 2, 3)
+    # One event more than the stage count + 1: rejected before anything runs.
+    n = svr.moe_stage_count(_desc(), 4) + 2
+    evs = (ctypes.c_void_p * n)(*range(1, n + 1))
     st = L.moe_layer_forward_timed(ctypes.byref(d), ctypes.byref(w), FAKE, 4, FAKE, None, None,
-                                   FAKE, 1 << 40, None, evs, 3)
+                                   FAKE, 1 << 40, None, evs, n)
     assert st == B.ERR_ARG
     st = L.moe_layer_forward_timed(ctypes.byref(d), ctypes.byref(w), FAKE, 4, FAKE, None, None,
                                    FAKE, 1 << 40, None, None, 0)
