@@ -49,3 +49,32 @@ def test_full_config(name):
     assert int(r["n_active"][0]) == len(ref["active"])
     del w, inp
     gc.collect()
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["step35_verify_m4", "step5_verify_m4"])
+def test_verify_batches_of_one_to_four_tokens_agree_bitwise(name):
+    # The MTP verify batch is the last accepted token plus up to three drafts,
+    # and the draft count changes from round to round ("Support Step3.5/3.7
+    # flash mtp3", data-flow trace: the drafting batch grows by one token per
+    # head, and adaptive draft lengths shorten it).  Every token's routing
+    # and output must not depend on how many drafts share its batch: the
+    # rows of a 4-token call equal, bit for bit, the same tokens' rows of
+    # 1-, 2- and 3-token calls (and the M=4 result is checked against the
+    # oracle in test_full_config).
+    cfg = synth.CONFIGS[name]
+    log(f"[{name}] drawing layer")
+    inp = synth.draw_layer(cfg)
+    x, _ = conditioned_tokens(inp)
+    w = upload(inp)
+    y4, ids4, tw4 = gpu_forward(cfg, w, x)
+    for M in (1, 2, 3):
+        for t0 in range(0, 4 - M + 1):
+            sub = cfg.replace(n_tokens=M)
+            y, ids, tw = gpu_forward(sub, w, x[t0:t0 + M])
+            log(f"[{name}] M={M} rows {t0}..{t0 + M - 1}")
+            assert np.array_equal(ids, ids4[t0:t0 + M])
+            assert np.array_equal(tw.view(np.uint32), tw4[t0:t0 + M].view(np.uint32))
+            assert np.array_equal(y.view(np.uint32), y4[t0:t0 + M].view(np.uint32))
+    del w, inp
+    gc.collect()
