@@ -12,7 +12,8 @@
  * token ("Step-5 Preview GGUF", Model background, configuration table).
  * Routers are F32, shared experts Q8_0 and routed experts Q4_K in the mixed
  * recipes ("Step-5 Preview GGUF", Precision distribution table; "Step 3.7
- * Flash Mixed-Quant GGUF", Tensor recipe).
+ * Flash Mixed-Quant GGUF", Tensor recipe); the 2-bit Step-5 recipes store
+ * routed matrices in Q2_K ("Step-5 Preview GGUF", Tensor-type table).
  *
  * What one call computes, for each token t of x [M][H]:
  *   l[e]    = sum_h router[e][h] * x[t][h]                      (F32 router)
@@ -46,6 +47,18 @@
  *            16*rows*ns + 128*(r*ns + b); sub-block s in bytes [16s, 16s+16)
  *            of them; weight i of a sub-block in byte i/2, low nibble for
  *            even i, high nibble for odd i.  Total 144*rows*ns bytes.
+ *   MOE_Q2_K rows x cols, cols % 256 == 0, ns = cols / 256, routed experts
+ *            only.  Super-blocks of 256 weights: fp16 d and dmin, 16
+ *            sub-blocks of 16 weights with a 4-bit scale sc and a 4-bit min
+ *            m, 2-bit quants q, w = d*sc_s*q - dmin*m_s.
+ *            Bytes [0, 4*rows*ns): fp16 d then fp16 dmin of super-block
+ *            (r, b) at 4*(r*ns + b).
+ *            Bytes from S = round_up(4*rows*ns, 256): 16 scale bytes of
+ *            super-block (r, b) at S + 16*(r*ns + b), byte s = sc_s | m_s << 4.
+ *            Bytes from Q = round_up(S + 16*rows*ns, 256): 64 quant bytes of
+ *            super-block (r, b) at Q + 64*(r*ns + b); sub-block s in bytes
+ *            [4s, 4s+4) of them; weight i of a sub-block in byte i % 4, bits
+ *            [2*(i/4), 2*(i/4)+2).  Total Q + 64*rows*ns bytes.
  *   Expert tensors are stacked experts-outermost and stored as one tensor:
  *   gate and up are (E*F) x H, down is (E*H) x F; expert e owns rows
  *   [e*F, (e+1)*F) (resp. [e*H, (e+1)*H)).  The shared expert's gate and up
@@ -65,9 +78,10 @@
  *   it returns MOE_OK, except MOE_ERR_LAUNCH, which reports a failure seen
  *   after enqueueing (hipGetLastError).  Shapes are checked before launch:
  *   1 <= n_experts <= 1024; 1 <= top_k <= min(n_experts, 64); hidden,
- *   ffn and shared_ffn multiples of 32 (Q8_0) or 256 (Q4_K) for the tensors
- *   that use them, and a row of at most 512 blocks of 16 bytes (Q8_0:
- *   8192 columns, Q4_K: 16384 columns); n_tokens >= 0 (0 enqueues nothing).
+ *   ffn and shared_ffn multiples of 32 (Q8_0) or 256 (Q4_K, Q2_K) for the
+ *   tensors that use them, and a row of at most 512 blocks of 16 bytes
+ *   (Q8_0: 8192 columns, Q4_K: 16384, Q2_K: 32768); n_tokens >= 0 (0
+ *   enqueues nothing).  MOE_Q2_K as shared_type is MOE_ERR_DTYPE.
  */
 #ifndef SVR_MOE_LAYER_H
 #define SVR_MOE_LAYER_H
@@ -83,6 +97,7 @@ extern "C" {
 #define MOE_F32 0
 #define MOE_Q8_0 1
 #define MOE_Q4_K 2
+#define MOE_Q2_K 3
 
 /* Status codes. */
 #define MOE_OK 0
@@ -100,7 +115,7 @@ typedef struct moe_layer_desc {
   int32_t top_k;       /* k */
   int32_t ffn;         /* F, routed expert FFN width */
   int32_t shared_ffn;  /* Fs, shared expert FFN width; 0 = no shared expert */
-  int32_t expert_type; /* MOE_Q8_0 or MOE_Q4_K: routed gate/up/down */
+  int32_t expert_type; /* MOE_Q8_0, MOE_Q4_K or MOE_Q2_K: routed gate/up/down */
   int32_t shared_type; /* MOE_Q8_0 or MOE_Q4_K: shared gate/up/down */
   int32_t flags;       /* 0 or MOE_SINGLE_LAUNCH; other bits: MOE_ERR_ARG */
 } moe_layer_desc;
@@ -140,7 +155,7 @@ int32_t moe_tensor_bytes(int32_t dtype, int64_t rows, int64_t cols, int64_t* byt
  * zero again, so zero-fill a workspace once when it is allocated.  Calls that
  * share a workspace must not overlap in time.  One exception: in the
  * single-launch path every device-side wait is bounded, and if one ever gave
- * up, the 32-bit word at byte offset 20 of the page becomes nonzero and stays
+ * up, the 32-bit word at byte offset 1280 of the page becomes nonzero and stays
  * so (that call's outputs are then undefined); it is zero in normal use. */
 int32_t moe_workspace_bytes(const moe_layer_desc* desc, int32_t max_tokens, size_t* bytes);
 
@@ -175,7 +190,9 @@ int32_t moe_route(const moe_layer_desc* desc, const float* router, const float* 
  * the expert FFNs as grouped GEMMs on the bf16 matrix cores with exact
  * integer quants, fp32 scales and activations split into two bf16 terms,
  * in five stages ("route", "shared_gateup", "gateup", "shared_down",
- * "down_combine"; the shared stages are empty without a shared expert).
+ * "down_combine"; the shared stages are empty without a shared expert);
+ * with Q2_K routed experts they run the three stages of the small batches
+ * instead (no matrix-core path for that type).
  * moe_stage_count / moe_stage_name say which. */
 int32_t moe_layer_forward(const moe_layer_desc* desc, const moe_layer_weights* weights,
                           const float* x, int32_t n_tokens, float* y,

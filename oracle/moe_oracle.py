@@ -14,7 +14,9 @@ blocks exactly, then dense products.  What the layer computes:
   Precision distribution table, routers row; "Step 3.7 Flash Mixed-Quant
   GGUF", Tensor recipe, router row), a Q8_0 shared expert beside the routed
   ones (same tables, shared-expert rows) and routed experts in Q4_K ("Step
-  3.7 Flash Mixed-Quant GGUF", Tensor recipe, routed rows).
+  3.7 Flash Mixed-Quant GGUF", Tensor recipe, routed rows), or in Q2_K as
+  the 2-bit recipes of "Step-5 Preview GGUF" store them (Tensor-type table,
+  routed gate/up and down rows).
 * It is run on the verify batch of MTP speculative decoding: the last
   accepted token plus up to three drafts, all with logits ("Support
   Step3.5/3.7 flash mtp3", Overview, data-flow trace, target batch step).
@@ -28,8 +30,11 @@ block layouts.  Readings taken here:
 * expert FFN: SwiGLU, h = silu(Wg x) * (Wu x), o = Wd h, silu(g) = g/(1+e^-g);
 * shared expert: the same FFN, ungated, added with weight one;
 * output y_t = s_t + sum_j w_tj o_tj, summed in slot order j = 0..k-1;
-* block layouts: the planar Q8_0 / Q4_K layouts documented in
-  include/moe_layer.h.
+* block layouts: the planar Q8_0 / Q4_K / Q2_K layouts documented in
+  include/moe_layer.h; Q2_K is read as the K-quant family's 2-bit member:
+  256-weight super-blocks with fp16 d and dmin, sixteen 16-weight
+  sub-blocks with a 4-bit scale and a 4-bit min, 2-bit quants,
+  w = d*sc*q - dmin*m.
 """
 
 from __future__ import annotations
@@ -135,11 +140,64 @@ def dequant_q4_k(buf, rows: int, cols: int, row_start: int = 0, row_count=None) 
     return w.reshape(n, cols)
 
 
+def q2_k_offsets(rows: int, cols: int):
+    """Plane starts of planar Q2_K: (scale plane, quant plane).
+
+    The d/dmin plane (4 bytes per super-block) starts at 0; each later plane
+    starts at the previous plane's end rounded up to 256 bytes.
+    """
+    ns = cols // 256
+    so = (4 * rows * ns + 255) // 256 * 256
+    qo = (so + 16 * rows * ns + 255) // 256 * 256
+    return so, qo
+
+
+def q2_k_fields(buf, rows: int, cols: int, row_start: int = 0, row_count=None):
+    """Decode Q2_K records into (d, dmin, sc[16], m[16], q[16][16]) per record.
+
+    Scale byte s of a record: sc_s in the low nibble, m_s in the high one.
+    Sub-block s owns quant bytes [4s, 4s+4) of the record's 64; weight i of
+    it is the 2-bit field at bits 2*(i // 4) of byte i % 4.
+    """
+    if cols % 256:
+        raise ValueError("Q2_K needs cols % 256 == 0")
+    r0, n = _rows(rows, row_start, row_count)
+    buf = np.asarray(buf, dtype=np.uint8)
+    ns = cols // 256
+    a, b = r0 * ns, (r0 + n) * ns
+    so, qo = q2_k_offsets(rows, cols)
+    dd = buf[4 * a: 4 * b].reshape(b - a, 4).astype(np.int64)
+    d = f16_to_f64(dd[:, 0] | (dd[:, 1] << 8))
+    dmin = f16_to_f64(dd[:, 2] | (dd[:, 3] << 8))
+    sb = buf[so + 16 * a: so + 16 * b].reshape(b - a, 16).astype(np.int64)
+    sc = sb & 15
+    m = sb >> 4
+    qb = buf[qo + 64 * a: qo + 64 * b].reshape(b - a, 16, 4).astype(np.int64)
+    q = np.empty((b - a, 16, 16), dtype=np.int64)
+    for i in range(16):
+        q[:, :, i] = (qb[:, :, i % 4] >> (2 * (i // 4))) & 3
+    return d, dmin, sc, m, q
+
+
+def dequant_q2_k(buf, rows: int, cols: int, row_start: int = 0, row_count=None) -> np.ndarray:
+    """Planar Q2_K -> float64 [row_count][cols].
+
+    256-weight super-block, 16 sub-blocks of 16: w = d*sc_s*q - dmin*m_s.
+    """
+    r0, n = _rows(rows, row_start, row_count)
+    d, dmin, sc, m, q = q2_k_fields(buf, rows, cols, r0, n)
+    w = (d[:, None, None] * sc[:, :, None].astype(np.float64) * q
+         - dmin[:, None, None] * m[:, :, None].astype(np.float64))
+    return w.reshape(n, cols)
+
+
 def dequant(dtype: str, buf, rows: int, cols: int, row_start: int = 0, row_count=None) -> np.ndarray:
     if dtype == "q8_0":
         return dequant_q8_0(buf, rows, cols, row_start, row_count)
     if dtype == "q4_k":
         return dequant_q4_k(buf, rows, cols, row_start, row_count)
+    if dtype == "q2_k":
+        return dequant_q2_k(buf, rows, cols, row_start, row_count)
     if dtype == "f32":
         r0, n = _rows(rows, row_start, row_count)
         a = np.asarray(buf).view(np.float32).reshape(rows, cols)

@@ -4,7 +4,9 @@ A second, deliberately naive CPU implementation of the same layer used to pin
 the vectorised oracle on tiny shapes.  It shares no code with
 ``moe_oracle.py``: fp16 is decoded with Python's ``struct`` half-precision
 codec, the Q4_K scale/min fields are cut from one Python integer holding the
-96-bit stream, and every product is an explicit loop over Python floats.
+96-bit stream, a Q2_K quant is cut from the little-endian integer of its
+sub-block's four bytes (weight i at bit 8 (i % 4) + 2 (i // 4)), and every
+product is an explicit loop over Python floats.
 Meant for hidden sizes of a few hundred and a handful of experts.
 """
 
@@ -46,8 +48,26 @@ def weight_q4_k(buf, rows: int, cols: int, r: int, c: int) -> float:
     return d * sc * q - dmin * mn
 
 
+def weight_q2_k(buf, rows: int, cols: int, r: int, c: int) -> float:
+    ns = cols // 256
+    rec = r * ns + c // 256
+    s, i = (c % 256) // 16, c % 16
+    d = _f16(int(buf[4 * rec]), int(buf[4 * rec + 1]))
+    dmin = _f16(int(buf[4 * rec + 2]), int(buf[4 * rec + 3]))
+    sbase = -(-4 * rows * ns // 256) * 256
+    qbase = -(-(sbase + 16 * rows * ns) // 256) * 256
+    sbyte = int(buf[sbase + 16 * rec + s])
+    word = int.from_bytes(bytes(int(v) for v in buf[qbase + 64 * rec + 4 * s: qbase + 64 * rec + 4 * s + 4]),
+                          "little")
+    q = (word >> (8 * (i % 4) + 2 * (i // 4))) & 3
+    return d * (sbyte % 16) * q - dmin * (sbyte // 16)
+
+
+_WEIGHT = {"q8_0": weight_q8_0, "q4_k": weight_q4_k, "q2_k": weight_q2_k}
+
+
 def weight(dtype: str, buf, rows: int, cols: int, r: int, c: int) -> float:
-    return (weight_q8_0 if dtype == "q8_0" else weight_q4_k)(buf, rows, cols, r, c)
+    return _WEIGHT[dtype](buf, rows, cols, r, c)
 
 
 def _matvec(dtype, buf, rows, cols, row0, nrows, v):

@@ -14,6 +14,9 @@ from .layers import (  # noqa: F401
     LayerInputs,
     draw_layer,
     draw_tokens,
+    q2_k_bytes,
+    q2_k_quant_offset,
+    q2_k_scale_offset,
     q4_k_bytes,
     q4_k_header_bytes,
     q8_0_bytes,

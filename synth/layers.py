@@ -22,6 +22,14 @@ Byte layouts (planar block quantisation) are those documented in
   sub-block s of a record occupies bytes [16s, 16s+16) and weight i of the
   sub-block sits in byte i // 2, low nibble for even i.
   W = d * sc_s * q - dmin * m_s.
+* Q2_K, R rows x K columns, K % 256 == 0, ns = K / 256: a plane of R*ns
+  4-byte records (fp16 d, fp16 dmin) at byte 0; at ``q2_k_scale_offset``
+  (that plane's size rounded up to 256 bytes) a plane of R*ns 16-byte scale
+  records, byte s holding the scale of sub-block s in its low nibble and the
+  min in its high nibble; at ``q2_k_quant_offset`` (scale plane end rounded
+  up to 256) R*ns 64-byte quant records, sub-block s (16 weights) in bytes
+  [4s, 4s+4) and weight i of it in byte i % 4, bits [2 (i // 4), 2 (i // 4) + 2).
+  W = d * sc_s * q - dmin * m_s.
 
 Nothing here routes, dequantises or multiplies: those steps belong to the
 oracle and to the HIP library.
@@ -58,7 +66,7 @@ class LayerConfig:
     top_k: int
     ffn: int
     shared_ffn: int
-    expert_type: str  # "q8_0" | "q4_k"
+    expert_type: str  # "q8_0" | "q4_k" | "q2_k"
     shared_type: str  # "q8_0" | "q4_k" (ignored when shared_ffn == 0)
     n_tokens: int
     router_std: float
@@ -90,6 +98,10 @@ CONFIGS = {
     # Step-5-shaped prefill micro-batch of 512 tokens.
     "step5_prefill_m512": LayerConfig(
         "step5_prefill_m512", 4096, 352, 8, 1536, 1536, "q4_k", "q8_0", 512, 0.02, 0.02, "iid", 5),
+    # The Step-5 verify batch with 2-bit routed experts (the Q2_K routed
+    # matrices of the "Step-5 Preview GGUF" Q2 recipes, Tensor-type table).
+    "step5_q2k_verify_m4": LayerConfig(
+        "step5_q2k_verify_m4", 4096, 352, 8, 1536, 1536, "q2_k", "q8_0", 4, 0.02, 0.02, "disjoint", 6),
 }
 
 
@@ -115,6 +127,20 @@ def q4_k_bytes(rows: int, cols: int) -> int:
     return 144 * rows * (cols // 256)
 
 
+def q2_k_scale_offset(rows: int, cols: int) -> int:
+    """Byte offset of the scale plane in a planar Q2_K tensor."""
+    return (4 * rows * (cols // 256) + 255) // 256 * 256
+
+
+def q2_k_quant_offset(rows: int, cols: int) -> int:
+    """Byte offset of the 2-bit quant plane in a planar Q2_K tensor."""
+    return (q2_k_scale_offset(rows, cols) + 16 * rows * (cols // 256) + 255) // 256 * 256
+
+
+def q2_k_bytes(rows: int, cols: int) -> int:
+    return q2_k_quant_offset(rows, cols) + 64 * rows * (cols // 256)
+
+
 def tensor_bytes(dtype: str, rows: int, cols: int) -> int:
     if dtype == "q8_0":
         if cols % 32:
@@ -124,6 +150,10 @@ def tensor_bytes(dtype: str, rows: int, cols: int) -> int:
         if cols % 256:
             raise ValueError("Q4_K needs cols % 256 == 0")
         return q4_k_bytes(rows, cols)
+    if dtype == "q2_k":
+        if cols % 256:
+            raise ValueError("Q2_K needs cols % 256 == 0")
+        return q2_k_bytes(rows, cols)
     if dtype == "f32":
         return 4 * rows * cols
     raise ValueError(f"unknown dtype {dtype!r}")
@@ -196,6 +226,36 @@ def _fill_q4_k(buf: np.ndarray, rows_total: int, cols: int, row0: int, hdr, qs):
     buf[hb + 128 * s0: hb + 128 * (s0 + n)] = qs.reshape(-1)
 
 
+def _draw_q2_k_rows(rng: np.random.Generator, rows: int, cols: int):
+    """Uniform-random Q2_K fields for ``rows`` rows.
+
+    d ~ U[2^-10, 2^-8), dmin ~ U[2^-10, 2^-8), both rounded to fp16 (weights
+    of a few hundredths, as the Q4_K draw gives); the scale bytes and the
+    quant bytes are uniform random bytes, so every 4-bit scale and min is
+    uniform on 0..15 and every 2-bit quant on 0..3.
+    """
+    n = rows * (cols // 256)
+    dd = np.empty((n, 4), dtype=np.uint8)
+    d = rng.uniform(2.0 ** -10, 2.0 ** -8, n).astype(np.float16)
+    dmin = rng.uniform(2.0 ** -10, 2.0 ** -8, n).astype(np.float16)
+    dd[:, 0:2] = d.view(np.uint16).reshape(n, 1).view(np.uint8)
+    dd[:, 2:4] = dmin.view(np.uint16).reshape(n, 1).view(np.uint8)
+    sc = rng.integers(0, 256, (n, 16), dtype=np.uint8)
+    qs = rng.integers(0, 256, (n, 64), dtype=np.uint8)
+    return dd, sc, qs
+
+
+def _fill_q2_k(buf: np.ndarray, rows_total: int, cols: int, row0: int, dd, sc, qs):
+    ns = cols // 256
+    so = q2_k_scale_offset(rows_total, cols)
+    qo = q2_k_quant_offset(rows_total, cols)
+    n = dd.shape[0]
+    s0 = row0 * ns
+    buf[4 * s0: 4 * (s0 + n)] = dd.reshape(-1)
+    buf[so + 16 * s0: so + 16 * (s0 + n)] = sc.reshape(-1)
+    buf[qo + 64 * s0: qo + 64 * (s0 + n)] = qs.reshape(-1)
+
+
 def _rng(cfg: LayerConfig, instance: int, *key: int) -> np.random.Generator:
     ss = np.random.SeedSequence([cfg.seed, instance, *key])
     return np.random.Generator(np.random.PCG64(ss))
@@ -227,9 +287,14 @@ def _stacked(cfg: LayerConfig, instance: int, tid: int, rows: int, cols: int,
         if dtype == "q8_0":
             d_bits, q = _draw_q8_0_rows(rng, rows, cols, cfg.weight_std)
             _fill_q8_0(buf, total_rows, cols, e * rows, d_bits, q)
-        else:
+        elif dtype == "q4_k":
             hdr, qs = _draw_q4_k_rows(rng, rows, cols)
             _fill_q4_k(buf, total_rows, cols, e * rows, hdr, qs)
+        elif dtype == "q2_k":
+            dd, sc, qs = _draw_q2_k_rows(rng, rows, cols)
+            _fill_q2_k(buf, total_rows, cols, e * rows, dd, sc, qs)
+        else:
+            raise ValueError(f"unknown dtype {dtype!r}")
 
     if pool is None or n_exp == 1:
         for e in range(n_exp):

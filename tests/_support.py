@@ -95,10 +95,12 @@ def conditioned_tokens(inp, instance: int = 0, n_tokens=None, margin: float = 1e
 # --------------------------------------------------------------------------
 
 def scale_fields(dtype: str, buf: np.ndarray, rows: int, cols: int) -> np.ndarray:
-    """uint16 view of every fp16 scale field (Q8_0 d; Q4_K d and dmin)."""
+    """uint16 view of every fp16 scale field (Q8_0 d; Q4_K and Q2_K d and dmin)."""
     if dtype == "q8_0":
         return buf[: 2 * rows * (cols // 32)].view(np.uint16)
     n = rows * (cols // 256)
+    if dtype == "q2_k":
+        return buf[: 4 * n].view(np.uint16).reshape(n, 2)
     return buf[: 16 * n].view(np.uint16).reshape(n, 8)[:, 0:2]
 
 
@@ -128,6 +130,12 @@ def copy_expert_rows(dtype: str, buf: np.ndarray, rows_per_expert: int, cols: in
         qo = synth.q8_0_quant_offset(R, cols)
         qp = out[qo: qo + R * cols].reshape(n_experts, rows_per_expert * cols)
         qp[:] = qp[src]
+    elif dtype == "q2_k":
+        ns = cols // 256
+        so, qo = synth.q2_k_scale_offset(R, cols), synth.q2_k_quant_offset(R, cols)
+        for start, width in ((0, 4), (so, 16), (qo, 64)):
+            pl = out[start: start + R * ns * width].reshape(n_experts, rows_per_expert * ns * width)
+            pl[:] = pl[src]
     else:
         ns = cols // 256
         hb = synth.q4_k_header_bytes(R, cols)

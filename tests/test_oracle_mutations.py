@@ -18,13 +18,16 @@ _orig = {name: getattr(om, name) for name in dir(om) if callable(getattr(om, nam
 
 def _pins():
     yield P.test_f16_decode_all_bit_patterns_match_numpy
-    for fx, dt in [("q8_0_planar.txt", "q8_0"), ("q4_k_planar.txt", "q4_k")]:
+    for fx, dt in P.FIXTURES:
         yield lambda fx=fx, dt=dt: P.test_dequant_matches_hand_derived_fixture(fx, dt)
     yield P.test_dequant_fixture_twin_agrees
     yield P.test_q8_0_requantise_roundtrip_is_byte_exact
     for s in (0, 3, 7):
         yield lambda s=s: P.test_q4_k_single_field_positions(s)
     yield P.test_q4_k_multi_row_record_order
+    for s in (0, 5, 15):
+        yield lambda s=s: P.test_q2_k_single_field_positions(s)
+    yield P.test_q2_k_multi_row_record_order
     yield P.test_router_logits_unit_vectors_pick_columns
     yield P.test_select_ties_go_to_lower_index
     yield P.test_select_matches_brute_force_sort
@@ -36,7 +39,7 @@ def _pins():
     for args in [("q8_0", 256, 128, 0, 8), ("q8_0", 256, 64, 96, 4)]:
         yield lambda a=args: P.test_oracle_matches_scalar_twin(*a)
     yield P.test_one_expert_top1_layer_is_dense_swiglu_ffn
-    for et in ("q8_0", "q4_k"):
+    for et in ("q8_0", "q4_k", "q2_k"):
         yield lambda et=et: P.test_doubling_down_scales_doubles_routed_part_exactly(et)
     yield P.test_rows_are_independent_of_batch
 
@@ -67,6 +70,29 @@ def _q4k_field_shifted(sbytes, bit):
 def _q4k_plus_min(buf, rows, cols, row_start=0, row_count=None):
     r0, n = om._rows(rows, row_start, row_count)
     d, dmin, sc, m, q = om.q4_k_fields(buf, rows, cols, r0, n)
+    w = d[:, None, None] * sc[:, :, None] * q + dmin[:, None, None] * m[:, :, None]
+    return w.reshape(n, cols)
+
+
+def _q2k_fields_transposed(buf, rows, cols, row_start=0, row_count=None):
+    # weight i read from byte i // 4, bits 2 (i % 4): the field order transposed
+    d, dmin, sc, m, q = _orig["q2_k_fields"](buf, rows, cols, row_start, row_count)
+    return d, dmin, sc, m, q.reshape(q.shape[0], 16, 4, 4).transpose(0, 1, 3, 2).reshape(q.shape)
+
+
+def _q2k_fields_scale_nibbles_swapped(*a, **k):
+    d, dmin, sc, m, q = _orig["q2_k_fields"](*a, **k)
+    return d, dmin, m, sc, q
+
+
+def _q2k_offsets_unpadded(rows, cols):
+    ns = cols // 256
+    return 4 * rows * ns, 20 * rows * ns
+
+
+def _q2k_plus_min(buf, rows, cols, row_start=0, row_count=None):
+    r0, n = om._rows(rows, row_start, row_count)
+    d, dmin, sc, m, q = om.q2_k_fields(buf, rows, cols, r0, n)
     w = d[:, None, None] * sc[:, :, None] * q + dmin[:, None, None] * m[:, :, None]
     return w.reshape(n, cols)
 
@@ -110,6 +136,10 @@ MUTATIONS = {
     "q4k_min_offset": ("_q4_k_field", _q4k_field_shifted),
     "q4k_min_sign": ("dequant_q4_k", _q4k_plus_min),
     "q8_plane_offset": ("q8_0_quant_offset", _q8_offset_unpadded),
+    "q2k_field_order": ("q2_k_fields", _q2k_fields_transposed),
+    "q2k_scale_nibbles": ("q2_k_fields", _q2k_fields_scale_nibbles_swapped),
+    "q2k_plane_offsets": ("q2_k_offsets", _q2k_offsets_unpadded),
+    "q2k_min_sign": ("dequant_q2_k", _q2k_plus_min),
     "tie_to_higher": ("select_experts", _select_high_tie),
     "no_renormalise": ("routing_weights", _weights_unnormalised),
     "silu_is_sigmoid": ("silu", _sigmoid_only),

@@ -30,7 +30,10 @@ def test_f16_decode_all_bit_patterns_match_numpy():
     assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
 
 
-@pytest.mark.parametrize("fixture,dtype", [("q8_0_planar.txt", "q8_0"), ("q4_k_planar.txt", "q4_k")])
+FIXTURES = [("q8_0_planar.txt", "q8_0"), ("q4_k_planar.txt", "q4_k"), ("q2_k_planar.txt", "q2_k")]
+
+
+@pytest.mark.parametrize("fixture,dtype", FIXTURES)
 def test_dequant_matches_hand_derived_fixture(fixture, dtype):
     rows, cols, buf, expects = read_fixture(fixture)
     assert synth.tensor_bytes(dtype, rows, cols) == buf.size
@@ -41,7 +44,7 @@ def test_dequant_matches_hand_derived_fixture(fixture, dtype):
 
 
 def test_dequant_fixture_twin_agrees():
-    for fixture, dtype in [("q8_0_planar.txt", "q8_0"), ("q4_k_planar.txt", "q4_k")]:
+    for fixture, dtype in FIXTURES:
         rows, cols, buf, _ = read_fixture(fixture)
         W = om.dequant(dtype, buf, rows, cols)
         for r in range(rows):
@@ -125,6 +128,65 @@ def test_q4_k_multi_row_record_order():
         for b in range(2):
             assert np.all(W[r, 256 * b:256 * (b + 1)] == r * 2 + b + 1)
     assert np.array_equal(om.dequant_q4_k(buf, 2, 512, row_start=1, row_count=1), W[1:2])
+
+
+def _q2k_tensor(recs, rows, cols):
+    """Planar Q2_K bytes from records (d_bits, dmin_bits, sc[16], m[16],
+    q[16][16]) in row-major super-block order (test-side encoder, written
+    from the layout: plane starts rounded up to 256 bytes, scale byte
+    m << 4 | sc, weight i of a sub-block at bits 2 (i // 4) of its byte i % 4).
+    """
+    n = len(recs)
+    so = -(-4 * n // 256) * 256
+    qo = -(-(so + 16 * n) // 256) * 256
+    out = bytearray(qo + 64 * n)
+    for k, (db, mb, sc, m, q) in enumerate(recs):
+        out[4 * k: 4 * k + 4] = int(db).to_bytes(2, "little") + int(mb).to_bytes(2, "little")
+        for s in range(16):
+            out[so + 16 * k + s] = (m[s] & 15) << 4 | (sc[s] & 15)
+            for i in range(16):
+                out[qo + 64 * k + 4 * s + i % 4] |= (q[s][i] & 3) << (2 * (i // 4))
+    assert len(out) == synth.tensor_bytes("q2_k", rows, cols)
+    return np.frombuffer(bytes(out), dtype=np.uint8).copy()
+
+
+@pytest.mark.parametrize("s", [0, 1, 5, 10, 15])
+def test_q2_k_single_field_positions(s):
+    # Only sub-block s gets a scale, and only one weight a quant: exactly one
+    # non-zero weight must appear, at column 16*s + i, with value sc * q.
+    for i in (0, 1, 3, 4, 6, 11, 15):
+        q = [[0] * 16 for _ in range(16)]
+        q[s][i] = 3 - (i % 2)
+        sc = [0] * 16
+        sc[s] = 15 - (s % 7)
+        buf = _q2k_tensor([(0x3C00, 0x3C00, sc, [0] * 16, q)], 1, 256)
+        W = om.dequant_q2_k(buf, 1, 256)[0]
+        assert list(np.nonzero(W)[0]) == [16 * s + i]
+        assert W[16 * s + i] == (3 - (i % 2)) * (15 - (s % 7))
+    # Only min m_s set: the whole sub-block s equals -dmin * m_s.
+    m = [0] * 16
+    m[s] = 1 + (s % 15)
+    buf = _q2k_tensor([(0x3C00, 0x3800, [0] * 16, m, [[3] * 16 for _ in range(16)])], 1, 256)
+    W = om.dequant_q2_k(buf, 1, 256)[0]
+    exp = np.zeros(256)
+    exp[16 * s:16 * s + 16] = -0.5 * (1 + (s % 15))
+    assert np.array_equal(W, exp)
+
+
+def test_q2_k_multi_row_record_order():
+    # Three rows x 512 cols: record (r, b) is at r*ns + b in all three planes,
+    # and the planes start at the rounded offsets of a 6-record tensor.
+    recs = []
+    for r in range(3):
+        for b in range(2):
+            v = r * 2 + b + 1          # 1..6
+            recs.append((0x3C00, 0x3C00, [v] * 16, [0] * 16, [[1] * 16 for _ in range(16)]))
+    buf = _q2k_tensor(recs, 3, 512)
+    W = om.dequant_q2_k(buf, 3, 512)
+    for r in range(3):
+        for b in range(2):
+            assert np.all(W[r, 256 * b:256 * (b + 1)] == r * 2 + b + 1)
+    assert np.array_equal(om.dequant_q2_k(buf, 3, 512, row_start=1, row_count=2), W[1:3])
 
 
 def test_q8_0_row_slice_matches_full():
@@ -230,7 +292,7 @@ def test_silu_is_g_times_logistic():
 
 
 @pytest.mark.parametrize("etype,H,F,Fs,E", [("q8_0", 256, 128, 0, 8), ("q8_0", 256, 64, 96, 4),
-                                             ("q4_k", 256, 256, 64, 4)])
+                                             ("q4_k", 256, 256, 64, 4), ("q2_k", 256, 256, 64, 4)])
 def test_oracle_matches_scalar_twin(etype, H, F, Fs, E):
     cfg = small_config(hidden=H, ffn=F, shared_ffn=Fs, n_experts=E, expert_type=etype,
                        n_tokens=2, seed_index=200 + F)
@@ -274,7 +336,7 @@ def test_identical_experts_make_routing_irrelevant():
     assert np.allclose(ref["y"], one, rtol=1e-12, atol=1e-12 * np.abs(one).max())
 
 
-@pytest.mark.parametrize("etype", ["q8_0", "q4_k"])
+@pytest.mark.parametrize("etype", ["q8_0", "q4_k", "q2_k"])
 def test_doubling_down_scales_doubles_routed_part_exactly(etype):
     F = 128 if etype == "q8_0" else 256
     cfg = small_config(n_experts=4, ffn=F, shared_ffn=64, expert_type=etype, n_tokens=2)
@@ -329,6 +391,20 @@ def test_q4_k_generated_fields_cover_their_ranges():
     assert dmin.min() >= 2.0 ** -12 and dmin.max() <= 2.0 ** -10
     assert sc.min() == 0 and sc.max() == 63 and m.min() == 0 and m.max() == 63
     assert q.min() == 0 and q.max() == 15
+
+
+def test_q2_k_generated_fields_cover_their_ranges():
+    cfg = small_config(n_experts=4, expert_type="q2_k", ffn=256)
+    inp = synth.draw_layer(cfg, threads=1)
+    assert inp.gate.size == synth.tensor_bytes("q2_k", 4 * 256, 256)
+    d, dmin, sc, m, q = om.q2_k_fields(inp.gate, 4 * 256, 256)
+    assert d.min() >= 2.0 ** -10 and d.max() <= 2.0 ** -8
+    assert dmin.min() >= 2.0 ** -10 and dmin.max() <= 2.0 ** -8
+    assert sc.min() == 0 and sc.max() == 15 and m.min() == 0 and m.max() == 15
+    assert q.min() == 0 and q.max() == 3
+    # every quant value is about equally frequent (uniform random bytes)
+    counts = np.bincount(q.reshape(-1), minlength=4) / q.size
+    assert np.all(np.abs(counts - 0.25) < 0.01)
 
 
 def test_margin_predicate_enforces_gaps():
