@@ -53,7 +53,9 @@ def traffic_file(kernel: str, workload: str) -> str:
 
 
 def _bytes_per_row(dtype: str, cols: int) -> float:
-    return cols // 32 * 34 if dtype == "q8_0" else cols // 256 * 144
+    if dtype == "q8_0":
+        return cols // 32 * 34
+    return cols // 256 * (144 if dtype == "q4_k" else 84)
 
 
 def layer_bytes(cfg, distinct: int, batched: bool = False) -> dict:
@@ -447,8 +449,9 @@ def main(argv=None) -> int:
         metric = f"MoE layer tokens/s + achieved HBM GB/s, {cfg.name} ({M} tokens), 1 MI355X"
     # Arithmetic of the expert products: integer quants times 16-bit integer
     # activations (int8 limbs, int32 sums, fp32 scales) up to 16 tokens; bf16
-    # matrix-core products of exact integer quants and split activations above.
-    dtype = "i8xi16->i32+f32" if M <= 16 else "bf16x2->f32"
+    # matrix-core products of exact integer quants and split activations above
+    # (Q2_K experts stay on the integer path at every batch size).
+    dtype = "i8xi16->i32+f32" if M <= 16 or cfg.expert_type == "q2_k" else "bf16x2->f32"
     out = {
         "metric": metric,
         "value": round(value, 1),

@@ -218,8 +218,8 @@ int32_t moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_weig
 
 /* Dequantise rows [row_start, row_start + row_count) of a rows x cols tensor
  * of `dtype` into out [row_count][cols] float (test hook for the block
- * decoders).  Q8_0 yields d*q, Q4_K yields fma(d*sc, q, -(dmin*m)); both are
- * the exactly rounded float of the block's value. */
+ * decoders).  Q8_0 yields d*q, Q4_K and Q2_K yield fma(d*sc, q, -(dmin*m));
+ * all are the exactly rounded float of the block's value. */
 int32_t moe_dequant_rows(int32_t dtype, const void* tensor, int64_t rows, int32_t cols,
                          int64_t row_start, int64_t row_count, float* out, void* hip_stream);
 

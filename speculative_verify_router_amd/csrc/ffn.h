@@ -1,14 +1,15 @@
 // Fused dequantise-and-multiply skinny GEMM for the expert FFNs.
 //
-// Routed gate/up/down are Q4_K or Q8_0 and the shared expert Q8_0 ("Step
-// 3.7 Flash Mixed-Quant GGUF", Tensor recipe; "Step-5 Preview GGUF",
-// Precision distribution table).  At a verify batch of four tokens with 8
+// Routed gate/up/down are Q4_K, Q2_K or Q8_0 and the shared expert Q8_0
+// ("Step 3.7 Flash Mixed-Quant GGUF", Tensor recipe; "Step-5 Preview GGUF",
+// Precision distribution table and Tensor-type table).  At a verify batch of four tokens with 8
 // of 288-352 experts each, an expert serves about one token, so this is an
 // HBM-bound matrix-vector product: each selected expert's quant blocks are
 // streamed once for all of that expert's tokens.
 //
 // Mapping.  A 16-byte chunk of the quant plane is the unit of loading:
-// 16 weights for Q8_0, one 32-weight sub-block for Q4_K.  A row of K
+// 16 weights for Q8_0, one 32-weight sub-block for Q4_K, four 16-weight
+// sub-blocks for Q2_K.  A row of K
 // columns has K / kWpc chunks, covered by a group of `lpr` consecutive
 // lanes (lpr | 64), lane j of the group taking chunks j, j+lpr, ...,
 // j+(CPL-1)*lpr.  A wave works on 64/lpr rows at once and every wave load
@@ -60,8 +61,9 @@ constexpr int shape_cpl(int code) { return code & 255; }
 constexpr int shape_lpr(int code) { return code >> 8; }
 
 // Tokens per pass: keep the per-lane activation slice within 64 floats.
+constexpr int wpc_for(int fmt) { return fmt == kQ8_0 ? 16 : fmt == kQ4_K ? 32 : 64; }
 constexpr int tp_for(int fmt, int cpl) {
-  return (cpl * (fmt == kQ8_0 ? 16 : 32) <= 16) ? 4 : (cpl * (fmt == kQ8_0 ? 16 : 32) <= 32) ? 2 : 1;
+  return (cpl * wpc_for(fmt) <= 16) ? 4 : (cpl * wpc_for(fmt) <= 32) ? 2 : 1;
 }
 
 // Ring depth: as many stages (2 to 5) as fit in about kRingVgprs VGPRs of
@@ -70,11 +72,12 @@ constexpr int tp_for(int fmt, int cpl) {
 #define SVR_RING_VGPRS 100
 #endif
 constexpr int kRingVgprs = SVR_RING_VGPRS;
+constexpr int chunk_vgprs(int fmt) { return fmt == kQ8_0 ? 5 : fmt == kQ4_K ? 8 : 6; }
 constexpr int nst_for(int fmt, int cpl, bool gateup) {
-  return (cpl * (gateup ? 2 : 1) * (fmt == kQ8_0 ? 5 : 8) * 5 <= kRingVgprs)   ? 5
-         : (cpl * (gateup ? 2 : 1) * (fmt == kQ8_0 ? 5 : 8) * 4 <= kRingVgprs) ? 4
-         : (cpl * (gateup ? 2 : 1) * (fmt == kQ8_0 ? 5 : 8) * 3 <= kRingVgprs) ? 3
-                                                                                : 2;
+  return (cpl * (gateup ? 2 : 1) * chunk_vgprs(fmt) * 5 <= kRingVgprs)   ? 5
+         : (cpl * (gateup ? 2 : 1) * chunk_vgprs(fmt) * 4 <= kRingVgprs) ? 4
+         : (cpl * (gateup ? 2 : 1) * chunk_vgprs(fmt) * 3 <= kRingVgprs) ? 3
+                                                                          : 2;
 }
 
 template <int FMT, int CPL, bool GATEUP>
@@ -118,22 +121,14 @@ __device__ __forceinline__ void compute_stage(const Stage<FMT, CPL, GATEUP>& s,
   for (int t = 0; t < NT; ++t) acc0[t] = acc1[t] = 0.f;
 #pragma unroll
   for (int ci = 0; ci < CPL; ++ci) {
-    const int sub = cc[ci] & 7;  // Q4_K sub-block of this chunk
+    const int sub = cc[ci] & 7;  // Q4_K sub-block of this chunk (unused otherwise)
     const ChunkScale k0 = decode_scale(s.c0[ci], sub);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const float v = chunk_dot(s.c0[ci], xs[t][ci]) * xs[t][ci].s;
-      acc0[t] = FMT == kQ8_0 ? fmaf(k0.a, v, acc0[t])
-                             : fmaf(k0.a, v, fmaf(-k0.b, xs[t][ci].sum, acc0[t]));
-    }
+    for (int t = 0; t < NT; ++t) acc0[t] = chunk_fma(s.c0[ci], k0, xs[t][ci], acc0[t]);
     if (GATEUP) {
       const ChunkScale k1 = decode_scale(s.c1[ci], sub);
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const float v = chunk_dot(s.c1[ci], xs[t][ci]) * xs[t][ci].s;
-        acc1[t] = FMT == kQ8_0 ? fmaf(k1.a, v, acc1[t])
-                               : fmaf(k1.a, v, fmaf(-k1.b, xs[t][ci].sum, acc1[t]));
-      }
+      for (int t = 0; t < NT; ++t) acc1[t] = chunk_fma(s.c1[ci], k1, xs[t][ci], acc1[t]);
     }
   }
 #pragma unroll

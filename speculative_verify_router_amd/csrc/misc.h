@@ -29,8 +29,8 @@ __global__ __launch_bounds__(kBlock) void k_combine(const float* __restrict__ o,
 }
 
 // Dequantise rows [r0, r0 + n) of a planar tensor into out[n][cols].
-// Q8_0: d*q.  Q4_K: fma(d*sc, q, -(dmin*m)); d*sc and dmin*m are exact in
-// fp32, so the result is the correctly rounded block value.
+// Q8_0: d*q.  Q4_K and Q2_K: fma(d*sc, q, -(dmin*m)); d*sc and dmin*m are
+// exact in fp32, so the result is the correctly rounded block value.
 __global__ __launch_bounds__(kBlock) void k_dequant(int fmt, const uint8_t* __restrict__ base,
                                                     int64_t rows, int cols, int64_t r0, int64_t n,
                                                     float* __restrict__ out) {
@@ -46,6 +46,19 @@ __global__ __launch_bounds__(kBlock) void k_dequant(int fmt, const uint8_t* __re
       const float d = f16_to_f32(*reinterpret_cast<const uint16_t*>(base + 2 * (r * nb + (c >> 5))));
       const int q = (int)(int8_t)base[qoff + r * cols + c];
       v = d * (float)q;
+    } else if (fmt == MOE_Q2_K) {
+      const int64_t n_sb = rows * (cols >> 8);
+      const int64_t soff = (4 * n_sb + 255) & ~(int64_t)255;
+      const int64_t qoff = (soff + 16 * n_sb + 255) & ~(int64_t)255;
+      const int64_t rec = r * (cols >> 8) + (c >> 8);
+      const uint8_t* dd = base + 4 * rec;
+      const float d = f16_to_f32((uint32_t)dd[0] | ((uint32_t)dd[1] << 8));
+      const float dmin = f16_to_f32((uint32_t)dd[2] | ((uint32_t)dd[3] << 8));
+      const int s = (c >> 4) & 15, wi = c & 15;
+      const uint32_t sm = base[soff + 16 * rec + s];
+      const uint32_t qb = base[qoff + 64 * rec + 4 * s + (wi & 3)];
+      const float q = (float)((qb >> (2 * (wi >> 2))) & 3u);
+      v = fmaf(d * (float)(sm & 15u), q, -(dmin * (float)(sm >> 4)));
     } else {
       const int64_t ns = cols >> 8;
       const int64_t rec = r * ns + (c >> 8);

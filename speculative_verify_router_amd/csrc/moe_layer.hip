@@ -56,14 +56,16 @@ constexpr double kFlowSharedWaveBytes = 64.0 * 1024.0;
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-int wpc_of(int dtype) { return dtype == MOE_Q8_0 ? 16 : 32; }
+int wpc_of(int dtype) { return dtype == MOE_Q8_0 ? 16 : dtype == MOE_Q4_K ? 32 : 64; }
 int blk_of(int dtype) { return dtype == MOE_Q8_0 ? 32 : 256; }
+// Types of the shared expert, and of the routed experts (also Q2_K).
 bool quant_type(int dtype) { return dtype == MOE_Q8_0 || dtype == MOE_Q4_K; }
-int qfmt(int dtype) { return dtype == MOE_Q8_0 ? kQ8_0 : kQ4_K; }
+bool routed_type(int dtype) { return quant_type(dtype) || dtype == MOE_Q2_K; }
+int qfmt(int dtype) { return dtype == MOE_Q8_0 ? kQ8_0 : dtype == MOE_Q4_K ? kQ4_K : kQ2_K; }
 
 // Lanes per row and 16-byte chunks per lane for a row of K columns.  The
 // shape keeps the per-lane activation slice within 96 floats (Q4_K: 3
-// chunks of 32, Q8_0: 6 chunks of 16) where possible and wastes the fewest
+// chunks of 32, Q8_0: 6 chunks of 16, Q2_K: 1 chunk of 64) where possible and wastes the fewest
 // lane positions (chunk positions past the row's end load the row's last
 // chunk against a zero activation); among equal shapes the fewest chunks
 // per lane.  Rows too long for that take 64 lanes and up to 8 chunks.
@@ -73,7 +75,7 @@ struct FfnShape {
 bool ffn_shape(int dtype, int K, FfnShape* s) {
   if (K <= 0 || K % blk_of(dtype)) return false;
   const int chunks = K / wpc_of(dtype);
-  const int cap = dtype == MOE_Q8_0 ? 6 : 3;
+  const int cap = dtype == MOE_Q8_0 ? 6 : dtype == MOE_Q4_K ? 3 : 1;
   double best = 0.0;
   for (int lpr = 64; lpr >= 1; lpr >>= 1) {
     const int cpl = (chunks + lpr - 1) / lpr;
@@ -105,7 +107,7 @@ int check_desc(const moe_layer_desc* d) {
   if (d->hidden <= 0 || d->n_experts <= 0 || d->top_k <= 0 || d->ffn <= 0 || d->shared_ffn < 0)
     return MOE_ERR_SHAPE;
   if (d->flags & ~MOE_SINGLE_LAUNCH) return MOE_ERR_ARG;
-  if (!quant_type(d->expert_type)) return MOE_ERR_DTYPE;
+  if (!routed_type(d->expert_type)) return MOE_ERR_DTYPE;
   if (d->shared_ffn > 0 && !quant_type(d->shared_type)) return MOE_ERR_DTYPE;
   if (d->n_experts > kMaxExperts) return MOE_ERR_SHAPE;
   if (d->top_k > d->n_experts || d->top_k > kMaxTopK) return MOE_ERR_SHAPE;
@@ -243,7 +245,9 @@ int tiles_of(const FfnArgs& a) {
 }
 
 // Bytes per weight row of K columns.
-double row_bytes(int dtype, int K) { return dtype == MOE_Q8_0 ? K / 32 * 34.0 : K / 256 * 144.0; }
+double row_bytes(int dtype, int K) {
+  return dtype == MOE_Q8_0 ? K / 32 * 34.0 : K / 256 * (dtype == MOE_Q4_K ? 144.0 : 84.0);
+}
 
 // Single-role launches, every (format, chunks-per-lane) pair.
 template <int FMT, bool GU>
@@ -268,6 +272,9 @@ bool launch_ffn(int dtype, bool gateup, FfnArgs a, int slots_max, hipStream_t st
   if (dtype == MOE_Q8_0)
     return gateup ? launch_ffn_c<kQ8_0, true>(s.cpl, a, dtype, slots_max, st)
                   : launch_ffn_c<kQ8_0, false>(s.cpl, a, dtype, slots_max, st);
+  if (dtype == MOE_Q2_K)
+    return gateup ? launch_ffn_c<kQ2_K, true>(s.cpl, a, dtype, slots_max, st)
+                  : launch_ffn_c<kQ2_K, false>(s.cpl, a, dtype, slots_max, st);
   return gateup ? launch_ffn_c<kQ4_K, true>(s.cpl, a, dtype, slots_max, st)
                 : launch_ffn_c<kQ4_K, false>(s.cpl, a, dtype, slots_max, st);
 }
@@ -356,7 +363,8 @@ bool launch_dual_keys(int akey, int bkey, hipStream_t st, const FfnArgs& a, cons
   SVR_D(FA, CA, 0, kQ8_0, 5, 0)
   SVR_D(kQ4_K, 2, 64, kQ8_0, 5, 16) SVR_D(kQ4_K, 2, 64, kQ8_0, 3, 32)
   SVR_D(kQ8_0, 4, 64, kQ8_0, 5, 16) SVR_D(kQ8_0, 4, 64, kQ8_0, 3, 32)
-  SVR_DG(kQ4_K, 1) SVR_DG(kQ4_K, 2) SVR_DG(kQ4_K, 3) SVR_DG(kQ8_0, 4)
+  SVR_D(kQ2_K, 1, 64, kQ8_0, 5, 16) SVR_D(kQ2_K, 1, 64, kQ8_0, 3, 32)
+  SVR_DG(kQ4_K, 1) SVR_DG(kQ4_K, 2) SVR_DG(kQ4_K, 3) SVR_DG(kQ8_0, 4) SVR_DG(kQ2_K, 1)
 #undef SVR_DG
 #undef SVR_D
   return false;
@@ -401,7 +409,7 @@ bool launch_down_tok(int dtype, const FfnShape& ds, hipStream_t st, const FfnArg
     SVR_DT(kQ4_K, 3, 16) SVR_DT(kQ8_0, 5, 16) SVR_DT(kQ8_0, 3, 32)
     SVR_DT(kQ4_K, 1, 0) SVR_DT(kQ4_K, 2, 0) SVR_DT(kQ4_K, 3, 0) SVR_DT(kQ8_0, 1, 0)
     SVR_DT(kQ8_0, 2, 0) SVR_DT(kQ8_0, 3, 0) SVR_DT(kQ8_0, 4, 0) SVR_DT(kQ8_0, 5, 0)
-    SVR_DT(kQ8_0, 6, 0)
+    SVR_DT(kQ8_0, 6, 0) SVR_DT(kQ2_K, 1, 32) SVR_DT(kQ2_K, 1, 0) SVR_DT(kQ2_K, 2, 0)
   }
 #undef SVR_DT
   return false;
@@ -425,6 +433,7 @@ bool launch_down_combine_key(int k, hipStream_t st, const FfnArgs& a, const Comb
   SVR_DC(kQ4_K, 3, 16) SVR_DC(kQ8_0, 5, 16)
   SVR_DC(kQ4_K, 1, 0) SVR_DC(kQ4_K, 2, 0) SVR_DC(kQ4_K, 3, 0) SVR_DC(kQ8_0, 1, 0) SVR_DC(kQ8_0, 2, 0)
   SVR_DC(kQ8_0, 3, 0) SVR_DC(kQ8_0, 4, 0) SVR_DC(kQ8_0, 5, 0) SVR_DC(kQ8_0, 6, 0)
+  SVR_DC(kQ2_K, 1, 32) SVR_DC(kQ2_K, 1, 0) SVR_DC(kQ2_K, 2, 0)
 #undef SVR_DC
   return false;
 }
@@ -719,6 +728,7 @@ const char* const kGemmStageNames[kGemmStages] = {"route", "shared_gateup", "gat
 
 bool gemm_path(const Plan& p) {
   if (p.M <= kFusedMaxTokens) return false;
+  if (p.et == MOE_Q2_K) return false;  // no matrix-core decoder for this type
   // Split activations and h are addressed with 32-bit byte offsets.
   const int64_t P = (int64_t)p.M * p.k;
   if (P * std::max(p.H, p.F) * 4 >= (1ll << 31)) return false;
@@ -986,6 +996,13 @@ int32_t moe_tensor_bytes(int32_t dtype, int64_t rows, int64_t cols, int64_t* byt
       if (cols % 256) return MOE_ERR_SHAPE;
       *bytes = 144 * rows * (cols / 256);
       return MOE_OK;
+    case MOE_Q2_K: {
+      if (cols % 256) return MOE_ERR_SHAPE;
+      const int64_t n = rows * (cols / 256);
+      const int64_t s = (int64_t)align256((size_t)(4 * n));
+      *bytes = (int64_t)align256((size_t)(s + 16 * n)) + 64 * n;
+      return MOE_OK;
+    }
     default: return MOE_ERR_DTYPE;
   }
 }
@@ -1055,7 +1072,7 @@ int32_t moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_weig
 
 int32_t moe_dequant_rows(int32_t dtype, const void* tensor, int64_t rows, int32_t cols,
                          int64_t row_start, int64_t row_count, float* out, void* hip_stream) {
-  if (!quant_type(dtype)) return MOE_ERR_DTYPE;
+  if (!routed_type(dtype)) return MOE_ERR_DTYPE;
   if (rows < 0 || cols <= 0 || row_start < 0 || row_count < 0) return MOE_ERR_SHAPE;
   if (cols % blk_of(dtype)) return MOE_ERR_SHAPE;
   if (row_start + row_count > rows) return MOE_ERR_SHAPE;

@@ -1,11 +1,12 @@
-// Planar Q8_0 / Q4_K blocks: 16-byte chunk loads, scale decoding and the
-// fused dequantise-and-dot of one chunk against 16-bit activations.
+// Planar Q8_0 / Q4_K / Q2_K blocks: 16-byte chunk loads, scale decoding and
+// the fused dequantise-and-dot of one chunk against 16-bit activations.
 //
 // Formats (include/moe_layer.h): Q8_0 blocks of 32 int8 with an fp16 scale
 // d, w = d*q; Q4_K super-blocks of 256 with fp16 d, dmin and per-32 6-bit
-// sc, m, 4-bit q, w = d*sc*q - dmin*m ("Step-5 Preview GGUF" and "Step 3.7
-// Flash Mixed-Quant GGUF" name these tensor types; their bit layouts are
-// this library's).
+// sc, m, 4-bit q, w = d*sc*q - dmin*m; Q2_K super-blocks of 256 with fp16
+// d, dmin and per-16 4-bit sc, m, 2-bit q, the same rule ("Step-5 Preview
+// GGUF" and "Step 3.7 Flash Mixed-Quant GGUF" name these tensor types;
+// their bit layouts are this library's).
 //
 // Dot product.  The weights' integer quants go into v_dot4_i32_i8 as they
 // are: a Q8_0 quant dword is four int8 weights; a Q4_K dword (8 nibbles,
@@ -20,7 +21,7 @@
 
 namespace svr {
 
-enum QFmt { kQ8_0 = 1, kQ4_K = 2 };
+enum QFmt { kQ8_0 = 1, kQ4_K = 2, kQ2_K = 3 };
 
 template <int FMT>
 struct QTraits;
@@ -32,26 +33,44 @@ template <>
 struct QTraits<kQ4_K> {
   static constexpr int kWpc = 32;
 };
-
-// The two planes of one expert's rows of a stacked planar tensor, as buffer
-// resources (32-bit offsets; reads past the expert's rows return zero).
-// Both formats carry K/16 bytes of scale data per row: Q8_0 K/32 fp16
-// scales, Q4_K K/256 headers of 16 bytes.
-struct QPlanes {
-  __amdgpu_buffer_rsrc_t q, s;
-  uint32_t qrow, srow;  // bytes per row in each plane
+template <>
+struct QTraits<kQ2_K> {
+  static constexpr int kWpc = 64;  // four 16-weight sub-blocks
 };
+
+// The planes of one expert's rows of a stacked planar tensor, as buffer
+// resources (32-bit offsets; reads past the expert's rows return zero).
+// Every format carries K/16 bytes of scale data per row in plane s: Q8_0
+// K/32 fp16 scales, Q4_K K/256 headers of 16 bytes, Q2_K K/256 records of
+// 16 scale bytes.  Q2_K keeps d and dmin in a third plane d of K/64 bytes
+// per row, so a row's offset there is its plane-s offset / 4.
+struct QPlanes {
+  __amdgpu_buffer_rsrc_t q, s, d;
+  uint32_t qrow, srow;  // bytes per row in planes q and s
+};
+
+__device__ __forceinline__ int64_t round256(int64_t v) { return (v + 255) & ~(int64_t)255; }
 
 template <int FMT>
 __device__ __forceinline__ QPlanes expert_planes(const uint8_t* base, int64_t total_rows, int K,
                                                  int64_t row0, int rows) {
   QPlanes p;
   p.srow = (uint32_t)(K >> 4);
-  p.qrow = (FMT == kQ8_0) ? (uint32_t)K : (uint32_t)(K >> 1);
+  p.qrow = (FMT == kQ8_0) ? (uint32_t)K : (FMT == kQ4_K) ? (uint32_t)(K >> 1) : (uint32_t)(K >> 2);
   const int64_t sbytes = total_rows * (int64_t)p.srow;
-  const int64_t qstart = (FMT == kQ8_0) ? ((sbytes + 255) & ~(int64_t)255) : sbytes;
-  p.s = make_rsrc(base + row0 * p.srow, (uint32_t)rows * p.srow);
-  p.q = make_rsrc(base + qstart + row0 * p.qrow, (uint32_t)rows * p.qrow);
+  if constexpr (FMT == kQ2_K) {
+    const uint32_t drow = (uint32_t)(K >> 6);
+    const int64_t sstart = round256(total_rows * (int64_t)drow);
+    const int64_t qstart = round256(sstart + sbytes);
+    p.d = make_rsrc(base + row0 * drow, (uint32_t)rows * drow);
+    p.s = make_rsrc(base + sstart + row0 * p.srow, (uint32_t)rows * p.srow);
+    p.q = make_rsrc(base + qstart + row0 * p.qrow, (uint32_t)rows * p.qrow);
+  } else {
+    const int64_t qstart = (FMT == kQ8_0) ? round256(sbytes) : sbytes;
+    p.s = make_rsrc(base + row0 * p.srow, (uint32_t)rows * p.srow);
+    p.q = make_rsrc(base + qstart + row0 * p.qrow, (uint32_t)rows * p.qrow);
+    p.d = p.s;
+  }
   return p;
 }
 
@@ -67,6 +86,12 @@ struct Chunk<kQ4_K> {
   uint4 q;
   uint4 h;  // super-block header: d | dmin << 16, then the 96-bit sc/m stream
 };
+template <>
+struct Chunk<kQ2_K> {
+  uint4 q;       // dword k: sub-block 4 (c % 4) + k of the super-block
+  uint32_t sc;   // byte k: that sub-block's sc | m << 4
+  uint32_t dd;   // d | dmin << 16
+};
 
 // Chunk c of a row whose plane offsets are qo = row * qrow and so = row * srow.
 __device__ __forceinline__ void load_chunk(Chunk<kQ8_0>& ch, const QPlanes& p, uint32_t qo,
@@ -79,12 +104,18 @@ __device__ __forceinline__ void load_chunk(Chunk<kQ4_K>& ch, const QPlanes& p, u
   ch.q = bload16(p.q, qo + 16u * c);
   ch.h = bload16(p.s, so + 16u * (c >> 3));
 }
+__device__ __forceinline__ void load_chunk(Chunk<kQ2_K>& ch, const QPlanes& p, uint32_t qo,
+                                           uint32_t so, int c) {
+  ch.q = bload16(p.q, qo + 16u * c);
+  ch.sc = bload4(p.s, so + 4u * c);
+  ch.dd = bload4(p.d, (so >> 2) + 4u * (c >> 2));
+}
 
 // Activations of one chunk position for one token, as 16-bit integers.
 //
 // A lane quantises each of its chunk slices of activations when it loads
-// them: q_i = rint(x_i / s) with s = max|x| / 32639 over the slice (32
-// values for Q4_K, 16 for Q8_0), split q = 256 hi + lo with hi, lo in
+// them: q_i = rint(x_i / s) with s = max|x| / 32639 over the slice (64
+// values for Q2_K, 32 for Q4_K, 16 for Q8_0), split q = 256 hi + lo with hi, lo in
 // int8, and packed in the byte order of the chunk's quant dwords.  Then
 // v_dot4_i32_i8 multiplies four weights by four limbs and accumulates
 // exactly in int32, and sum_i w_i x_i = (dot_hi * 256 + dot_lo) * s * scale.
@@ -109,6 +140,12 @@ struct XSlice<kQ8_0> {
   float s;
   float sum;  // unused
 };
+template <>
+struct XSlice<kQ2_K> {
+  uint32_t h[16], l[16];  // dword 4k + j: limbs of weights 16k + 4j .. 16k + 4j + 3
+  float s;
+  float sum[4];  // s * (sum of the quantised activations) of sub-block k
+};
 
 constexpr float kQ16Max = 32639.0f;     // |q| bound: hi = (q + 128) >> 8 stays in int8
 constexpr float kQ16Magic = 12583040.0f;  // 1.5 * 2^23 + 128
@@ -126,7 +163,8 @@ __device__ __forceinline__ void limbs4(float a, float b, float c, float d, uint3
   hi = __builtin_amdgcn_perm(cd, ab, 0x07060302u);
 }
 
-// Quantise N values (N = 32 for Q4_K, 16 for Q8_0) in slice order.
+// Quantise N values (N = 64 for Q2_K, 32 for Q4_K, 16 for Q8_0) in slice
+// order.
 template <int FMT, int N>
 __device__ __forceinline__ void quantize_slice(XSlice<FMT>& xs, const float (&v)[N]) {
   float amax = 0.f;
@@ -149,6 +187,17 @@ __device__ __forceinline__ void quantize_slice(XSlice<FMT>& xs, const float (&v)
       limbs4(g[1], g[3], g[5], g[7], xs.h[2 * k + 1], xs.l[2 * k + 1]);
     }
     xs.sum = xs.s * (float)(int32_t)(bsum - (uint32_t)N * kQ16MagicBits);
+  } else if constexpr (FMT == kQ2_K) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) limbs4(y[4 * k], y[4 * k + 1], y[4 * k + 2], y[4 * k + 3], xs.h[k], xs.l[k]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t b = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) b += __builtin_bit_cast(uint32_t, y[16 * k + i]);
+      xs.sum[k] = xs.s * (float)(int32_t)(b - 16u * kQ16MagicBits);
+    }
+    (void)bsum;
   } else {
 #pragma unroll
     for (int k = 0; k < 4; ++k) limbs4(y[4 * k], y[4 * k + 1], y[4 * k + 2], y[4 * k + 3], xs.h[k], xs.l[k]);
@@ -195,11 +244,16 @@ __device__ __forceinline__ void load_x_shared(XSlice<FMT>& xs, const float* base
 
 template <int FMT>
 __device__ __forceinline__ void zero_x(XSlice<FMT>& xs) {
-  constexpr int D = FMT == kQ4_K ? 8 : 4;
+  constexpr int D = FMT == kQ2_K ? 16 : FMT == kQ4_K ? 8 : 4;
 #pragma unroll
   for (int i = 0; i < D; ++i) xs.h[i] = xs.l[i] = 0u;
   xs.s = 0.f;
-  xs.sum = 0.f;
+  if constexpr (FMT == kQ2_K) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) xs.sum[k] = 0.f;
+  } else {
+    xs.sum = 0.f;
+  }
 }
 
 // acc += a * dot - b * xs.sum for one chunk: the chunk's contribution,
@@ -246,6 +300,12 @@ __device__ __forceinline__ ChunkScale decode_scale(const Chunk<kQ4_K>& ch, int s
   return decode_scale(ch, q4k_sel(sub));
 }
 
+// Q2_K: a = d, b = dmin of the super-block (sub-block scales and mins are
+// applied inside chunk_fma).
+__device__ __forceinline__ ChunkScale decode_scale(const Chunk<kQ2_K>& ch, int /*sub*/) {
+  return {f16_lo(ch.dd), f16_hi(ch.dd)};
+}
+
 // sum_i q_i x16_i over the chunk (exact in int32; converted with at most one
 // rounding).
 __device__ __forceinline__ float chunk_dot(const Chunk<kQ8_0>& ch, const XSlice<kQ8_0>& xs) {
@@ -271,6 +331,50 @@ __device__ __forceinline__ float chunk_dot(const Chunk<kQ4_K>& ch, const XSlice<
     al = __builtin_amdgcn_sdot4(o, (int)xs.l[2 * k + 1], al, false);
   }
   return (float)(ah * 256 + al);  // |.| < 2^24: exact
+}
+
+// acc + the chunk's contribution sum_i w_i x_i.
+__device__ __forceinline__ float chunk_fma(const Chunk<kQ8_0>& ch, const ChunkScale& k,
+                                           const XSlice<kQ8_0>& xs, float acc) {
+  return fmaf(k.a, chunk_dot(ch, xs) * xs.s, acc);
+}
+__device__ __forceinline__ float chunk_fma(const Chunk<kQ4_K>& ch, const ChunkScale& k,
+                                           const XSlice<kQ4_K>& xs, float acc) {
+  return fmaf(k.a, chunk_dot(ch, xs) * xs.s, fmaf(-k.b, xs.sum, acc));
+}
+
+// Q2_K: for sub-block k of the chunk, four v_dot4 per limb give the exact
+// dot of its 16 quants with the 16-bit activations; the 4-bit scales then
+// weight the four sub-block dots in int32 (|dot| <= 16*3*128 per limb, so
+// each product fits the 24-bit multiply), and the mins weight the
+// sub-block activation sums: contribution = d*s*(256 H + L) - dmin*sum_k
+// m_k*sum_k.  The plane extractions and scale fields depend only on the
+// chunk, so they are shared by every token of a pass.
+__device__ __forceinline__ float chunk_fma(const Chunk<kQ2_K>& ch, const ChunkScale& k,
+                                           const XSlice<kQ2_K>& xs, float acc) {
+  const uint32_t w[4] = {ch.q.x, ch.q.y, ch.q.z, ch.q.w};
+  int ah = 0, al = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    int h = 0, l = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int p = (int)((w[b] >> (2 * j)) & 0x03030303u);
+      h = __builtin_amdgcn_sdot4(p, (int)xs.h[4 * b + j], h, false);
+      l = __builtin_amdgcn_sdot4(p, (int)xs.l[4 * b + j], l, false);
+    }
+    const int sc = (int)__builtin_amdgcn_ubfe(ch.sc, 8 * b, 4);
+    // The sign extension from bit 23 is the identity on these values and
+    // tells the compiler that a 24-bit multiply-add suffices.
+    ah += __builtin_amdgcn_sbfe(h, 0, 24) * sc;
+    al += __builtin_amdgcn_sbfe(l, 0, 24) * sc;
+  }
+  const uint32_t mv = (ch.sc >> 4) & 0x0F0F0F0Fu;
+  float mn = (float)(mv & 0xFFu) * xs.sum[0];
+  mn = fmaf((float)((mv >> 8) & 0xFFu), xs.sum[1], mn);
+  mn = fmaf((float)((mv >> 16) & 0xFFu), xs.sum[2], mn);
+  mn = fmaf((float)(mv >> 24), xs.sum[3], mn);
+  return fmaf(k.a, fmaf((float)ah, 256.0f, (float)al) * xs.s, fmaf(-k.b, mn, acc));
 }
 
 }  // namespace svr

@@ -73,7 +73,8 @@ def test_missing_library_fails_loudly(monkeypatch):
 
 @pytest.mark.parametrize("dtype,rows,cols", [("q8_0", 1, 32), ("q8_0", 1280, 4096), ("q8_0", 7, 96),
                                              ("q4_k", 5, 256), ("q4_k", 352 * 1536, 4096),
-                                             ("f32", 3, 5)])
+                                             ("q2_k", 1, 256), ("q2_k", 3, 512),
+                                             ("q2_k", 352 * 4096, 1536), ("f32", 3, 5)])
 def test_tensor_bytes_match_the_generator(dtype, rows, cols):
     assert svr.moe_tensor_bytes(dtype, rows, cols) == synth.tensor_bytes(dtype, rows, cols)
 
@@ -114,11 +115,23 @@ def test_workspace_grows_with_tokens():
         (dict(hidden=100, expert_type="q8_0", shared_type="q8_0"), B.ERR_SHAPE),  # not k*32
     (dict(expert_type="f32"), B.ERR_DTYPE),
     (dict(shared_type="f32"), B.ERR_DTYPE),
+    (dict(shared_type="q2_k"), B.ERR_DTYPE),           # 2-bit: routed experts only
+    (dict(expert_type="q2_k", ffn=1000), B.ERR_SHAPE),
+    (dict(expert_type="q2_k", hidden=65536, shared_ffn=0), B.ERR_SHAPE),  # > 512 chunks a row
 ])
 def test_bad_descriptors_are_rejected(kw, status):
     d = _desc(**kw).c()
     out = ctypes.c_size_t()
     assert svr.lib().moe_workspace_bytes(ctypes.byref(d), 4, ctypes.byref(out)) == status
+
+
+def test_q2_k_routed_experts_are_accepted():
+    for M in (1, 4, 16, 512):
+        assert svr.moe_workspace_bytes(_desc(expert_type="q2_k"), M) > 0
+    # no matrix-core decoder for 2-bit experts: large batches take the three stages
+    d = _desc(expert_type="q2_k").c()
+    assert svr.lib().moe_stage_count(ctypes.byref(d), 512) == 3
+    assert svr.lib().moe_stage_count(ctypes.byref(_desc().c()), 512) == 5
 
 
 def test_shared_type_ignored_without_shared_expert():
