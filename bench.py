@@ -55,14 +55,14 @@ def traffic_file(kernel: str, workload: str) -> str:
 def _bytes_per_row(dtype: str, cols: int) -> float:
     if dtype == "q8_0":
         return cols // 32 * 34
-    return cols // 256 * (144 if dtype == "q4_k" else 84)
+    return cols // 256 * {"q4_k": 144, "q2_k": 84, "q3_k": 114}[dtype]
 
 
 def layer_bytes(cfg, distinct: int, batched: bool = False) -> dict:
     """Algorithmic HBM bytes of one call: router, distinct experts, shared expert, x, y;
     and of the "gateup" stage of the staged (default) or batched path."""
     H, F, Fs, M, k = cfg.hidden, cfg.ffn, cfg.shared_ffn, cfg.n_tokens, cfg.top_k
-    expert = 2 * F * _bytes_per_row(cfg.expert_type, H) + H * _bytes_per_row(cfg.expert_type, F)
+    expert = 2 * F * _bytes_per_row(cfg.expert_type, H) + H * _bytes_per_row(cfg.routed_down_type, F)
     shared = 0
     if Fs:
         shared = 2 * Fs * _bytes_per_row(cfg.shared_type, H) + H * _bytes_per_row(cfg.shared_type, Fs)
@@ -108,7 +108,7 @@ def cpu_baseline(cfg, inp, x) -> dict:
         limiter = threadpool_limits(1)
     except Exception:  # pragma: no cover
         limiter = None
-    kw = dict(top_k=cfg.top_k, ffn=cfg.ffn, expert_type=cfg.expert_type)
+    kw = dict(top_k=cfg.top_k, ffn=cfg.ffn, expert_type=cfg.expert_type, down_type=cfg.down_type)
     if cfg.shared_ffn:
         kw.update(shared=(inp.shared_gate, inp.shared_up, inp.shared_down),
                   shared_ffn=cfg.shared_ffn, shared_type=cfg.shared_type)
@@ -324,7 +324,8 @@ def main(argv=None) -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     desc = svr.LayerDesc(cfg.hidden, cfg.n_experts, cfg.top_k, cfg.ffn, cfg.shared_ffn,
-                         cfg.expert_type, cfg.shared_type, single_launch=args.single_launch)
+                         cfg.expert_type, cfg.shared_type, single_launch=args.single_launch,
+                         down_type=cfg.down_type)
     M, k = cfg.n_tokens, cfg.top_k
     R = max(1, args.instances)
 
@@ -450,8 +451,9 @@ def main(argv=None) -> int:
     # Arithmetic of the expert products: integer quants times 16-bit integer
     # activations (int8 limbs, int32 sums, fp32 scales) up to 16 tokens; bf16
     # matrix-core products of exact integer quants and split activations above
-    # (Q2_K experts stay on the integer path at every batch size).
-    dtype = "i8xi16->i32+f32" if M <= 16 or cfg.expert_type == "q2_k" else "bf16x2->f32"
+    # (Q2_K and Q3_K experts stay on the integer path at every batch size).
+    low_bit = cfg.expert_type in ("q2_k", "q3_k") or cfg.routed_down_type in ("q2_k", "q3_k")
+    dtype = "i8xi16->i32+f32" if M <= 16 or low_bit else "bf16x2->f32"
     out = {
         "metric": metric,
         "value": round(value, 1),
@@ -468,7 +470,8 @@ def main(argv=None) -> int:
         "config": {
             "workload": cfg.name, "tokens": M, "hidden": cfg.hidden, "experts": cfg.n_experts,
             "top_k": k, "ffn": cfg.ffn, "shared_ffn": cfg.shared_ffn,
-            "routed": cfg.expert_type, "shared": cfg.shared_type, "router": "f32",
+            "routed": cfg.expert_type, "routed_down": cfg.routed_down_type,
+            "shared": cfg.shared_type, "router": "f32",
             "instances_rotated": R, "distinct_experts": distinct,
         },
         "hbm_gbps": round(lay_bytes / K / (ms_per_step * 1e-3) / 1e9, 1),

@@ -13,7 +13,8 @@
  * Routers are F32, shared experts Q8_0 and routed experts Q4_K in the mixed
  * recipes ("Step-5 Preview GGUF", Precision distribution table; "Step 3.7
  * Flash Mixed-Quant GGUF", Tensor recipe); the 2-bit Step-5 recipes store
- * routed matrices in Q2_K ("Step-5 Preview GGUF", Tensor-type table).
+ * routed matrices in Q2_K and Q3_K, Q2_K-Protected2 with Q2_K gate/up and
+ * Q3_K down ("Step-5 Preview GGUF", Tensor-type table).
  *
  * What one call computes, for each token t of x [M][H]:
  *   l[e]    = sum_h router[e][h] * x[t][h]                      (F32 router)
@@ -59,6 +60,22 @@
  *            super-block (r, b) at Q + 64*(r*ns + b); sub-block s in bytes
  *            [4s, 4s+4) of them; weight i of a sub-block in byte i % 4, bits
  *            [2*(i/4), 2*(i/4)+2).  Total Q + 64*rows*ns bytes.
+ *   MOE_Q3_K rows x cols, cols % 256 == 0, ns = cols / 256, routed experts
+ *            only.  Super-blocks of 256 weights: fp16 d, 16 sub-blocks of 16
+ *            weights with a 6-bit scale S, 3-bit quants Q,
+ *            w = d*(S_s - 32)*(Q - 4).
+ *            Bytes [0, 2*rows*ns): fp16 d of super-block (r, b) at
+ *            2*(r*ns + b).
+ *            Bytes from S = round_up(2*rows*ns, 256): 16 scale bytes of
+ *            super-block (r, b) at S + 16*(r*ns + b), byte s = S_s (bits
+ *            6..7 zero).
+ *            Bytes from L = round_up(S + 16*rows*ns, 256): the low two bits
+ *            of every Q, 64 bytes per super-block at L + 64*(r*ns + b), laid
+ *            out as the Q2_K quants.
+ *            Bytes from G = round_up(L + 64*rows*ns, 256): the high bit of
+ *            every Q, 32 bytes per super-block at G + 32*(r*ns + b); weight i
+ *            of sub-block s in byte 4*(s/2) + i % 4, bit 4*(s % 2) + i/4.
+ *            Total G + 32*rows*ns bytes.
  *   Expert tensors are stacked experts-outermost and stored as one tensor:
  *   gate and up are (E*F) x H, down is (E*H) x F; expert e owns rows
  *   [e*F, (e+1)*F) (resp. [e*H, (e+1)*H)).  The shared expert's gate and up
@@ -78,10 +95,11 @@
  *   it returns MOE_OK, except MOE_ERR_LAUNCH, which reports a failure seen
  *   after enqueueing (hipGetLastError).  Shapes are checked before launch:
  *   1 <= n_experts <= 1024; 1 <= top_k <= min(n_experts, 64); hidden,
- *   ffn and shared_ffn multiples of 32 (Q8_0) or 256 (Q4_K, Q2_K) for the
- *   tensors that use them, and a row of at most 512 blocks of 16 bytes
- *   (Q8_0: 8192 columns, Q4_K: 16384, Q2_K: 32768); n_tokens >= 0 (0
- *   enqueues nothing).  MOE_Q2_K as shared_type is MOE_ERR_DTYPE.
+ *   ffn and shared_ffn multiples of 32 (Q8_0) or 256 (Q4_K, Q2_K, Q3_K) for
+ *   the tensors that use them, and a row of at most 512 blocks of 16 bytes
+ *   (Q8_0: 8192 columns, Q4_K: 16384, Q2_K and Q3_K: 32768); n_tokens >= 0
+ *   (0 enqueues nothing).  MOE_Q2_K or MOE_Q3_K as shared_type is
+ *   MOE_ERR_DTYPE.
  */
 #ifndef SVR_MOE_LAYER_H
 #define SVR_MOE_LAYER_H
@@ -98,6 +116,7 @@ extern "C" {
 #define MOE_Q8_0 1
 #define MOE_Q4_K 2
 #define MOE_Q2_K 3
+#define MOE_Q3_K 4
 
 /* Status codes. */
 #define MOE_OK 0
@@ -115,9 +134,12 @@ typedef struct moe_layer_desc {
   int32_t top_k;       /* k */
   int32_t ffn;         /* F, routed expert FFN width */
   int32_t shared_ffn;  /* Fs, shared expert FFN width; 0 = no shared expert */
-  int32_t expert_type; /* MOE_Q8_0, MOE_Q4_K or MOE_Q2_K: routed gate/up/down */
+  int32_t expert_type; /* MOE_Q8_0, MOE_Q4_K, MOE_Q2_K or MOE_Q3_K: routed
+                          gate/up, and down unless down_type says otherwise */
   int32_t shared_type; /* MOE_Q8_0 or MOE_Q4_K: shared gate/up/down */
   int32_t flags;       /* 0 or MOE_SINGLE_LAUNCH; other bits: MOE_ERR_ARG */
+  int32_t down_type;   /* routed down: 0 = expert_type, else MOE_Q8_0, MOE_Q4_K,
+                          MOE_Q2_K or MOE_Q3_K */
 } moe_layer_desc;
 
 /* desc->flags: run batches of 1 to 4 tokens as one kernel launch where the
@@ -129,7 +151,7 @@ typedef struct moe_layer_weights {
   const float* router;      /* [E][H] float */
   const void* gate;         /* (E*F) x H, expert_type */
   const void* up;           /* (E*F) x H, expert_type */
-  const void* down;         /* (E*H) x F, expert_type */
+  const void* down;         /* (E*H) x F, down_type (0: expert_type) */
   const void* shared_gate;  /* Fs x H, shared_type (unused if Fs == 0) */
   const void* shared_up;    /* Fs x H, shared_type */
   const void* shared_down;  /* H x Fs, shared_type */
@@ -191,8 +213,9 @@ int32_t moe_route(const moe_layer_desc* desc, const float* router, const float* 
  * integer quants, fp32 scales and activations split into two bf16 terms,
  * in five stages ("route", "shared_gateup", "gateup", "shared_down",
  * "down_combine"; the shared stages are empty without a shared expert);
- * with Q2_K routed experts they run the three stages of the small batches
- * instead (no matrix-core path for that type).
+ * with Q2_K or Q3_K routed matrices they run the three stages of the small
+ * batches instead (no matrix-core path for those types).  The single
+ * launch needs down_type equal to expert_type.
  * moe_stage_count / moe_stage_name say which. */
 int32_t moe_layer_forward(const moe_layer_desc* desc, const moe_layer_weights* weights,
                           const float* x, int32_t n_tokens, float* y,
@@ -218,8 +241,9 @@ int32_t moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_weig
 
 /* Dequantise rows [row_start, row_start + row_count) of a rows x cols tensor
  * of `dtype` into out [row_count][cols] float (test hook for the block
- * decoders).  Q8_0 yields d*q, Q4_K and Q2_K yield fma(d*sc, q, -(dmin*m));
- * all are the exactly rounded float of the block's value. */
+ * decoders).  Q8_0 yields d*q, Q4_K and Q2_K yield fma(d*sc, q, -(dmin*m)),
+ * Q3_K yields (d*(S-32))*(Q-4); all are the exactly rounded float of the
+ * block's value. */
 int32_t moe_dequant_rows(int32_t dtype, const void* tensor, int64_t rows, int32_t cols,
                          int64_t row_start, int64_t row_count, float* out, void* hip_stream);
 

@@ -16,7 +16,8 @@ blocks exactly, then dense products.  What the layer computes:
   ones (same tables, shared-expert rows) and routed experts in Q4_K ("Step
   3.7 Flash Mixed-Quant GGUF", Tensor recipe, routed rows), or in Q2_K as
   the 2-bit recipes of "Step-5 Preview GGUF" store them (Tensor-type table,
-  routed gate/up and down rows).
+  routed gate/up and down rows; the Q2_K-Protected2 recipe pairs Q2_K
+  gate/up with Q3_K down).
 * It is run on the verify batch of MTP speculative decoding: the last
   accepted token plus up to three drafts, all with logits ("Support
   Step3.5/3.7 flash mtp3", Overview, data-flow trace, target batch step).
@@ -34,7 +35,9 @@ block layouts.  Readings taken here:
   include/moe_layer.h; Q2_K is read as the K-quant family's 2-bit member:
   256-weight super-blocks with fp16 d and dmin, sixteen 16-weight
   sub-blocks with a 4-bit scale and a 4-bit min, 2-bit quants,
-  w = d*sc*q - dmin*m.
+  w = d*sc*q - dmin*m; Q3_K as the 3-bit member without mins: fp16 d,
+  sixteen 16-weight sub-blocks with a 6-bit scale S stored with offset 32
+  and 3-bit quants Q stored with offset 4, w = d*(S - 32)*(Q - 4).
 """
 
 from __future__ import annotations
@@ -191,6 +194,59 @@ def dequant_q2_k(buf, rows: int, cols: int, row_start: int = 0, row_count=None) 
     return w.reshape(n, cols)
 
 
+def q3_k_offsets(rows: int, cols: int):
+    """Plane starts of planar Q3_K: (scale plane, low-bit plane, high-bit plane).
+
+    The fp16 d plane (2 bytes per super-block) starts at 0; each later plane
+    starts at the previous plane's end rounded up to 256 bytes.
+    """
+    ns = cols // 256
+    so = (2 * rows * ns + 255) // 256 * 256
+    lo = (so + 16 * rows * ns + 255) // 256 * 256
+    hi = (lo + 64 * rows * ns + 255) // 256 * 256
+    return so, lo, hi
+
+
+def q3_k_fields(buf, rows: int, cols: int, row_start: int = 0, row_count=None):
+    """Decode Q3_K records into (d, S[16], Q[16][16]) per record.
+
+    S_s is the low six bits of scale byte s.  Q = low | high << 2: the low
+    two bits as in Q2_K (weight i of sub-block s at bits 2 (i // 4) of byte
+    4s + i % 4 of the record's 64), the high bit at bit 4 (s % 2) + i // 4 of
+    byte 4 (s // 2) + i % 4 of the record's 32.
+    """
+    if cols % 256:
+        raise ValueError("Q3_K needs cols % 256 == 0")
+    r0, n = _rows(rows, row_start, row_count)
+    buf = np.asarray(buf, dtype=np.uint8)
+    ns = cols // 256
+    a, b = r0 * ns, (r0 + n) * ns
+    so, lo, hi = q3_k_offsets(rows, cols)
+    db = buf[2 * a: 2 * b].reshape(b - a, 2).astype(np.int64)
+    d = f16_to_f64(db[:, 0] | (db[:, 1] << 8))
+    S = buf[so + 16 * a: so + 16 * b].reshape(b - a, 16).astype(np.int64) & 63
+    lb = buf[lo + 64 * a: lo + 64 * b].reshape(b - a, 16, 4).astype(np.int64)
+    hb = buf[hi + 32 * a: hi + 32 * b].reshape(b - a, 8, 4).astype(np.int64)
+    Q = np.empty((b - a, 16, 16), dtype=np.int64)
+    for s in range(16):
+        for i in range(16):
+            low = (lb[:, s, i % 4] >> (2 * (i // 4))) & 3
+            high = (hb[:, s // 2, i % 4] >> (4 * (s % 2) + i // 4)) & 1
+            Q[:, s, i] = low | (high << 2)
+    return d, S, Q
+
+
+def dequant_q3_k(buf, rows: int, cols: int, row_start: int = 0, row_count=None) -> np.ndarray:
+    """Planar Q3_K -> float64 [row_count][cols].
+
+    256-weight super-block, 16 sub-blocks of 16: w = d*(S_s - 32)*(Q - 4).
+    """
+    r0, n = _rows(rows, row_start, row_count)
+    d, S, Q = q3_k_fields(buf, rows, cols, r0, n)
+    w = d[:, None, None] * (S[:, :, None] - 32).astype(np.float64) * (Q - 4).astype(np.float64)
+    return w.reshape(n, cols)
+
+
 def dequant(dtype: str, buf, rows: int, cols: int, row_start: int = 0, row_count=None) -> np.ndarray:
     if dtype == "q8_0":
         return dequant_q8_0(buf, rows, cols, row_start, row_count)
@@ -198,6 +254,8 @@ def dequant(dtype: str, buf, rows: int, cols: int, row_start: int = 0, row_count
         return dequant_q4_k(buf, rows, cols, row_start, row_count)
     if dtype == "q2_k":
         return dequant_q2_k(buf, rows, cols, row_start, row_count)
+    if dtype == "q3_k":
+        return dequant_q3_k(buf, rows, cols, row_start, row_count)
     if dtype == "f32":
         r0, n = _rows(rows, row_start, row_count)
         a = np.asarray(buf).view(np.float32).reshape(rows, cols)
@@ -291,11 +349,12 @@ def swiglu_ffn(Wg, Wu, Wd, xs) -> np.ndarray:
 
 def moe_layer(x, router, gate, up, down, *, top_k: int, ffn: int, expert_type: str,
               shared=None, shared_ffn: int = 0, shared_type: str = "q8_0",
-              tokens=None) -> dict:
+              tokens=None, down_type=None) -> dict:
     """The routed-MoE layer on x [M][H] (float32 input), in float64.
 
-    ``gate``/``up`` are stacked E*F x H tensors, ``down`` E*H x F, in the
-    planar layout of ``expert_type``; ``shared`` is (gate, up, down) of the
+    ``gate``/``up`` are stacked E*F x H tensors in the planar layout of
+    ``expert_type``, ``down`` E*H x F in that of ``down_type`` (None: the
+    same); ``shared`` is (gate, up, down) of the
     shared expert (Fs x H, Fs x H, H x Fs) or None.  ``tokens`` restricts
     the FFN part to a subset of tokens (routing is always computed for all).
     Returns the routing of ``route`` plus y [len(tokens)][H].
@@ -325,7 +384,7 @@ def moe_layer(x, router, gate, up, down, *, top_k: int, ffn: int, expert_type: s
     for e in sorted(need):
         Wg = dequant(expert_type, gate, E * F, H, e * F, F)
         Wu = dequant(expert_type, up, E * F, H, e * F, F)
-        Wd = dequant(expert_type, down, E * H, F, e * H, H)
+        Wd = dequant(down_type or expert_type, down, E * H, F, e * H, H)
         pairs = need[e]
         out = swiglu_ffn(Wg, Wu, Wd, X[[toks[ti] for ti, _ in pairs]])
         for (ti, j), row in zip(pairs, out):

@@ -5,8 +5,10 @@ the vectorised oracle on tiny shapes.  It shares no code with
 ``moe_oracle.py``: fp16 is decoded with Python's ``struct`` half-precision
 codec, the Q4_K scale/min fields are cut from one Python integer holding the
 96-bit stream, a Q2_K quant is cut from the little-endian integer of its
-sub-block's four bytes (weight i at bit 8 (i % 4) + 2 (i // 4)), and every
-product is an explicit loop over Python floats.
+sub-block's four bytes (weight i at bit 8 (i % 4) + 2 (i // 4)), a Q3_K
+high bit from the integer of its sub-block pair's four bytes (bit
+8 (i % 4) + 4 (s % 2) + i // 4), and every product is an explicit loop over
+Python floats.
 Meant for hidden sizes of a few hundred and a handful of experts.
 """
 
@@ -63,7 +65,24 @@ def weight_q2_k(buf, rows: int, cols: int, r: int, c: int) -> float:
     return d * (sbyte % 16) * q - dmin * (sbyte // 16)
 
 
-_WEIGHT = {"q8_0": weight_q8_0, "q4_k": weight_q4_k, "q2_k": weight_q2_k}
+def weight_q3_k(buf, rows: int, cols: int, r: int, c: int) -> float:
+    ns = cols // 256
+    rec = r * ns + c // 256
+    s, i = (c % 256) // 16, c % 16
+    d = _f16(int(buf[2 * rec]), int(buf[2 * rec + 1]))
+    sbase = -(-2 * rows * ns // 256) * 256
+    lbase = -(-(sbase + 16 * rows * ns) // 256) * 256
+    hbase = -(-(lbase + 64 * rows * ns) // 256) * 256
+    scale = int(buf[sbase + 16 * rec + s]) % 64 - 32
+    lw = int.from_bytes(bytes(int(v) for v in buf[lbase + 64 * rec + 4 * s: lbase + 64 * rec + 4 * s + 4]),
+                        "little")
+    hw = int.from_bytes(bytes(int(v) for v in buf[hbase + 32 * rec + 4 * (s // 2):
+                                                   hbase + 32 * rec + 4 * (s // 2) + 4]), "little")
+    q = ((lw >> (8 * (i % 4) + 2 * (i // 4))) & 3) + 4 * ((hw >> (8 * (i % 4) + 4 * (s % 2) + i // 4)) & 1)
+    return d * scale * (q - 4)
+
+
+_WEIGHT = {"q8_0": weight_q8_0, "q4_k": weight_q4_k, "q2_k": weight_q2_k, "q3_k": weight_q3_k}
 
 
 def weight(dtype: str, buf, rows: int, cols: int, r: int, c: int) -> float:
@@ -80,15 +99,15 @@ def _matvec(dtype, buf, rows, cols, row0, nrows, v):
     return out
 
 
-def _ffn(dtype, g_buf, u_buf, d_buf, rows_gu, rows_d, g_row0, d_row0, F, H, x):
+def _ffn(dtype, g_buf, u_buf, d_buf, rows_gu, rows_d, g_row0, d_row0, F, H, x, ddtype=None):
     g = _matvec(dtype, g_buf, rows_gu, H, g_row0, F, x)
     u = _matvec(dtype, u_buf, rows_gu, H, g_row0, F, x)
     h = [gi / (1.0 + math.exp(-gi)) * ui for gi, ui in zip(g, u)]
-    return _matvec(dtype, d_buf, rows_d, F, d_row0, H, h)
+    return _matvec(ddtype or dtype, d_buf, rows_d, F, d_row0, H, h)
 
 
 def moe_layer(x, router, gate, up, down, *, top_k, ffn, expert_type,
-              shared=None, shared_ffn=0, shared_type="q8_0"):
+              shared=None, shared_ffn=0, shared_type="q8_0", down_type=None):
     """Returns (y, ids, w) with y a list of lists of floats."""
     E = len(router)
     H = len(router[0])
@@ -124,7 +143,7 @@ def moe_layer(x, router, gate, up, down, *, top_k, ffn, expert_type,
                      0, 0, shared_ffn, H, xt)
             y = [a + b for a, b in zip(y, s)]
         for j, e in enumerate(chosen):
-            o = _ffn(expert_type, gate, up, down, E * F, E * H, e * F, e * H, F, H, xt)
+            o = _ffn(expert_type, gate, up, down, E * F, E * H, e * F, e * H, F, H, xt, down_type)
             y = [a + w[j] * b for a, b in zip(y, o)]
         ys.append(y)
         all_ids.append(chosen)

@@ -18,8 +18,8 @@ import torch  # load torch first: the library then binds to torch's HIP runtime
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "lib", "libsvr_moe.so")
 
-F32, Q8_0, Q4_K, Q2_K = 0, 1, 2, 3
-_DTYPES = {"f32": F32, "q8_0": Q8_0, "q4_k": Q4_K, "q2_k": Q2_K}
+F32, Q8_0, Q4_K, Q2_K, Q3_K = 0, 1, 2, 3, 4
+_DTYPES = {"f32": F32, "q8_0": Q8_0, "q4_k": Q4_K, "q2_k": Q2_K, "q3_k": Q3_K}
 
 OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_WORKSPACE, ERR_LAUNCH, ERR_ARG = range(7)
 
@@ -37,7 +37,8 @@ class _Desc(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("n_experts", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("ffn", ctypes.c_int32),
                 ("shared_ffn", ctypes.c_int32), ("expert_type", ctypes.c_int32),
-                ("shared_type", ctypes.c_int32), ("flags", ctypes.c_int32)]
+                ("shared_type", ctypes.c_int32), ("flags", ctypes.c_int32),
+                ("down_type", ctypes.c_int32)]
 
 
 class _Weights(ctypes.Structure):
@@ -56,11 +57,13 @@ class LayerDesc:
     expert_type: str = "q4_k"
     shared_type: str = "q8_0"
     single_launch: bool = False  # MOE_SINGLE_LAUNCH
+    down_type: Optional[str] = None  # routed down; None: expert_type
 
     def c(self) -> _Desc:
         return _Desc(self.hidden, self.n_experts, self.top_k, self.ffn, self.shared_ffn,
                      _DTYPES[self.expert_type], _DTYPES[self.shared_type],
-                     SINGLE_LAUNCH if self.single_launch else 0)
+                     SINGLE_LAUNCH if self.single_launch else 0,
+                     _DTYPES[self.down_type] if self.down_type else 0)
 
 
 @dataclasses.dataclass

@@ -146,6 +146,11 @@ __device__ __forceinline__ uint32_t bload2(__amdgpu_buffer_rsrc_t r, uint32_t of
 __device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+  return make_uint2(v.x, v.y);
+}
 // 16-byte load that reads past the per-XCD L2 (sc1), for data another
 // workgroup of the same launch wrote with store_shared.
 typedef float f32x4 __attribute__((ext_vector_type(4)));

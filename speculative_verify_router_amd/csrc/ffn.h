@@ -1,6 +1,6 @@
 // Fused dequantise-and-multiply skinny GEMM for the expert FFNs.
 //
-// Routed gate/up/down are Q4_K, Q2_K or Q8_0 and the shared expert Q8_0
+// Routed gate/up/down are Q4_K, Q2_K, Q3_K or Q8_0 and the shared expert Q8_0
 // ("Step 3.7 Flash Mixed-Quant GGUF", Tensor recipe; "Step-5 Preview GGUF",
 // Precision distribution table and Tensor-type table).  At a verify batch of four tokens with 8
 // of 288-352 experts each, an expert serves about one token, so this is an
@@ -9,7 +9,8 @@
 //
 // Mapping.  A 16-byte chunk of the quant plane is the unit of loading:
 // 16 weights for Q8_0, one 32-weight sub-block for Q4_K, four 16-weight
-// sub-blocks for Q2_K.  A row of K
+// sub-blocks for Q2_K and Q3_K (low bits; the high bits come from a plane
+// of their own).  A row of K
 // columns has K / kWpc chunks, covered by a group of `lpr` consecutive
 // lanes (lpr | 64), lane j of the group taking chunks j, j+lpr, ...,
 // j+(CPL-1)*lpr.  A wave works on 64/lpr rows at once and every wave load
@@ -72,7 +73,9 @@ constexpr int tp_for(int fmt, int cpl) {
 #define SVR_RING_VGPRS 100
 #endif
 constexpr int kRingVgprs = SVR_RING_VGPRS;
-constexpr int chunk_vgprs(int fmt) { return fmt == kQ8_0 ? 5 : fmt == kQ4_K ? 8 : 6; }
+constexpr int chunk_vgprs(int fmt) {
+  return fmt == kQ8_0 ? 5 : fmt == kQ4_K ? 8 : fmt == kQ2_K ? 6 : 8;
+}
 constexpr int nst_for(int fmt, int cpl, bool gateup) {
   return (cpl * (gateup ? 2 : 1) * chunk_vgprs(fmt) * 5 <= kRingVgprs)   ? 5
          : (cpl * (gateup ? 2 : 1) * chunk_vgprs(fmt) * 4 <= kRingVgprs) ? 4

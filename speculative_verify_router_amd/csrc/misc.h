@@ -30,7 +30,8 @@ __global__ __launch_bounds__(kBlock) void k_combine(const float* __restrict__ o,
 
 // Dequantise rows [r0, r0 + n) of a planar tensor into out[n][cols].
 // Q8_0: d*q.  Q4_K and Q2_K: fma(d*sc, q, -(dmin*m)); d*sc and dmin*m are
-// exact in fp32, so the result is the correctly rounded block value.
+// exact in fp32, so the result is the correctly rounded block value.  Q3_K:
+// (d*(S-32))*(Q-4), exact (at most 20 significant bits).
 __global__ __launch_bounds__(kBlock) void k_dequant(int fmt, const uint8_t* __restrict__ base,
                                                     int64_t rows, int cols, int64_t r0, int64_t n,
                                                     float* __restrict__ out) {
@@ -59,6 +60,18 @@ __global__ __launch_bounds__(kBlock) void k_dequant(int fmt, const uint8_t* __re
       const uint32_t qb = base[qoff + 64 * rec + 4 * s + (wi & 3)];
       const float q = (float)((qb >> (2 * (wi >> 2))) & 3u);
       v = fmaf(d * (float)(sm & 15u), q, -(dmin * (float)(sm >> 4)));
+    } else if (fmt == MOE_Q3_K) {
+      const int64_t n_sb = rows * (cols >> 8);
+      const int64_t soff = (2 * n_sb + 255) & ~(int64_t)255;
+      const int64_t loff = (soff + 16 * n_sb + 255) & ~(int64_t)255;
+      const int64_t hoff = (loff + 64 * n_sb + 255) & ~(int64_t)255;
+      const int64_t rec = r * (cols >> 8) + (c >> 8);
+      const float d = f16_to_f32((uint32_t)base[2 * rec] | ((uint32_t)base[2 * rec + 1] << 8));
+      const int s = (c >> 4) & 15, wi = c & 15;
+      const int S = (int)(base[soff + 16 * rec + s] & 63u) - 32;
+      const uint32_t lo = (base[loff + 64 * rec + 4 * s + (wi & 3)] >> (2 * (wi >> 2))) & 3u;
+      const uint32_t hi = (base[hoff + 32 * rec + 4 * (s >> 1) + (wi & 3)] >> (4 * (s & 1) + (wi >> 2))) & 1u;
+      v = (d * (float)S) * (float)((int)(lo | (hi << 2)) - 4);
     } else {
       const int64_t ns = cols >> 8;
       const int64_t rec = r * ns + (c >> 8);

@@ -39,7 +39,7 @@ using namespace svr;
 
 namespace {
 
-constexpr int kVersion = 300;  // 0.3.0
+constexpr int kVersion = 400;  // 0.4.0
 constexpr int kFusedMaxTokens = 16;
 // Batches up to this size give every (token, slot) pair its own workgroups
 // (equal work per workgroup); larger ones go by expert with token passes.
@@ -58,14 +58,17 @@ inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 int wpc_of(int dtype) { return dtype == MOE_Q8_0 ? 16 : dtype == MOE_Q4_K ? 32 : 64; }
 int blk_of(int dtype) { return dtype == MOE_Q8_0 ? 32 : 256; }
-// Types of the shared expert, and of the routed experts (also Q2_K).
+// Types of the shared expert, and of the routed experts (also Q2_K, Q3_K).
 bool quant_type(int dtype) { return dtype == MOE_Q8_0 || dtype == MOE_Q4_K; }
-bool routed_type(int dtype) { return quant_type(dtype) || dtype == MOE_Q2_K; }
-int qfmt(int dtype) { return dtype == MOE_Q8_0 ? kQ8_0 : dtype == MOE_Q4_K ? kQ4_K : kQ2_K; }
+bool low_bit_type(int dtype) { return dtype == MOE_Q2_K || dtype == MOE_Q3_K; }
+bool routed_type(int dtype) { return quant_type(dtype) || low_bit_type(dtype); }
+int qfmt(int dtype) {
+  return dtype == MOE_Q8_0 ? kQ8_0 : dtype == MOE_Q4_K ? kQ4_K : dtype == MOE_Q2_K ? kQ2_K : kQ3_K;
+}
 
 // Lanes per row and 16-byte chunks per lane for a row of K columns.  The
 // shape keeps the per-lane activation slice within 96 floats (Q4_K: 3
-// chunks of 32, Q8_0: 6 chunks of 16, Q2_K: 1 chunk of 64) where possible and wastes the fewest
+// chunks of 32, Q8_0: 6 chunks of 16, Q2_K and Q3_K: 1 chunk of 64) where possible and wastes the fewest
 // lane positions (chunk positions past the row's end load the row's last
 // chunk against a zero activation); among equal shapes the fewest chunks
 // per lane.  Rows too long for that take 64 lanes and up to 8 chunks.
@@ -75,7 +78,7 @@ struct FfnShape {
 bool ffn_shape(int dtype, int K, FfnShape* s) {
   if (K <= 0 || K % blk_of(dtype)) return false;
   const int chunks = K / wpc_of(dtype);
-  const int cap = dtype == MOE_Q8_0 ? 6 : dtype == MOE_Q4_K ? 3 : 1;
+  const int cap = 96 / wpc_of(dtype);
   double best = 0.0;
   for (int lpr = 64; lpr >= 1; lpr >>= 1) {
     const int cpl = (chunks + lpr - 1) / lpr;
@@ -96,7 +99,7 @@ bool ffn_shape(int dtype, int K, FfnShape* s) {
 }
 
 struct Plan {
-  int H, E, k, F, Fs, et, st, M, flags;
+  int H, E, k, F, Fs, et, st, dt, M, flags;  // dt: routed down type
   size_t ctr, logits, ids, w, counts, offsets, slots, active, nactive, h, hs, o, s, xs, tiles,
       total;
   int tiles_cap;  // routed token tiles of the batched path, at most
@@ -108,11 +111,13 @@ int check_desc(const moe_layer_desc* d) {
     return MOE_ERR_SHAPE;
   if (d->flags & ~MOE_SINGLE_LAUNCH) return MOE_ERR_ARG;
   if (!routed_type(d->expert_type)) return MOE_ERR_DTYPE;
+  if (d->down_type != 0 && !routed_type(d->down_type)) return MOE_ERR_DTYPE;
   if (d->shared_ffn > 0 && !quant_type(d->shared_type)) return MOE_ERR_DTYPE;
   if (d->n_experts > kMaxExperts) return MOE_ERR_SHAPE;
   if (d->top_k > d->n_experts || d->top_k > kMaxTopK) return MOE_ERR_SHAPE;
   FfnShape s;
-  if (!ffn_shape(d->expert_type, d->hidden, &s) || !ffn_shape(d->expert_type, d->ffn, &s))
+  const int dt = d->down_type ? d->down_type : d->expert_type;
+  if (!ffn_shape(d->expert_type, d->hidden, &s) || !ffn_shape(dt, d->ffn, &s))
     return MOE_ERR_SHAPE;
   if (d->shared_ffn > 0 &&
       (!ffn_shape(d->shared_type, d->hidden, &s) || !ffn_shape(d->shared_type, d->shared_ffn, &s)))
@@ -130,6 +135,7 @@ int make_plan(const moe_layer_desc* d, int M, Plan* p) {
   p->F = d->ffn;
   p->Fs = d->shared_ffn;
   p->et = d->expert_type;
+  p->dt = d->down_type ? d->down_type : d->expert_type;
   p->st = d->shared_type;
   p->flags = d->flags;
   p->M = M;
@@ -246,7 +252,8 @@ int tiles_of(const FfnArgs& a) {
 
 // Bytes per weight row of K columns.
 double row_bytes(int dtype, int K) {
-  return dtype == MOE_Q8_0 ? K / 32 * 34.0 : K / 256 * (dtype == MOE_Q4_K ? 144.0 : 84.0);
+  if (dtype == MOE_Q8_0) return K / 32 * 34.0;
+  return K / 256 * (dtype == MOE_Q4_K ? 144.0 : dtype == MOE_Q2_K ? 84.0 : 114.0);
 }
 
 // Single-role launches, every (format, chunks-per-lane) pair.
@@ -275,6 +282,9 @@ bool launch_ffn(int dtype, bool gateup, FfnArgs a, int slots_max, hipStream_t st
   if (dtype == MOE_Q2_K)
     return gateup ? launch_ffn_c<kQ2_K, true>(s.cpl, a, dtype, slots_max, st)
                   : launch_ffn_c<kQ2_K, false>(s.cpl, a, dtype, slots_max, st);
+  if (dtype == MOE_Q3_K)
+    return gateup ? launch_ffn_c<kQ3_K, true>(s.cpl, a, dtype, slots_max, st)
+                  : launch_ffn_c<kQ3_K, false>(s.cpl, a, dtype, slots_max, st);
   return gateup ? launch_ffn_c<kQ4_K, true>(s.cpl, a, dtype, slots_max, st)
                 : launch_ffn_c<kQ4_K, false>(s.cpl, a, dtype, slots_max, st);
 }
@@ -365,6 +375,7 @@ bool launch_dual_keys(int akey, int bkey, hipStream_t st, const FfnArgs& a, cons
   SVR_D(kQ8_0, 4, 64, kQ8_0, 5, 16) SVR_D(kQ8_0, 4, 64, kQ8_0, 3, 32)
   SVR_D(kQ2_K, 1, 64, kQ8_0, 5, 16) SVR_D(kQ2_K, 1, 64, kQ8_0, 3, 32)
   SVR_DG(kQ4_K, 1) SVR_DG(kQ4_K, 2) SVR_DG(kQ4_K, 3) SVR_DG(kQ8_0, 4) SVR_DG(kQ2_K, 1)
+  SVR_DG(kQ3_K, 1)
 #undef SVR_DG
 #undef SVR_D
   return false;
@@ -409,7 +420,8 @@ bool launch_down_tok(int dtype, const FfnShape& ds, hipStream_t st, const FfnArg
     SVR_DT(kQ4_K, 3, 16) SVR_DT(kQ8_0, 5, 16) SVR_DT(kQ8_0, 3, 32)
     SVR_DT(kQ4_K, 1, 0) SVR_DT(kQ4_K, 2, 0) SVR_DT(kQ4_K, 3, 0) SVR_DT(kQ8_0, 1, 0)
     SVR_DT(kQ8_0, 2, 0) SVR_DT(kQ8_0, 3, 0) SVR_DT(kQ8_0, 4, 0) SVR_DT(kQ8_0, 5, 0)
-    SVR_DT(kQ8_0, 6, 0) SVR_DT(kQ2_K, 1, 32) SVR_DT(kQ2_K, 1, 0) SVR_DT(kQ2_K, 2, 0)
+    SVR_DT(kQ8_0, 6, 0) SVR_DT(kQ2_K, 1, 32) SVR_DT(kQ2_K, 1, 0) SVR_DT(kQ3_K, 1, 32)
+    SVR_DT(kQ3_K, 1, 0)
   }
 #undef SVR_DT
   return false;
@@ -433,7 +445,7 @@ bool launch_down_combine_key(int k, hipStream_t st, const FfnArgs& a, const Comb
   SVR_DC(kQ4_K, 3, 16) SVR_DC(kQ8_0, 5, 16)
   SVR_DC(kQ4_K, 1, 0) SVR_DC(kQ4_K, 2, 0) SVR_DC(kQ4_K, 3, 0) SVR_DC(kQ8_0, 1, 0) SVR_DC(kQ8_0, 2, 0)
   SVR_DC(kQ8_0, 3, 0) SVR_DC(kQ8_0, 4, 0) SVR_DC(kQ8_0, 5, 0) SVR_DC(kQ8_0, 6, 0)
-  SVR_DC(kQ2_K, 1, 32) SVR_DC(kQ2_K, 1, 0) SVR_DC(kQ2_K, 2, 0)
+  SVR_DC(kQ2_K, 1, 32) SVR_DC(kQ2_K, 1, 0) SVR_DC(kQ3_K, 1, 32) SVR_DC(kQ3_K, 1, 0)
 #undef SVR_DC
   return false;
 }
@@ -460,6 +472,7 @@ struct FlowKey {
 bool flow_key(const Plan& p, FlowKey* k) {
   if (!(p.flags & MOE_SINGLE_LAUNCH)) return false;
   if (p.M < 1 || p.M > kFlowTokens || p.M * p.k > kFlowMaxPairs) return false;
+  if (p.dt != p.et) return false;
   FfnShape a{}, b{};
   if (!(k->nc = router_nc(p.H))) return false;
   if (!ffn_shape(p.et, p.H, &a) || !ffn_shape(p.et, p.F, &b)) return false;
@@ -728,7 +741,9 @@ const char* const kGemmStageNames[kGemmStages] = {"route", "shared_gateup", "gat
 
 bool gemm_path(const Plan& p) {
   if (p.M <= kFusedMaxTokens) return false;
-  if (p.et == MOE_Q2_K) return false;  // no matrix-core decoder for this type
+  // no matrix-core decoder for the 2- and 3-bit types
+  if (low_bit_type(p.et) || low_bit_type(p.dt)) return false;
+  if (p.dt != p.et) return false;  // the down GEMMs decode the gate/up type
   // Split activations and h are addressed with 32-bit byte offsets.
   const int64_t P = (int64_t)p.M * p.k;
   if (P * std::max(p.H, p.F) * 4 >= (1ll << 31)) return false;
@@ -948,13 +963,13 @@ int forward_impl(const moe_layer_desc* desc, const moe_layer_weights* wt, const 
     FfnArgs rd = routed_args(p, b, false, wt, x, pairs);
     rd.coherent_out = 1;  // the last workgroup of each row tile reads them
     FfnShape ds;
-    ffn_shape(p.et, p.F, &ds);
+    ffn_shape(p.dt, p.F, &ds);
     CombineArgs c{b.o, shared ? b.s : nullptr, b.w, y, p.M, p.H, p.k, b.ctr};
-    if (pairs && launch_down_tok(p.et, ds, st, rd, c)) {
+    if (pairs && launch_down_tok(p.dt, ds, st, rd, c)) {
       // one workgroup per (token, row tile), combined in LDS
-    } else if (!launch_down_combine(p.et, ds, st, rd, c, slots_max)) {
+    } else if (!launch_down_combine(p.dt, ds, st, rd, c, slots_max)) {
       rd.coherent_out = 0;
-      if (!launch_ffn(p.et, false, rd, slots_max, st)) return MOE_ERR_SHAPE;
+      if (!launch_ffn(p.dt, false, rd, slots_max, st)) return MOE_ERR_SHAPE;
       const int64_t n4 = (int64_t)p.M * (p.H / 4);
       hipLaunchKernelGGL(k_combine, dim3((unsigned)((n4 + kBlock - 1) / kBlock)), dim3(kBlock), 0,
                          st, b.o, shared ? b.s : nullptr, b.w, y, p.M, p.H, p.k);
@@ -1001,6 +1016,14 @@ int32_t moe_tensor_bytes(int32_t dtype, int64_t rows, int64_t cols, int64_t* byt
       const int64_t n = rows * (cols / 256);
       const int64_t s = (int64_t)align256((size_t)(4 * n));
       *bytes = (int64_t)align256((size_t)(s + 16 * n)) + 64 * n;
+      return MOE_OK;
+    }
+    case MOE_Q3_K: {
+      if (cols % 256) return MOE_ERR_SHAPE;
+      const int64_t n = rows * (cols / 256);
+      const int64_t s = (int64_t)align256((size_t)(2 * n));
+      const int64_t l = (int64_t)align256((size_t)(s + 16 * n));
+      *bytes = (int64_t)align256((size_t)(l + 64 * n)) + 32 * n;
       return MOE_OK;
     }
     default: return MOE_ERR_DTYPE;

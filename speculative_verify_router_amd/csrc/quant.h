@@ -1,18 +1,23 @@
-// Planar Q8_0 / Q4_K / Q2_K blocks: 16-byte chunk loads, scale decoding and
-// the fused dequantise-and-dot of one chunk against 16-bit activations.
+// Planar Q8_0 / Q4_K / Q2_K / Q3_K blocks: 16-byte chunk loads, scale
+// decoding and the fused dequantise-and-dot of one chunk against 16-bit
+// activations.
 //
 // Formats (include/moe_layer.h): Q8_0 blocks of 32 int8 with an fp16 scale
 // d, w = d*q; Q4_K super-blocks of 256 with fp16 d, dmin and per-32 6-bit
 // sc, m, 4-bit q, w = d*sc*q - dmin*m; Q2_K super-blocks of 256 with fp16
-// d, dmin and per-16 4-bit sc, m, 2-bit q, the same rule ("Step-5 Preview
-// GGUF" and "Step 3.7 Flash Mixed-Quant GGUF" name these tensor types;
-// their bit layouts are this library's).
+// d, dmin and per-16 4-bit sc, m, 2-bit q, the same rule; Q3_K
+// super-blocks of 256 with fp16 d and per-16 6-bit S, 3-bit Q,
+// w = d*(S-32)*(Q-4) ("Step-5 Preview GGUF" and "Step 3.7 Flash Mixed-Quant
+// GGUF" name these tensor types; their bit layouts are this library's).
 //
 // Dot product.  The weights' integer quants go into v_dot4_i32_i8 as they
 // are: a Q8_0 quant dword is four int8 weights; a Q4_K dword (8 nibbles,
 // weights 2b / 2b+1 in the low / high nibble of byte b) gives the even
-// weights with one AND and the odd ones with a shift and an AND.  The
-// activations enter as 16-bit integers in two int8 limbs (XSlice below),
+// weights with one AND and the odd ones with a shift and an AND; a Q2_K
+// dword is one 16-weight sub-block whose four 2-bit planes (weights
+// 4j..4j+3 in bits 2j of each byte) come out with a shift and an AND each,
+// and Q3_K adds each plane's high bits with one more shift and an AND-OR.
+// The activations enter as 16-bit integers in two int8 limbs (XSlice below),
 // so each chunk's dot product is exact in int32 and the block scales are
 // applied once per chunk in fp32.
 #pragma once
@@ -21,7 +26,7 @@
 
 namespace svr {
 
-enum QFmt { kQ8_0 = 1, kQ4_K = 2, kQ2_K = 3 };
+enum QFmt { kQ8_0 = 1, kQ4_K = 2, kQ2_K = 3, kQ3_K = 4 };
 
 template <int FMT>
 struct QTraits;
@@ -37,15 +42,21 @@ template <>
 struct QTraits<kQ2_K> {
   static constexpr int kWpc = 64;  // four 16-weight sub-blocks
 };
+template <>
+struct QTraits<kQ3_K> {
+  static constexpr int kWpc = 64;
+};
 
 // The planes of one expert's rows of a stacked planar tensor, as buffer
 // resources (32-bit offsets; reads past the expert's rows return zero).
 // Every format carries K/16 bytes of scale data per row in plane s: Q8_0
 // K/32 fp16 scales, Q4_K K/256 headers of 16 bytes, Q2_K K/256 records of
 // 16 scale bytes.  Q2_K keeps d and dmin in a third plane d of K/64 bytes
-// per row, so a row's offset there is its plane-s offset / 4.
+// per row, so a row's offset there is its plane-s offset / 4.  Q3_K keeps
+// fp16 d in plane d (K/128 bytes per row: offset / 8), its low quant bits
+// in plane q and its high bits in plane h (K/8 bytes per row: offset * 2).
 struct QPlanes {
-  __amdgpu_buffer_rsrc_t q, s, d;
+  __amdgpu_buffer_rsrc_t q, s, d, h;
   uint32_t qrow, srow;  // bytes per row in planes q and s
 };
 
@@ -58,18 +69,28 @@ __device__ __forceinline__ QPlanes expert_planes(const uint8_t* base, int64_t to
   p.srow = (uint32_t)(K >> 4);
   p.qrow = (FMT == kQ8_0) ? (uint32_t)K : (FMT == kQ4_K) ? (uint32_t)(K >> 1) : (uint32_t)(K >> 2);
   const int64_t sbytes = total_rows * (int64_t)p.srow;
-  if constexpr (FMT == kQ2_K) {
+  if constexpr (FMT == kQ3_K) {
+    const uint32_t drow = (uint32_t)(K >> 7), hrow = (uint32_t)(K >> 3);
+    const int64_t sstart = round256(total_rows * (int64_t)drow);
+    const int64_t qstart = round256(sstart + sbytes);
+    const int64_t hstart = round256(qstart + total_rows * (int64_t)p.qrow);
+    p.d = make_rsrc(base + row0 * drow, (uint32_t)rows * drow);
+    p.s = make_rsrc(base + sstart + row0 * p.srow, (uint32_t)rows * p.srow);
+    p.q = make_rsrc(base + qstart + row0 * p.qrow, (uint32_t)rows * p.qrow);
+    p.h = make_rsrc(base + hstart + row0 * hrow, (uint32_t)rows * hrow);
+  } else if constexpr (FMT == kQ2_K) {
     const uint32_t drow = (uint32_t)(K >> 6);
     const int64_t sstart = round256(total_rows * (int64_t)drow);
     const int64_t qstart = round256(sstart + sbytes);
     p.d = make_rsrc(base + row0 * drow, (uint32_t)rows * drow);
     p.s = make_rsrc(base + sstart + row0 * p.srow, (uint32_t)rows * p.srow);
     p.q = make_rsrc(base + qstart + row0 * p.qrow, (uint32_t)rows * p.qrow);
+    p.h = p.s;
   } else {
     const int64_t qstart = (FMT == kQ8_0) ? round256(sbytes) : sbytes;
     p.s = make_rsrc(base + row0 * p.srow, (uint32_t)rows * p.srow);
     p.q = make_rsrc(base + qstart + row0 * p.qrow, (uint32_t)rows * p.qrow);
-    p.d = p.s;
+    p.d = p.h = p.s;
   }
   return p;
 }
@@ -92,6 +113,13 @@ struct Chunk<kQ2_K> {
   uint32_t sc;   // byte k: that sub-block's sc | m << 4
   uint32_t dd;   // d | dmin << 16
 };
+template <>
+struct Chunk<kQ3_K> {
+  uint4 q;       // low two bits; dword k: sub-block 4 (c % 4) + k
+  uint2 hb;      // high bits; dword t: sub-blocks 2t (low nibbles), 2t + 1
+  uint32_t sc;   // byte k: S of sub-block k
+  uint32_t d;    // fp16 d (low half)
+};
 
 // Chunk c of a row whose plane offsets are qo = row * qrow and so = row * srow.
 __device__ __forceinline__ void load_chunk(Chunk<kQ8_0>& ch, const QPlanes& p, uint32_t qo,
@@ -109,6 +137,13 @@ __device__ __forceinline__ void load_chunk(Chunk<kQ2_K>& ch, const QPlanes& p, u
   ch.q = bload16(p.q, qo + 16u * c);
   ch.sc = bload4(p.s, so + 4u * c);
   ch.dd = bload4(p.d, (so >> 2) + 4u * (c >> 2));
+}
+__device__ __forceinline__ void load_chunk(Chunk<kQ3_K>& ch, const QPlanes& p, uint32_t qo,
+                                           uint32_t so, int c) {
+  ch.q = bload16(p.q, qo + 16u * c);
+  ch.hb = bload8(p.h, 2u * so + 8u * c);
+  ch.sc = bload4(p.s, so + 4u * c);
+  ch.d = bload2(p.d, (so >> 3) + 2u * (c >> 2));
 }
 
 // Activations of one chunk position for one token, as 16-bit integers.
@@ -145,6 +180,12 @@ struct XSlice<kQ2_K> {
   uint32_t h[16], l[16];  // dword 4k + j: limbs of weights 16k + 4j .. 16k + 4j + 3
   float s;
   float sum[4];  // s * (sum of the quantised activations) of sub-block k
+};
+template <>
+struct XSlice<kQ3_K> {
+  uint32_t h[16], l[16];  // as for Q2_K
+  float s;
+  int nsum4[4];  // -4 * (sum of the quantised activations) of sub-block k
 };
 
 constexpr float kQ16Max = 32639.0f;     // |q| bound: hi = (q + 128) >> 8 stays in int8
@@ -198,6 +239,17 @@ __device__ __forceinline__ void quantize_slice(XSlice<FMT>& xs, const float (&v)
       xs.sum[k] = xs.s * (float)(int32_t)(b - 16u * kQ16MagicBits);
     }
     (void)bsum;
+  } else if constexpr (FMT == kQ3_K) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) limbs4(y[4 * k], y[4 * k + 1], y[4 * k + 2], y[4 * k + 3], xs.h[k], xs.l[k]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t b = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) b += __builtin_bit_cast(uint32_t, y[16 * k + i]);
+      xs.nsum4[k] = -4 * (int32_t)(b - 16u * kQ16MagicBits);
+    }
+    (void)bsum;
   } else {
 #pragma unroll
     for (int k = 0; k < 4; ++k) limbs4(y[4 * k], y[4 * k + 1], y[4 * k + 2], y[4 * k + 3], xs.h[k], xs.l[k]);
@@ -244,13 +296,16 @@ __device__ __forceinline__ void load_x_shared(XSlice<FMT>& xs, const float* base
 
 template <int FMT>
 __device__ __forceinline__ void zero_x(XSlice<FMT>& xs) {
-  constexpr int D = FMT == kQ2_K ? 16 : FMT == kQ4_K ? 8 : 4;
+  constexpr int D = (FMT == kQ2_K || FMT == kQ3_K) ? 16 : FMT == kQ4_K ? 8 : 4;
 #pragma unroll
   for (int i = 0; i < D; ++i) xs.h[i] = xs.l[i] = 0u;
   xs.s = 0.f;
   if constexpr (FMT == kQ2_K) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) xs.sum[k] = 0.f;
+  } else if constexpr (FMT == kQ3_K) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) xs.nsum4[k] = 0;
   } else {
     xs.sum = 0.f;
   }
@@ -304,6 +359,11 @@ __device__ __forceinline__ ChunkScale decode_scale(const Chunk<kQ4_K>& ch, int s
 // applied inside chunk_fma).
 __device__ __forceinline__ ChunkScale decode_scale(const Chunk<kQ2_K>& ch, int /*sub*/) {
   return {f16_lo(ch.dd), f16_hi(ch.dd)};
+}
+
+// Q3_K: a = d (the 6-bit scales are applied inside chunk_fma).
+__device__ __forceinline__ ChunkScale decode_scale(const Chunk<kQ3_K>& ch, int /*sub*/) {
+  return {f16_lo(ch.d), 0.f};
 }
 
 // sum_i q_i x16_i over the chunk (exact in int32; converted with at most one
@@ -375,6 +435,37 @@ __device__ __forceinline__ float chunk_fma(const Chunk<kQ2_K>& ch, const ChunkSc
   mn = fmaf((float)((mv >> 16) & 0xFFu), xs.sum[2], mn);
   mn = fmaf((float)(mv >> 24), xs.sum[3], mn);
   return fmaf(k.a, fmaf((float)ah, 256.0f, (float)al) * xs.s, fmaf(-k.b, mn, acc));
+}
+
+// Q3_K: plane j of sub-block k is (w_k >> 2j) & 0x03030303 with the high
+// bits (bit 4 (k % 2) + j of each byte of high dword k / 2) moved to bit 2
+// of each byte, so one v_dot4 per limb takes four 3-bit quants Q.  Per
+// sub-block the exact integer sum of (Q - 4) x16 is 256 H + L - 4 sum x16
+// (|.| <= 16*4*32639 < 2^21), weighted by S - 32 in int32 with 24-bit
+// multiply-adds; contribution = d*s*(that total).
+__device__ __forceinline__ float chunk_fma(const Chunk<kQ3_K>& ch, const ChunkScale& k,
+                                           const XSlice<kQ3_K>& xs, float acc) {
+  const uint32_t w[4] = {ch.q.x, ch.q.y, ch.q.z, ch.q.w};
+  const uint32_t hw[2] = {ch.hb.x, ch.hb.y};
+  const uint32_t sx = ch.sc ^ 0x20202020u;  // S - 32 as a signed 6-bit field
+  int tot = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const uint32_t H = hw[b >> 1];
+    int h = 0, l = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = 4 * (b & 1) + j;
+      const uint32_t hi = (i >= 2 ? (H >> (i - 2)) : (H << (2 - i))) & 0x04040404u;
+      const int p = (int)(((w[b] >> (2 * j)) & 0x03030303u) | hi);
+      h = __builtin_amdgcn_sdot4(p, (int)xs.h[4 * b + j], h, false);
+      l = __builtin_amdgcn_sdot4(p, (int)xs.l[4 * b + j], l, false);
+    }
+    const int dsub = h * 256 + l + xs.nsum4[b];
+    const int sc = __builtin_amdgcn_sbfe((int)sx, 8 * b, 6);
+    tot += __builtin_amdgcn_sbfe(dsub, 0, 24) * sc;
+  }
+  return fmaf(k.a * xs.s, (float)tot, acc);
 }
 
 }  // namespace svr

@@ -17,6 +17,10 @@ from .layers import (  # noqa: F401
     q2_k_bytes,
     q2_k_quant_offset,
     q2_k_scale_offset,
+    q3_k_bytes,
+    q3_k_high_offset,
+    q3_k_low_offset,
+    q3_k_scale_offset,
     q4_k_bytes,
     q4_k_header_bytes,
     q8_0_bytes,

@@ -30,6 +30,13 @@ Byte layouts (planar block quantisation) are those documented in
   up to 256) R*ns 64-byte quant records, sub-block s (16 weights) in bytes
   [4s, 4s+4) and weight i of it in byte i % 4, bits [2 (i // 4), 2 (i // 4) + 2).
   W = d * sc_s * q - dmin * m_s.
+* Q3_K, R rows x K columns, K % 256 == 0, ns = K / 256: a plane of R*ns fp16
+  d at byte 0; at ``q3_k_scale_offset`` (rounded up to 256) R*ns 16-byte
+  scale records, byte s = S_s (6 bits); at ``q3_k_low_offset`` the low two
+  bits of every quant, 64 bytes per record laid out as the Q2_K quants; at
+  ``q3_k_high_offset`` the high bit of every quant, 32 bytes per record,
+  weight i of sub-block s in byte 4 (s // 2) + i % 4, bit 4 (s % 2) + i // 4.
+  W = d * (S_s - 32) * (Q - 4) with Q = low | high << 2.
 
 Nothing here routes, dequantises or multiplies: those steps belong to the
 oracle and to the HIP library.
@@ -66,13 +73,18 @@ class LayerConfig:
     top_k: int
     ffn: int
     shared_ffn: int
-    expert_type: str  # "q8_0" | "q4_k" | "q2_k"
+    expert_type: str  # "q8_0" | "q4_k" | "q2_k" | "q3_k"
     shared_type: str  # "q8_0" | "q4_k" (ignored when shared_ffn == 0)
     n_tokens: int
     router_std: float
     weight_std: float  # std of the normal draw that Q8_0 tensors quantise
     routing: str = "iid"
     seed_index: int = 0
+    down_type: Optional[str] = None  # routed down type; None: expert_type
+
+    @property
+    def routed_down_type(self) -> str:
+        return self.down_type or self.expert_type
 
     @property
     def seed(self) -> int:
@@ -102,6 +114,12 @@ CONFIGS = {
     # matrices of the "Step-5 Preview GGUF" Q2 recipes, Tensor-type table).
     "step5_q2k_verify_m4": LayerConfig(
         "step5_q2k_verify_m4", 4096, 352, 8, 1536, 1536, "q2_k", "q8_0", 4, 0.02, 0.02, "disjoint", 6),
+    # The same verify batch with the routed types of the Q2_K-Protected2
+    # recipe: Q2_K gate/up, Q3_K down ("Step-5 Preview GGUF", Tensor-type
+    # table), shared expert Q8_0.
+    "step5_q2kp2_verify_m4": LayerConfig(
+        "step5_q2kp2_verify_m4", 4096, 352, 8, 1536, 1536, "q2_k", "q8_0", 4, 0.02, 0.02, "disjoint",
+        7, "q3_k"),
 }
 
 
@@ -141,6 +159,22 @@ def q2_k_bytes(rows: int, cols: int) -> int:
     return q2_k_quant_offset(rows, cols) + 64 * rows * (cols // 256)
 
 
+def q3_k_scale_offset(rows: int, cols: int) -> int:
+    return (2 * rows * (cols // 256) + 255) // 256 * 256
+
+
+def q3_k_low_offset(rows: int, cols: int) -> int:
+    return (q3_k_scale_offset(rows, cols) + 16 * rows * (cols // 256) + 255) // 256 * 256
+
+
+def q3_k_high_offset(rows: int, cols: int) -> int:
+    return (q3_k_low_offset(rows, cols) + 64 * rows * (cols // 256) + 255) // 256 * 256
+
+
+def q3_k_bytes(rows: int, cols: int) -> int:
+    return q3_k_high_offset(rows, cols) + 32 * rows * (cols // 256)
+
+
 def tensor_bytes(dtype: str, rows: int, cols: int) -> int:
     if dtype == "q8_0":
         if cols % 32:
@@ -154,6 +188,10 @@ def tensor_bytes(dtype: str, rows: int, cols: int) -> int:
         if cols % 256:
             raise ValueError("Q2_K needs cols % 256 == 0")
         return q2_k_bytes(rows, cols)
+    if dtype == "q3_k":
+        if cols % 256:
+            raise ValueError("Q3_K needs cols % 256 == 0")
+        return q3_k_bytes(rows, cols)
     if dtype == "f32":
         return 4 * rows * cols
     raise ValueError(f"unknown dtype {dtype!r}")
@@ -256,6 +294,34 @@ def _fill_q2_k(buf: np.ndarray, rows_total: int, cols: int, row0: int, dd, sc, q
     buf[qo + 64 * s0: qo + 64 * (s0 + n)] = qs.reshape(-1)
 
 
+def _draw_q3_k_rows(rng: np.random.Generator, rows: int, cols: int):
+    """Uniform-random Q3_K fields for ``rows`` rows.
+
+    d ~ U[2^-11, 2^-9) rounded to fp16 (weights of a few hundredths); every
+    scale uniform on 0..63, every low and high quant byte uniform, so every
+    3-bit quant is uniform on 0..7.
+    """
+    n = rows * (cols // 256)
+    d = rng.uniform(2.0 ** -11, 2.0 ** -9, n).astype(np.float16)
+    sc = rng.integers(0, 64, (n, 16), dtype=np.uint8)
+    lo = rng.integers(0, 256, (n, 64), dtype=np.uint8)
+    hi = rng.integers(0, 256, (n, 32), dtype=np.uint8)
+    return d.view(np.uint16).reshape(n, 1).view(np.uint8), sc, lo, hi
+
+
+def _fill_q3_k(buf: np.ndarray, rows_total: int, cols: int, row0: int, d, sc, lo, hi):
+    ns = cols // 256
+    n = d.shape[0]
+    s0 = row0 * ns
+    so = q3_k_scale_offset(rows_total, cols)
+    lo_off = q3_k_low_offset(rows_total, cols)
+    hi_off = q3_k_high_offset(rows_total, cols)
+    buf[2 * s0: 2 * (s0 + n)] = d.reshape(-1)
+    buf[so + 16 * s0: so + 16 * (s0 + n)] = sc.reshape(-1)
+    buf[lo_off + 64 * s0: lo_off + 64 * (s0 + n)] = lo.reshape(-1)
+    buf[hi_off + 32 * s0: hi_off + 32 * (s0 + n)] = hi.reshape(-1)
+
+
 def _rng(cfg: LayerConfig, instance: int, *key: int) -> np.random.Generator:
     ss = np.random.SeedSequence([cfg.seed, instance, *key])
     return np.random.Generator(np.random.PCG64(ss))
@@ -293,6 +359,8 @@ def _stacked(cfg: LayerConfig, instance: int, tid: int, rows: int, cols: int,
         elif dtype == "q2_k":
             dd, sc, qs = _draw_q2_k_rows(rng, rows, cols)
             _fill_q2_k(buf, total_rows, cols, e * rows, dd, sc, qs)
+        elif dtype == "q3_k":
+            _fill_q3_k(buf, total_rows, cols, e * rows, *_draw_q3_k_rows(rng, rows, cols))
         else:
             raise ValueError(f"unknown dtype {dtype!r}")
 
@@ -319,7 +387,7 @@ def draw_layer(cfg: LayerConfig, instance: int = 0, threads: Optional[int] = Non
         et = cfg.expert_type
         gate = _stacked(cfg, instance, _T_GATE, F, H, et, E, pool)
         up = _stacked(cfg, instance, _T_UP, F, H, et, E, pool)
-        down = _stacked(cfg, instance, _T_DOWN, H, F, et, E, pool)
+        down = _stacked(cfg, instance, _T_DOWN, H, F, cfg.routed_down_type, E, pool)
         sg = su = sd = None
         if Fs > 0:
             st = cfg.shared_type

@@ -44,6 +44,8 @@ def read_fixture(name: str):
 def oracle_kwargs(inp) -> dict:
     c = inp.cfg
     kw = dict(top_k=c.top_k, ffn=c.ffn, expert_type=c.expert_type)
+    if c.down_type:
+        kw.update(down_type=c.down_type)
     if c.shared_ffn > 0:
         kw.update(shared=(inp.shared_gate, inp.shared_up, inp.shared_down),
                   shared_ffn=c.shared_ffn, shared_type=c.shared_type)
@@ -101,6 +103,8 @@ def scale_fields(dtype: str, buf: np.ndarray, rows: int, cols: int) -> np.ndarra
     n = rows * (cols // 256)
     if dtype == "q2_k":
         return buf[: 4 * n].view(np.uint16).reshape(n, 2)
+    if dtype == "q3_k":
+        return buf[: 2 * n].view(np.uint16).reshape(n, 1)
     return buf[: 16 * n].view(np.uint16).reshape(n, 8)[:, 0:2]
 
 
@@ -130,10 +134,15 @@ def copy_expert_rows(dtype: str, buf: np.ndarray, rows_per_expert: int, cols: in
         qo = synth.q8_0_quant_offset(R, cols)
         qp = out[qo: qo + R * cols].reshape(n_experts, rows_per_expert * cols)
         qp[:] = qp[src]
-    elif dtype == "q2_k":
+    elif dtype in ("q2_k", "q3_k"):
         ns = cols // 256
-        so, qo = synth.q2_k_scale_offset(R, cols), synth.q2_k_quant_offset(R, cols)
-        for start, width in ((0, 4), (so, 16), (qo, 64)):
+        if dtype == "q2_k":
+            planes = ((0, 4), (synth.q2_k_scale_offset(R, cols), 16),
+                      (synth.q2_k_quant_offset(R, cols), 64))
+        else:
+            planes = ((0, 2), (synth.q3_k_scale_offset(R, cols), 16),
+                      (synth.q3_k_low_offset(R, cols), 64), (synth.q3_k_high_offset(R, cols), 32))
+        for start, width in planes:
             pl = out[start: start + R * ns * width].reshape(n_experts, rows_per_expert * ns * width)
             pl[:] = pl[src]
     else:

@@ -32,7 +32,7 @@ def log(msg: str):
 
 def desc_of(cfg) -> svr.LayerDesc:
     return svr.LayerDesc(cfg.hidden, cfg.n_experts, cfg.top_k, cfg.ffn, cfg.shared_ffn,
-                         cfg.expert_type, cfg.shared_type)
+                         cfg.expert_type, cfg.shared_type, down_type=cfg.down_type)
 
 
 def dev(a: np.ndarray) -> torch.Tensor:

@@ -74,7 +74,9 @@ def test_missing_library_fails_loudly(monkeypatch):
 @pytest.mark.parametrize("dtype,rows,cols", [("q8_0", 1, 32), ("q8_0", 1280, 4096), ("q8_0", 7, 96),
                                              ("q4_k", 5, 256), ("q4_k", 352 * 1536, 4096),
                                              ("q2_k", 1, 256), ("q2_k", 3, 512),
-                                             ("q2_k", 352 * 4096, 1536), ("f32", 3, 5)])
+                                             ("q2_k", 352 * 4096, 1536), ("q3_k", 1, 256),
+                                             ("q3_k", 5, 768), ("q3_k", 352 * 4096, 1536),
+                                             ("f32", 3, 5)])
 def test_tensor_bytes_match_the_generator(dtype, rows, cols):
     assert svr.moe_tensor_bytes(dtype, rows, cols) == synth.tensor_bytes(dtype, rows, cols)
 
@@ -118,6 +120,9 @@ def test_workspace_grows_with_tokens():
     (dict(shared_type="q2_k"), B.ERR_DTYPE),           # 2-bit: routed experts only
     (dict(expert_type="q2_k", ffn=1000), B.ERR_SHAPE),
     (dict(expert_type="q2_k", hidden=65536, shared_ffn=0), B.ERR_SHAPE),  # > 512 chunks a row
+    (dict(shared_type="q3_k"), B.ERR_DTYPE),
+    (dict(expert_type="q2_k", down_type="q3_k", ffn=1000), B.ERR_SHAPE),
+    (dict(expert_type="q8_0", down_type="q4_k", ffn=96), B.ERR_SHAPE),  # Q8_0 F fits, Q4_K does not
 ])
 def test_bad_descriptors_are_rejected(kw, status):
     d = _desc(**kw).c()
@@ -132,6 +137,25 @@ def test_q2_k_routed_experts_are_accepted():
     d = _desc(expert_type="q2_k").c()
     assert svr.lib().moe_stage_count(ctypes.byref(d), 512) == 3
     assert svr.lib().moe_stage_count(ctypes.byref(_desc().c()), 512) == 5
+
+
+def test_routed_down_type_selects_the_path():
+    mixed = _desc(expert_type="q2_k", down_type="q3_k")
+    for M in (1, 4, 16, 512):
+        assert svr.moe_workspace_bytes(mixed, M) > 0
+    L = svr.lib()
+    assert L.moe_stage_count(ctypes.byref(mixed.c()), 512) == 3
+    # down_type 0 is the gate/up type; a different down type leaves the
+    # matrix-core path and the single launch
+    assert L.moe_stage_count(ctypes.byref(_desc(down_type="q4_k").c()), 512) == 5
+    assert L.moe_stage_count(ctypes.byref(_desc(down_type="q8_0").c()), 512) == 3
+    one = _desc(single_launch=True)
+    assert L.moe_stage_count(ctypes.byref(one.c()), 4) == 1
+    assert L.moe_stage_count(ctypes.byref(_desc(single_launch=True, down_type="q8_0").c()), 4) == 3
+    out = ctypes.c_size_t()
+    bad = _desc().c()
+    bad.down_type = 9
+    assert L.moe_workspace_bytes(ctypes.byref(bad), 4, ctypes.byref(out)) == B.ERR_DTYPE
 
 
 def test_shared_type_ignored_without_shared_expert():

@@ -3,7 +3,8 @@ benchmark times (same shapes, same token counts, one moe_layer_forward).
 
 Step-3.5-Flash-shaped decode (M=1, Q8_0), the same layer as the 4-token
 verify batch (Q4_K routed), the Step-5-shaped verify batch with the four
-tokens on disjoint experts (Q4_K and Q2_K routed), and the 512-token prefill micro-batch, whose
+tokens on disjoint experts (Q4_K, Q2_K, and the Q2_K-Protected2 pairing of
+Q2_K gate/up with Q3_K down), and the 512-token prefill micro-batch, whose
 FFN outputs the oracle computes for a sample of tokens.
 """
 
@@ -23,7 +24,8 @@ SAMPLE_TOKENS = [0, 1, 2, 255, 256, 400, 510, 511]
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["step35_decode_m1", "step35_verify_m4", "step5_verify_m4",
-                                  "step5_q2k_verify_m4", "step5_prefill_m512"])
+                                  "step5_q2k_verify_m4", "step5_q2kp2_verify_m4",
+                                  "step5_prefill_m512"])
 def test_full_config(name):
     cfg = synth.CONFIGS[name]
     log(f"[{name}] drawing layer")
@@ -39,7 +41,7 @@ def test_full_config(name):
     check_routing(ids, tw, ref)
     rows = ref["tokens"]
     check_y(y[rows], ref["y"], name)
-    if name in ("step5_verify_m4", "step5_q2k_verify_m4"):
+    if name in ("step5_verify_m4", "step5_q2k_verify_m4", "step5_q2kp2_verify_m4"):
         assert len(ref["active"]) == 32
     # Routing lists of the whole batch, exactly.
     r = gpu_route(cfg, w.router, x)
@@ -52,7 +54,8 @@ def test_full_config(name):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("name", ["step35_verify_m4", "step5_verify_m4", "step5_q2k_verify_m4"])
+@pytest.mark.parametrize("name", ["step35_verify_m4", "step5_verify_m4", "step5_q2k_verify_m4",
+                                  "step5_q2kp2_verify_m4"])
 def test_verify_batches_of_one_to_four_tokens_agree_bitwise(name):
     # The MTP verify batch is the last accepted token plus up to three drafts,
     # and the draft count changes from round to round ("Support Step3.5/3.7

@@ -28,6 +28,9 @@ def _pins():
     for s in (0, 5, 15):
         yield lambda s=s: P.test_q2_k_single_field_positions(s)
     yield P.test_q2_k_multi_row_record_order
+    for s in (0, 1, 11):
+        yield lambda s=s: P.test_q3_k_single_field_positions(s)
+    yield P.test_q3_k_multi_row_record_order
     yield P.test_router_logits_unit_vectors_pick_columns
     yield P.test_select_ties_go_to_lower_index
     yield P.test_select_matches_brute_force_sort
@@ -39,7 +42,7 @@ def _pins():
     for args in [("q8_0", 256, 128, 0, 8), ("q8_0", 256, 64, 96, 4)]:
         yield lambda a=args: P.test_oracle_matches_scalar_twin(*a)
     yield P.test_one_expert_top1_layer_is_dense_swiglu_ffn
-    for et in ("q8_0", "q4_k", "q2_k"):
+    for et in ("q8_0", "q4_k", "q2_k", "q3_k"):
         yield lambda et=et: P.test_doubling_down_scales_doubles_routed_part_exactly(et)
     yield P.test_rows_are_independent_of_batch
 
@@ -97,6 +100,36 @@ def _q2k_plus_min(buf, rows, cols, row_start=0, row_count=None):
     return w.reshape(n, cols)
 
 
+def _q3k_fields_high_nibbles_swapped(buf, rows, cols, row_start=0, row_count=None):
+    # high bits of sub-blocks 2p and 2p+1 read from each other's nibble
+    d, S, Q = _orig["q3_k_fields"](buf, rows, cols, row_start, row_count)
+    low, high = Q & 3, Q >> 2
+    high = high.reshape(high.shape[0], 8, 2, 16)[:, :, ::-1, :].reshape(Q.shape)
+    return d, S, low | (high << 2)
+
+
+def _q3k_fields_high_bit_dropped(*a, **k):
+    d, S, Q = _orig["q3_k_fields"](*a, **k)
+    return d, S, Q & 3
+
+
+def _q3k_no_scale_offset(buf, rows, cols, row_start=0, row_count=None):
+    r0, n = om._rows(rows, row_start, row_count)
+    d, S, Q = om.q3_k_fields(buf, rows, cols, r0, n)
+    return (d[:, None, None] * S[:, :, None] * (Q - 4)).reshape(n, cols)
+
+
+def _q3k_quant_offset_sign(buf, rows, cols, row_start=0, row_count=None):
+    r0, n = om._rows(rows, row_start, row_count)
+    d, S, Q = om.q3_k_fields(buf, rows, cols, r0, n)
+    return (d[:, None, None] * (S[:, :, None] - 32) * (Q + 4)).reshape(n, cols)
+
+
+def _q3k_offsets_unpadded(rows, cols):
+    ns = cols // 256
+    return 2 * rows * ns, 18 * rows * ns, 82 * rows * ns
+
+
 def _q8_offset_unpadded(rows, cols):
     return 2 * rows * (cols // 32)
 
@@ -140,6 +173,11 @@ MUTATIONS = {
     "q2k_scale_nibbles": ("q2_k_fields", _q2k_fields_scale_nibbles_swapped),
     "q2k_plane_offsets": ("q2_k_offsets", _q2k_offsets_unpadded),
     "q2k_min_sign": ("dequant_q2_k", _q2k_plus_min),
+    "q3k_high_nibbles": ("q3_k_fields", _q3k_fields_high_nibbles_swapped),
+    "q3k_high_bit_dropped": ("q3_k_fields", _q3k_fields_high_bit_dropped),
+    "q3k_scale_offset": ("dequant_q3_k", _q3k_no_scale_offset),
+    "q3k_quant_offset_sign": ("dequant_q3_k", _q3k_quant_offset_sign),
+    "q3k_plane_offsets": ("q3_k_offsets", _q3k_offsets_unpadded),
     "tie_to_higher": ("select_experts", _select_high_tie),
     "no_renormalise": ("routing_weights", _weights_unnormalised),
     "silu_is_sigmoid": ("silu", _sigmoid_only),

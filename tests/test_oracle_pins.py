@@ -30,7 +30,8 @@ def test_f16_decode_all_bit_patterns_match_numpy():
     assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
 
 
-FIXTURES = [("q8_0_planar.txt", "q8_0"), ("q4_k_planar.txt", "q4_k"), ("q2_k_planar.txt", "q2_k")]
+FIXTURES = [("q8_0_planar.txt", "q8_0"), ("q4_k_planar.txt", "q4_k"), ("q2_k_planar.txt", "q2_k"),
+            ("q3_k_planar.txt", "q3_k")]
 
 
 @pytest.mark.parametrize("fixture,dtype", FIXTURES)
@@ -189,6 +190,66 @@ def test_q2_k_multi_row_record_order():
     assert np.array_equal(om.dequant_q2_k(buf, 3, 512, row_start=1, row_count=2), W[1:3])
 
 
+def _q3k_tensor(recs, rows, cols):
+    """Planar Q3_K bytes from records (d_bits, S[16], Q[16][16]) (test-side
+    encoder, written from the layout: plane starts rounded up to 256 bytes,
+    low two bits as in Q2_K, high bit of weight i of sub-block s at byte
+    4 (s // 2) + i % 4, bit 4 (s % 2) + i // 4 of the record's 32).
+    """
+    n = len(recs)
+    so = -(-2 * n // 256) * 256
+    lo = -(-(so + 16 * n) // 256) * 256
+    hi = -(-(lo + 64 * n) // 256) * 256
+    out = bytearray(hi + 32 * n)
+    for k, (db, S, Q) in enumerate(recs):
+        out[2 * k: 2 * k + 2] = int(db).to_bytes(2, "little")
+        for s in range(16):
+            out[so + 16 * k + s] = S[s] & 63
+            for i in range(16):
+                out[lo + 64 * k + 4 * s + i % 4] |= (Q[s][i] & 3) << (2 * (i // 4))
+                out[hi + 32 * k + 4 * (s // 2) + i % 4] |= ((Q[s][i] >> 2) & 1) << (4 * (s % 2) + i // 4)
+    assert len(out) == synth.tensor_bytes("q3_k", rows, cols)
+    return np.frombuffer(bytes(out), dtype=np.uint8).copy()
+
+
+@pytest.mark.parametrize("s", [0, 1, 6, 11, 15])
+def test_q3_k_single_field_positions(s):
+    # Every quant at the zero point Q = 4 except one: exactly one non-zero
+    # weight must appear, at column 16*s + i, with value (S - 32) * (Q - 4).
+    for i in (0, 1, 3, 4, 9, 14, 15):
+        for q in (0, 3, 5, 7):                   # high bit clear and set
+            Q = [[4] * 16 for _ in range(16)]
+            Q[s][i] = q
+            S = [32 + (s % 5) - 2 * (s % 3) + 1 for _ in range(16)]
+            S[s] = 32 - 7 + s
+            buf = _q3k_tensor([(0x3C00, S, Q)], 1, 256)
+            W = om.dequant_q3_k(buf, 1, 256)[0]
+            assert list(np.nonzero(W)[0]) == [16 * s + i]
+            assert W[16 * s + i] == (s - 7) * (q - 4)
+    # All quants zero (Q = 0): sub-block s is -4 * (S_s - 32) * d throughout.
+    S = [32] * 16
+    S[s] = 0 if s % 2 else 63
+    buf = _q3k_tensor([(0x3800, S, [[0] * 16 for _ in range(16)])], 1, 256)
+    W = om.dequant_q3_k(buf, 1, 256)[0]
+    exp = np.zeros(256)
+    exp[16 * s:16 * s + 16] = 0.5 * (S[s] - 32) * -4
+    assert np.array_equal(W, exp)
+
+
+def test_q3_k_multi_row_record_order():
+    recs = []
+    for r in range(3):
+        for b in range(2):
+            v = r * 2 + b + 1          # 1..6
+            recs.append((0x3C00, [32 + v] * 16, [[5] * 16 for _ in range(16)]))
+    buf = _q3k_tensor(recs, 3, 512)
+    W = om.dequant_q3_k(buf, 3, 512)
+    for r in range(3):
+        for b in range(2):
+            assert np.all(W[r, 256 * b:256 * (b + 1)] == r * 2 + b + 1)
+    assert np.array_equal(om.dequant_q3_k(buf, 3, 512, row_start=2, row_count=1), W[2:3])
+
+
 def test_q8_0_row_slice_matches_full():
     cfg = small_config(n_experts=3, ffn=64)
     inp = synth.draw_layer(cfg, threads=1)
@@ -292,10 +353,12 @@ def test_silu_is_g_times_logistic():
 
 
 @pytest.mark.parametrize("etype,H,F,Fs,E", [("q8_0", 256, 128, 0, 8), ("q8_0", 256, 64, 96, 4),
-                                             ("q4_k", 256, 256, 64, 4), ("q2_k", 256, 256, 64, 4)])
+                                             ("q4_k", 256, 256, 64, 4), ("q2_k", 256, 256, 64, 4),
+                                             ("q2_k/q3_k", 256, 256, 64, 4)])
 def test_oracle_matches_scalar_twin(etype, H, F, Fs, E):
+    etype, _, dtype = etype.partition("/")
     cfg = small_config(hidden=H, ffn=F, shared_ffn=Fs, n_experts=E, expert_type=etype,
-                       n_tokens=2, seed_index=200 + F)
+                       down_type=dtype or None, n_tokens=2, seed_index=200 + F)
     inp = synth.draw_layer(cfg, threads=1)
     x, _ = synth.draw_tokens(cfg)
     ref = run_oracle(inp, x)
@@ -336,7 +399,7 @@ def test_identical_experts_make_routing_irrelevant():
     assert np.allclose(ref["y"], one, rtol=1e-12, atol=1e-12 * np.abs(one).max())
 
 
-@pytest.mark.parametrize("etype", ["q8_0", "q4_k", "q2_k"])
+@pytest.mark.parametrize("etype", ["q8_0", "q4_k", "q2_k", "q3_k"])
 def test_doubling_down_scales_doubles_routed_part_exactly(etype):
     F = 128 if etype == "q8_0" else 256
     cfg = small_config(n_experts=4, ffn=F, shared_ffn=64, expert_type=etype, n_tokens=2)
@@ -405,6 +468,19 @@ def test_q2_k_generated_fields_cover_their_ranges():
     # every quant value is about equally frequent (uniform random bytes)
     counts = np.bincount(q.reshape(-1), minlength=4) / q.size
     assert np.all(np.abs(counts - 0.25) < 0.01)
+
+
+def test_q3_k_generated_fields_cover_their_ranges():
+    cfg = small_config(n_experts=4, expert_type="q2_k", down_type="q3_k", ffn=256)
+    inp = synth.draw_layer(cfg, threads=1)
+    assert inp.gate.size == synth.tensor_bytes("q2_k", 4 * 256, 256)
+    assert inp.down.size == synth.tensor_bytes("q3_k", 4 * 256, 256)
+    d, S, Q = om.q3_k_fields(inp.down, 4 * 256, 256)
+    assert d.min() >= 2.0 ** -11 and d.max() <= 2.0 ** -9
+    assert S.min() == 0 and S.max() == 63
+    assert Q.min() == 0 and Q.max() == 7
+    counts = np.bincount(Q.reshape(-1), minlength=8) / Q.size
+    assert np.all(np.abs(counts - 0.125) < 0.01)
 
 
 def test_margin_predicate_enforces_gaps():
