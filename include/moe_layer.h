@@ -14,7 +14,8 @@
  * recipes ("Step-5 Preview GGUF", Precision distribution table; "Step 3.7
  * Flash Mixed-Quant GGUF", Tensor recipe); the 2-bit Step-5 recipes store
  * routed matrices in Q2_K and Q3_K, Q2_K-Protected2 with Q2_K gate/up and
- * Q3_K down ("Step-5 Preview GGUF", Tensor-type table).
+ * Q3_K down ("Step-5 Preview GGUF", Tensor-type table); every recipe stores
+ * the MTP heads' matrices in Q6_K (same table).
  *
  * What one call computes, for each token t of x [M][H]:
  *   l[e]    = sum_h router[e][h] * x[t][h]                      (F32 router)
@@ -76,6 +77,24 @@
  *            every Q, 32 bytes per super-block at G + 32*(r*ns + b); weight i
  *            of sub-block s in byte 4*(s/2) + i % 4, bit 4*(s % 2) + i/4.
  *            Total G + 32*rows*ns bytes.
+ *   MOE_Q6_K rows x cols, cols % 256 == 0, ns = cols / 256, routed experts
+ *            only.  Super-blocks of 256 weights: fp16 d, 16 sub-blocks of 16
+ *            weights with a signed 8-bit scale sc, 6-bit quants Q,
+ *            w = d*sc_s*(Q - 32).
+ *            Bytes [0, 2*rows*ns): fp16 d of super-block (r, b) at
+ *            2*(r*ns + b).
+ *            Bytes from S = round_up(2*rows*ns, 256): 16 int8 scales of
+ *            super-block (r, b) at S + 16*(r*ns + b).
+ *            Bytes from L = round_up(S + 16*rows*ns, 256): the low four bits
+ *            of every Q, 128 bytes per super-block at L + 128*(r*ns + b),
+ *            laid out as the Q4_K quants (32-weight group g in bytes
+ *            [16g, 16g+16), weight i of it in byte i/2, low nibble for even
+ *            i); sub-block s is group s/2, weights 16*(s%2) onward.
+ *            Bytes from G = round_up(L + 128*rows*ns, 256): the high two
+ *            bits of every Q, 64 bytes per super-block at G + 64*(r*ns + b);
+ *            weight i of group g at byte 8g + 4*(i/16) + (i%8)/2, bits
+ *            4*((i/8)%2) + 2*(i%2) and the next one.
+ *            Total G + 64*rows*ns bytes.
  *   Expert tensors are stacked experts-outermost and stored as one tensor:
  *   gate and up are (E*F) x H, down is (E*H) x F; expert e owns rows
  *   [e*F, (e+1)*F) (resp. [e*H, (e+1)*H)).  The shared expert's gate and up
@@ -95,11 +114,11 @@
  *   it returns MOE_OK, except MOE_ERR_LAUNCH, which reports a failure seen
  *   after enqueueing (hipGetLastError).  Shapes are checked before launch:
  *   1 <= n_experts <= 1024; 1 <= top_k <= min(n_experts, 64); hidden,
- *   ffn and shared_ffn multiples of 32 (Q8_0) or 256 (Q4_K, Q2_K, Q3_K) for
- *   the tensors that use them, and a row of at most 512 blocks of 16 bytes
- *   (Q8_0: 8192 columns, Q4_K: 16384, Q2_K and Q3_K: 32768); n_tokens >= 0
- *   (0 enqueues nothing).  MOE_Q2_K or MOE_Q3_K as shared_type is
- *   MOE_ERR_DTYPE.
+ *   ffn and shared_ffn multiples of 32 (Q8_0) or 256 (Q4_K, Q2_K, Q3_K,
+ *   Q6_K) for the tensors that use them, and a row of at most 512 blocks of
+ *   16 bytes (Q8_0: 8192 columns, Q4_K and Q6_K: 16384, Q2_K and Q3_K:
+ *   32768); n_tokens >= 0 (0 enqueues nothing).  MOE_Q2_K, MOE_Q3_K or
+ *   MOE_Q6_K as shared_type is MOE_ERR_DTYPE.
  */
 #ifndef SVR_MOE_LAYER_H
 #define SVR_MOE_LAYER_H
@@ -117,6 +136,7 @@ extern "C" {
 #define MOE_Q4_K 2
 #define MOE_Q2_K 3
 #define MOE_Q3_K 4
+#define MOE_Q6_K 5
 
 /* Status codes. */
 #define MOE_OK 0
@@ -134,12 +154,13 @@ typedef struct moe_layer_desc {
   int32_t top_k;       /* k */
   int32_t ffn;         /* F, routed expert FFN width */
   int32_t shared_ffn;  /* Fs, shared expert FFN width; 0 = no shared expert */
-  int32_t expert_type; /* MOE_Q8_0, MOE_Q4_K, MOE_Q2_K or MOE_Q3_K: routed
-                          gate/up, and down unless down_type says otherwise */
+  int32_t expert_type; /* MOE_Q8_0, MOE_Q4_K, MOE_Q2_K, MOE_Q3_K or MOE_Q6_K:
+                          routed gate/up, and down unless down_type says
+                          otherwise */
   int32_t shared_type; /* MOE_Q8_0 or MOE_Q4_K: shared gate/up/down */
   int32_t flags;       /* 0 or MOE_SINGLE_LAUNCH; other bits: MOE_ERR_ARG */
-  int32_t down_type;   /* routed down: 0 = expert_type, else MOE_Q8_0, MOE_Q4_K,
-                          MOE_Q2_K or MOE_Q3_K */
+  int32_t down_type;   /* routed down: 0 = expert_type, else one of the types
+                          expert_type takes */
 } moe_layer_desc;
 
 /* desc->flags: run batches of 1 to 4 tokens as one kernel launch where the
@@ -213,8 +234,8 @@ int32_t moe_route(const moe_layer_desc* desc, const float* router, const float* 
  * integer quants, fp32 scales and activations split into two bf16 terms,
  * in five stages ("route", "shared_gateup", "gateup", "shared_down",
  * "down_combine"; the shared stages are empty without a shared expert);
- * with Q2_K or Q3_K routed matrices they run the three stages of the small
- * batches instead (no matrix-core path for those types).  The single
+ * with Q2_K, Q3_K or Q6_K routed matrices they run the three stages of the
+ * small batches instead (no matrix-core path for those types).  The single
  * launch needs down_type equal to expert_type.
  * moe_stage_count / moe_stage_name say which. */
 int32_t moe_layer_forward(const moe_layer_desc* desc, const moe_layer_weights* weights,
@@ -242,8 +263,8 @@ int32_t moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_weig
 /* Dequantise rows [row_start, row_start + row_count) of a rows x cols tensor
  * of `dtype` into out [row_count][cols] float (test hook for the block
  * decoders).  Q8_0 yields d*q, Q4_K and Q2_K yield fma(d*sc, q, -(dmin*m)),
- * Q3_K yields (d*(S-32))*(Q-4); all are the exactly rounded float of the
- * block's value. */
+ * Q3_K yields (d*(S-32))*(Q-4), Q6_K (d*sc)*(Q-32); all are the exactly
+ * rounded float of the block's value. */
 int32_t moe_dequant_rows(int32_t dtype, const void* tensor, int64_t rows, int32_t cols,
                          int64_t row_start, int64_t row_count, float* out, void* hip_stream);
 

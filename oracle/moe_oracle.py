@@ -37,7 +37,10 @@ block layouts.  Readings taken here:
   sub-blocks with a 4-bit scale and a 4-bit min, 2-bit quants,
   w = d*sc*q - dmin*m; Q3_K as the 3-bit member without mins: fp16 d,
   sixteen 16-weight sub-blocks with a 6-bit scale S stored with offset 32
-  and 3-bit quants Q stored with offset 4, w = d*(S - 32)*(Q - 4).
+  and 3-bit quants Q stored with offset 4, w = d*(S - 32)*(Q - 4); Q6_K as
+  the 6-bit member: fp16 d, sixteen 16-weight sub-blocks with a signed
+  8-bit scale and 6-bit quants stored with offset 32, w = d*sc*(Q - 32)
+  (the recipes' type for the MTP heads' matrices, same table).
 """
 
 from __future__ import annotations
@@ -247,6 +250,56 @@ def dequant_q3_k(buf, rows: int, cols: int, row_start: int = 0, row_count=None) 
     return w.reshape(n, cols)
 
 
+def q6_k_offsets(rows: int, cols: int):
+    """Plane starts of planar Q6_K: (scale plane, low-bit plane, high-bit plane)."""
+    ns = cols // 256
+    so = (2 * rows * ns + 255) // 256 * 256
+    lo = (so + 16 * rows * ns + 255) // 256 * 256
+    hi = (lo + 128 * rows * ns + 255) // 256 * 256
+    return so, lo, hi
+
+
+def q6_k_fields(buf, rows: int, cols: int, row_start: int = 0, row_count=None):
+    """Decode Q6_K records into (d, sc[16], Q[16][16]) per record.
+
+    sc is the signed byte of scale s.  Q = low | high << 4: weight i of
+    32-weight group g (sub-block 2g + i // 16, position i % 16) has its low
+    four bits in byte 16g + i // 2 of the record's 128 (low nibble for even
+    i) and its high two bits at bit 4 ((i // 8) % 2) + 2 (i % 2) of byte
+    8g + 4 (i // 16) + (i % 8) // 2 of the record's 64.
+    """
+    if cols % 256:
+        raise ValueError("Q6_K needs cols % 256 == 0")
+    r0, n = _rows(rows, row_start, row_count)
+    buf = np.asarray(buf, dtype=np.uint8)
+    ns = cols // 256
+    a, b = r0 * ns, (r0 + n) * ns
+    so, lo, hi = q6_k_offsets(rows, cols)
+    db = buf[2 * a: 2 * b].reshape(b - a, 2).astype(np.int64)
+    d = f16_to_f64(db[:, 0] | (db[:, 1] << 8))
+    sc = buf[so + 16 * a: so + 16 * b].view(np.int8).reshape(b - a, 16).astype(np.int64)
+    lb = buf[lo + 128 * a: lo + 128 * b].reshape(b - a, 8, 16).astype(np.int64)
+    hb = buf[hi + 64 * a: hi + 64 * b].reshape(b - a, 8, 8).astype(np.int64)
+    Q = np.empty((b - a, 16, 16), dtype=np.int64)
+    for g in range(8):
+        for i in range(32):
+            low = (lb[:, g, i // 2] >> (4 * (i % 2))) & 15
+            high = (hb[:, g, 4 * (i // 16) + (i % 8) // 2] >> (4 * ((i // 8) % 2) + 2 * (i % 2))) & 3
+            Q[:, 2 * g + i // 16, i % 16] = low | (high << 4)
+    return d, sc, Q
+
+
+def dequant_q6_k(buf, rows: int, cols: int, row_start: int = 0, row_count=None) -> np.ndarray:
+    """Planar Q6_K -> float64 [row_count][cols].
+
+    256-weight super-block, 16 sub-blocks of 16: w = d*sc_s*(Q - 32).
+    """
+    r0, n = _rows(rows, row_start, row_count)
+    d, sc, Q = q6_k_fields(buf, rows, cols, r0, n)
+    w = d[:, None, None] * sc[:, :, None].astype(np.float64) * (Q - 32).astype(np.float64)
+    return w.reshape(n, cols)
+
+
 def dequant(dtype: str, buf, rows: int, cols: int, row_start: int = 0, row_count=None) -> np.ndarray:
     if dtype == "q8_0":
         return dequant_q8_0(buf, rows, cols, row_start, row_count)
@@ -256,6 +309,8 @@ def dequant(dtype: str, buf, rows: int, cols: int, row_start: int = 0, row_count
         return dequant_q2_k(buf, rows, cols, row_start, row_count)
     if dtype == "q3_k":
         return dequant_q3_k(buf, rows, cols, row_start, row_count)
+    if dtype == "q6_k":
+        return dequant_q6_k(buf, rows, cols, row_start, row_count)
     if dtype == "f32":
         r0, n = _rows(rows, row_start, row_count)
         a = np.asarray(buf).view(np.float32).reshape(rows, cols)

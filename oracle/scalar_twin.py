@@ -7,8 +7,9 @@ codec, the Q4_K scale/min fields are cut from one Python integer holding the
 96-bit stream, a Q2_K quant is cut from the little-endian integer of its
 sub-block's four bytes (weight i at bit 8 (i % 4) + 2 (i // 4)), a Q3_K
 high bit from the integer of its sub-block pair's four bytes (bit
-8 (i % 4) + 4 (s % 2) + i // 4), and every product is an explicit loop over
-Python floats.
+8 (i % 4) + 4 (s % 2) + i // 4), a Q6_K quant from the integers of its
+group's 16 low bytes and 8 high bytes, and every product is an explicit
+loop over Python floats.
 Meant for hidden sizes of a few hundred and a handful of experts.
 """
 
@@ -82,7 +83,26 @@ def weight_q3_k(buf, rows: int, cols: int, r: int, c: int) -> float:
     return d * scale * (q - 4)
 
 
-_WEIGHT = {"q8_0": weight_q8_0, "q4_k": weight_q4_k, "q2_k": weight_q2_k, "q3_k": weight_q3_k}
+def weight_q6_k(buf, rows: int, cols: int, r: int, c: int) -> float:
+    ns = cols // 256
+    rec = r * ns + c // 256
+    g, i = (c % 256) // 32, c % 32
+    d = _f16(int(buf[2 * rec]), int(buf[2 * rec + 1]))
+    sbase = -(-2 * rows * ns // 256) * 256
+    lbase = -(-(sbase + 16 * rows * ns) // 256) * 256
+    hbase = -(-(lbase + 128 * rows * ns) // 256) * 256
+    sc = struct.unpack("<b", bytes([int(buf[sbase + 16 * rec + 2 * g + i // 16])]))[0]
+    lw = int.from_bytes(bytes(int(v) for v in buf[lbase + 128 * rec + 16 * g: lbase + 128 * rec + 16 * g + 16]),
+                        "little")
+    hw = int.from_bytes(bytes(int(v) for v in buf[hbase + 64 * rec + 8 * g: hbase + 64 * rec + 8 * g + 8]),
+                        "little")
+    low = (lw >> (4 * i)) & 15
+    high = (hw >> (32 * (i // 16) + 8 * ((i % 8) // 2) + 4 * ((i // 8) % 2) + 2 * (i % 2))) & 3
+    return d * sc * ((low | (high << 4)) - 32)
+
+
+_WEIGHT = {"q8_0": weight_q8_0, "q4_k": weight_q4_k, "q2_k": weight_q2_k, "q3_k": weight_q3_k,
+           "q6_k": weight_q6_k}
 
 
 def weight(dtype: str, buf, rows: int, cols: int, r: int, c: int) -> float:

@@ -22,6 +22,10 @@ from .layers import (  # noqa: F401
     q3_k_low_offset,
     q3_k_scale_offset,
     q4_k_bytes,
+    q6_k_bytes,
+    q6_k_high_offset,
+    q6_k_low_offset,
+    q6_k_scale_offset,
     q4_k_header_bytes,
     q8_0_bytes,
     q8_0_quant_offset,

@@ -37,6 +37,13 @@ Byte layouts (planar block quantisation) are those documented in
   ``q3_k_high_offset`` the high bit of every quant, 32 bytes per record,
   weight i of sub-block s in byte 4 (s // 2) + i % 4, bit 4 (s % 2) + i // 4.
   W = d * (S_s - 32) * (Q - 4) with Q = low | high << 2.
+* Q6_K, R rows x K columns, K % 256 == 0, ns = K / 256: a plane of R*ns fp16
+  d at byte 0; at ``q6_k_scale_offset`` R*ns 16-byte records of int8
+  scales; at ``q6_k_low_offset`` the low four bits of every quant, 128
+  bytes per record laid out as the Q4_K quants; at ``q6_k_high_offset``
+  the high two bits, 64 bytes per record, weight i of 32-weight group g at
+  byte 8g + 4 (i // 16) + (i % 8) // 2, bit 4 ((i // 8) % 2) + 2 (i % 2).
+  W = d * sc_s * (Q - 32) with Q = low | high << 4, s = 2g + i // 16.
 
 Nothing here routes, dequantises or multiplies: those steps belong to the
 oracle and to the HIP library.
@@ -73,7 +80,7 @@ class LayerConfig:
     top_k: int
     ffn: int
     shared_ffn: int
-    expert_type: str  # "q8_0" | "q4_k" | "q2_k" | "q3_k"
+    expert_type: str  # "q8_0" | "q4_k" | "q2_k" | "q3_k" | "q6_k"
     shared_type: str  # "q8_0" | "q4_k" (ignored when shared_ffn == 0)
     n_tokens: int
     router_std: float
@@ -120,6 +127,11 @@ CONFIGS = {
     "step5_q2kp2_verify_m4": LayerConfig(
         "step5_q2kp2_verify_m4", 4096, 352, 8, 1536, 1536, "q2_k", "q8_0", 4, 0.02, 0.02, "disjoint",
         7, "q3_k"),
+    # The Step-3.5 verify batch with 6-bit routed experts (Q6_K is the
+    # recipes' type for the MTP heads' matrices, "Step-5 Preview GGUF",
+    # Tensor-type table).
+    "step35_q6k_verify_m4": LayerConfig(
+        "step35_q6k_verify_m4", 4096, 288, 8, 1280, 1280, "q6_k", "q8_0", 4, 0.02, 0.02, "iid", 8),
 }
 
 
@@ -175,6 +187,22 @@ def q3_k_bytes(rows: int, cols: int) -> int:
     return q3_k_high_offset(rows, cols) + 32 * rows * (cols // 256)
 
 
+def q6_k_scale_offset(rows: int, cols: int) -> int:
+    return (2 * rows * (cols // 256) + 255) // 256 * 256
+
+
+def q6_k_low_offset(rows: int, cols: int) -> int:
+    return (q6_k_scale_offset(rows, cols) + 16 * rows * (cols // 256) + 255) // 256 * 256
+
+
+def q6_k_high_offset(rows: int, cols: int) -> int:
+    return (q6_k_low_offset(rows, cols) + 128 * rows * (cols // 256) + 255) // 256 * 256
+
+
+def q6_k_bytes(rows: int, cols: int) -> int:
+    return q6_k_high_offset(rows, cols) + 64 * rows * (cols // 256)
+
+
 def tensor_bytes(dtype: str, rows: int, cols: int) -> int:
     if dtype == "q8_0":
         if cols % 32:
@@ -192,6 +220,10 @@ def tensor_bytes(dtype: str, rows: int, cols: int) -> int:
         if cols % 256:
             raise ValueError("Q3_K needs cols % 256 == 0")
         return q3_k_bytes(rows, cols)
+    if dtype == "q6_k":
+        if cols % 256:
+            raise ValueError("Q6_K needs cols % 256 == 0")
+        return q6_k_bytes(rows, cols)
     if dtype == "f32":
         return 4 * rows * cols
     raise ValueError(f"unknown dtype {dtype!r}")
@@ -322,6 +354,34 @@ def _fill_q3_k(buf: np.ndarray, rows_total: int, cols: int, row0: int, d, sc, lo
     buf[hi_off + 32 * s0: hi_off + 32 * (s0 + n)] = hi.reshape(-1)
 
 
+def _draw_q6_k_rows(rng: np.random.Generator, rows: int, cols: int):
+    """Uniform-random Q6_K fields for ``rows`` rows.
+
+    d ~ U[2^-14, 2^-12) rounded to fp16; every scale uniform on -128..127
+    and every quant byte uniform, so every 6-bit quant is uniform on 0..63
+    (weights of a few hundredths).
+    """
+    n = rows * (cols // 256)
+    d = rng.uniform(2.0 ** -14, 2.0 ** -12, n).astype(np.float16)
+    sc = rng.integers(0, 256, (n, 16), dtype=np.uint8)
+    lo = rng.integers(0, 256, (n, 128), dtype=np.uint8)
+    hi = rng.integers(0, 256, (n, 64), dtype=np.uint8)
+    return d.view(np.uint16).reshape(n, 1).view(np.uint8), sc, lo, hi
+
+
+def _fill_q6_k(buf: np.ndarray, rows_total: int, cols: int, row0: int, d, sc, lo, hi):
+    ns = cols // 256
+    n = d.shape[0]
+    s0 = row0 * ns
+    so = q6_k_scale_offset(rows_total, cols)
+    lo_off = q6_k_low_offset(rows_total, cols)
+    hi_off = q6_k_high_offset(rows_total, cols)
+    buf[2 * s0: 2 * (s0 + n)] = d.reshape(-1)
+    buf[so + 16 * s0: so + 16 * (s0 + n)] = sc.reshape(-1)
+    buf[lo_off + 128 * s0: lo_off + 128 * (s0 + n)] = lo.reshape(-1)
+    buf[hi_off + 64 * s0: hi_off + 64 * (s0 + n)] = hi.reshape(-1)
+
+
 def _rng(cfg: LayerConfig, instance: int, *key: int) -> np.random.Generator:
     ss = np.random.SeedSequence([cfg.seed, instance, *key])
     return np.random.Generator(np.random.PCG64(ss))
@@ -361,6 +421,8 @@ def _stacked(cfg: LayerConfig, instance: int, tid: int, rows: int, cols: int,
             _fill_q2_k(buf, total_rows, cols, e * rows, dd, sc, qs)
         elif dtype == "q3_k":
             _fill_q3_k(buf, total_rows, cols, e * rows, *_draw_q3_k_rows(rng, rows, cols))
+        elif dtype == "q6_k":
+            _fill_q6_k(buf, total_rows, cols, e * rows, *_draw_q6_k_rows(rng, rows, cols))
         else:
             raise ValueError(f"unknown dtype {dtype!r}")
 

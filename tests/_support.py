@@ -103,7 +103,7 @@ def scale_fields(dtype: str, buf: np.ndarray, rows: int, cols: int) -> np.ndarra
     n = rows * (cols // 256)
     if dtype == "q2_k":
         return buf[: 4 * n].view(np.uint16).reshape(n, 2)
-    if dtype == "q3_k":
+    if dtype in ("q3_k", "q6_k"):
         return buf[: 2 * n].view(np.uint16).reshape(n, 1)
     return buf[: 16 * n].view(np.uint16).reshape(n, 8)[:, 0:2]
 
@@ -134,14 +134,17 @@ def copy_expert_rows(dtype: str, buf: np.ndarray, rows_per_expert: int, cols: in
         qo = synth.q8_0_quant_offset(R, cols)
         qp = out[qo: qo + R * cols].reshape(n_experts, rows_per_expert * cols)
         qp[:] = qp[src]
-    elif dtype in ("q2_k", "q3_k"):
+    elif dtype in ("q2_k", "q3_k", "q6_k"):
         ns = cols // 256
         if dtype == "q2_k":
             planes = ((0, 4), (synth.q2_k_scale_offset(R, cols), 16),
                       (synth.q2_k_quant_offset(R, cols), 64))
-        else:
+        elif dtype == "q3_k":
             planes = ((0, 2), (synth.q3_k_scale_offset(R, cols), 16),
                       (synth.q3_k_low_offset(R, cols), 64), (synth.q3_k_high_offset(R, cols), 32))
+        else:
+            planes = ((0, 2), (synth.q6_k_scale_offset(R, cols), 16),
+                      (synth.q6_k_low_offset(R, cols), 128), (synth.q6_k_high_offset(R, cols), 64))
         for start, width in planes:
             pl = out[start: start + R * ns * width].reshape(n_experts, rows_per_expert * ns * width)
             pl[:] = pl[src]

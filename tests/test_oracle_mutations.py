@@ -31,6 +31,9 @@ def _pins():
     for s in (0, 1, 11):
         yield lambda s=s: P.test_q3_k_single_field_positions(s)
     yield P.test_q3_k_multi_row_record_order
+    for s in (0, 7, 15):
+        yield lambda s=s: P.test_q6_k_single_field_positions(s)
+    yield P.test_q6_k_multi_row_record_order
     yield P.test_router_logits_unit_vectors_pick_columns
     yield P.test_select_ties_go_to_lower_index
     yield P.test_select_matches_brute_force_sort
@@ -42,7 +45,7 @@ def _pins():
     for args in [("q8_0", 256, 128, 0, 8), ("q8_0", 256, 64, 96, 4)]:
         yield lambda a=args: P.test_oracle_matches_scalar_twin(*a)
     yield P.test_one_expert_top1_layer_is_dense_swiglu_ffn
-    for et in ("q8_0", "q4_k", "q2_k", "q3_k"):
+    for et in ("q8_0", "q4_k", "q2_k", "q3_k", "q6_k"):
         yield lambda et=et: P.test_doubling_down_scales_doubles_routed_part_exactly(et)
     yield P.test_rows_are_independent_of_batch
 
@@ -130,6 +133,30 @@ def _q3k_offsets_unpadded(rows, cols):
     return 2 * rows * ns, 18 * rows * ns, 82 * rows * ns
 
 
+def _q6k_fields_high_pairs_swapped(buf, rows, cols, row_start=0, row_count=None):
+    # high bits of even and odd weights read from each other's bit pair
+    d, sc, Q = _orig["q6_k_fields"](buf, rows, cols, row_start, row_count)
+    low, high = Q & 15, Q >> 4
+    high = high.reshape(high.shape[0], 16, 8, 2)[:, :, :, ::-1].reshape(Q.shape)
+    return d, sc, low | (high << 4)
+
+
+def _q6k_fields_unsigned_scales(*a, **k):
+    d, sc, Q = _orig["q6_k_fields"](*a, **k)
+    return d, sc & 255, Q
+
+
+def _q6k_offset_sign(buf, rows, cols, row_start=0, row_count=None):
+    r0, n = om._rows(rows, row_start, row_count)
+    d, sc, Q = om.q6_k_fields(buf, rows, cols, r0, n)
+    return (d[:, None, None] * sc[:, :, None] * (Q + 32)).reshape(n, cols)
+
+
+def _q6k_offsets_unpadded(rows, cols):
+    ns = cols // 256
+    return 2 * rows * ns, 18 * rows * ns, 146 * rows * ns
+
+
 def _q8_offset_unpadded(rows, cols):
     return 2 * rows * (cols // 32)
 
@@ -178,6 +205,10 @@ MUTATIONS = {
     "q3k_scale_offset": ("dequant_q3_k", _q3k_no_scale_offset),
     "q3k_quant_offset_sign": ("dequant_q3_k", _q3k_quant_offset_sign),
     "q3k_plane_offsets": ("q3_k_offsets", _q3k_offsets_unpadded),
+    "q6k_high_pairs": ("q6_k_fields", _q6k_fields_high_pairs_swapped),
+    "q6k_unsigned_scales": ("q6_k_fields", _q6k_fields_unsigned_scales),
+    "q6k_offset_sign": ("dequant_q6_k", _q6k_offset_sign),
+    "q6k_plane_offsets": ("q6_k_offsets", _q6k_offsets_unpadded),
     "tie_to_higher": ("select_experts", _select_high_tie),
     "no_renormalise": ("routing_weights", _weights_unnormalised),
     "silu_is_sigmoid": ("silu", _sigmoid_only),

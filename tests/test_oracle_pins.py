@@ -31,7 +31,7 @@ def test_f16_decode_all_bit_patterns_match_numpy():
 
 
 FIXTURES = [("q8_0_planar.txt", "q8_0"), ("q4_k_planar.txt", "q4_k"), ("q2_k_planar.txt", "q2_k"),
-            ("q3_k_planar.txt", "q3_k")]
+            ("q3_k_planar.txt", "q3_k"), ("q6_k_planar.txt", "q6_k")]
 
 
 @pytest.mark.parametrize("fixture,dtype", FIXTURES)
@@ -250,6 +250,70 @@ def test_q3_k_multi_row_record_order():
     assert np.array_equal(om.dequant_q3_k(buf, 3, 512, row_start=2, row_count=1), W[2:3])
 
 
+def _q6k_tensor(recs, rows, cols):
+    """Planar Q6_K bytes from records (d_bits, sc[16] signed, Q[16][16])
+    (test-side encoder, from the layout: plane starts rounded up to 256
+    bytes; weight i of 32-weight group g: low nibble in byte 16g + i // 2,
+    high two bits at byte 8g + 4 (i // 16) + (i % 8) // 2, bit
+    4 ((i // 8) % 2) + 2 (i % 2); sub-block s = 2g + i // 16).
+    """
+    n = len(recs)
+    so = -(-2 * n // 256) * 256
+    lo = -(-(so + 16 * n) // 256) * 256
+    hi = -(-(lo + 128 * n) // 256) * 256
+    out = bytearray(hi + 64 * n)
+    for k, (db, sc, Q) in enumerate(recs):
+        out[2 * k: 2 * k + 2] = int(db).to_bytes(2, "little")
+        for s in range(16):
+            out[so + 16 * k + s] = sc[s] & 255
+        for g in range(8):
+            for i in range(32):
+                q = Q[2 * g + i // 16][i % 16]
+                out[lo + 128 * k + 16 * g + i // 2] |= (q & 15) << (4 * (i % 2))
+                out[hi + 64 * k + 8 * g + 4 * (i // 16) + (i % 8) // 2] |= \
+                    ((q >> 4) & 3) << (4 * ((i // 8) % 2) + 2 * (i % 2))
+    assert len(out) == synth.tensor_bytes("q6_k", rows, cols)
+    return np.frombuffer(bytes(out), dtype=np.uint8).copy()
+
+
+@pytest.mark.parametrize("s", [0, 1, 7, 10, 15])
+def test_q6_k_single_field_positions(s):
+    # Every quant at the zero point Q = 32 except one: exactly one non-zero
+    # weight, at column 16*s + i, with value sc * (Q - 32).
+    for i in (0, 1, 2, 7, 8, 9, 14, 15):
+        for q in (0, 17, 31, 33, 48, 63):         # every high-bit value
+            Q = [[32] * 16 for _ in range(16)]
+            Q[s][i] = q
+            sc = [3] * 16
+            sc[s] = -5 - s
+            buf = _q6k_tensor([(0x3C00, sc, Q)], 1, 256)
+            W = om.dequant_q6_k(buf, 1, 256)[0]
+            assert list(np.nonzero(W)[0]) == [16 * s + i]
+            assert W[16 * s + i] == (-5 - s) * (q - 32)
+    # All quants zero: sub-block s is -32 * sc_s * d throughout.
+    sc = [0] * 16
+    sc[s] = 127 if s % 2 else -128
+    buf = _q6k_tensor([(0x3800, sc, [[0] * 16 for _ in range(16)])], 1, 256)
+    W = om.dequant_q6_k(buf, 1, 256)[0]
+    exp = np.zeros(256)
+    exp[16 * s:16 * s + 16] = 0.5 * sc[s] * -32
+    assert np.array_equal(W, exp)
+
+
+def test_q6_k_multi_row_record_order():
+    recs = []
+    for r in range(3):
+        for b in range(2):
+            v = r * 2 + b + 1          # 1..6
+            recs.append((0x3C00, [v] * 16, [[33] * 16 for _ in range(16)]))
+    buf = _q6k_tensor(recs, 3, 512)
+    W = om.dequant_q6_k(buf, 3, 512)
+    for r in range(3):
+        for b in range(2):
+            assert np.all(W[r, 256 * b:256 * (b + 1)] == r * 2 + b + 1)
+    assert np.array_equal(om.dequant_q6_k(buf, 3, 512, row_start=1, row_count=1), W[1:2])
+
+
 def test_q8_0_row_slice_matches_full():
     cfg = small_config(n_experts=3, ffn=64)
     inp = synth.draw_layer(cfg, threads=1)
@@ -354,7 +418,8 @@ def test_silu_is_g_times_logistic():
 
 @pytest.mark.parametrize("etype,H,F,Fs,E", [("q8_0", 256, 128, 0, 8), ("q8_0", 256, 64, 96, 4),
                                              ("q4_k", 256, 256, 64, 4), ("q2_k", 256, 256, 64, 4),
-                                             ("q2_k/q3_k", 256, 256, 64, 4)])
+                                             ("q2_k/q3_k", 256, 256, 64, 4),
+                                             ("q6_k", 256, 256, 64, 4)])
 def test_oracle_matches_scalar_twin(etype, H, F, Fs, E):
     etype, _, dtype = etype.partition("/")
     cfg = small_config(hidden=H, ffn=F, shared_ffn=Fs, n_experts=E, expert_type=etype,
@@ -399,7 +464,7 @@ def test_identical_experts_make_routing_irrelevant():
     assert np.allclose(ref["y"], one, rtol=1e-12, atol=1e-12 * np.abs(one).max())
 
 
-@pytest.mark.parametrize("etype", ["q8_0", "q4_k", "q2_k", "q3_k"])
+@pytest.mark.parametrize("etype", ["q8_0", "q4_k", "q2_k", "q3_k", "q6_k"])
 def test_doubling_down_scales_doubles_routed_part_exactly(etype):
     F = 128 if etype == "q8_0" else 256
     cfg = small_config(n_experts=4, ffn=F, shared_ffn=64, expert_type=etype, n_tokens=2)
@@ -481,6 +546,18 @@ def test_q3_k_generated_fields_cover_their_ranges():
     assert Q.min() == 0 and Q.max() == 7
     counts = np.bincount(Q.reshape(-1), minlength=8) / Q.size
     assert np.all(np.abs(counts - 0.125) < 0.01)
+
+
+def test_q6_k_generated_fields_cover_their_ranges():
+    cfg = small_config(n_experts=4, expert_type="q6_k", ffn=256)
+    inp = synth.draw_layer(cfg, threads=1)
+    assert inp.gate.size == synth.tensor_bytes("q6_k", 4 * 256, 256)
+    d, sc, Q = om.q6_k_fields(inp.gate, 4 * 256, 256)
+    assert d.min() >= 2.0 ** -14 and d.max() <= 2.0 ** -12
+    assert sc.min() == -128 and sc.max() == 127
+    assert Q.min() == 0 and Q.max() == 63
+    counts = np.bincount(Q.reshape(-1), minlength=64) / Q.size
+    assert np.all(np.abs(counts - 1 / 64) < 0.004)
 
 
 def test_margin_predicate_enforces_gaps():
