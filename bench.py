@@ -55,7 +55,7 @@ def traffic_file(kernel: str, workload: str) -> str:
 def _bytes_per_row(dtype: str, cols: int) -> float:
     if dtype == "q8_0":
         return cols // 32 * 34
-    return cols // 256 * {"q4_k": 144, "q2_k": 84, "q3_k": 114}[dtype]
+    return cols // 256 * {"q4_k": 144, "q2_k": 84, "q3_k": 114, "q6_k": 210}[dtype]
 
 
 def layer_bytes(cfg, distinct: int, batched: bool = False) -> dict:
@@ -451,9 +451,11 @@ def main(argv=None) -> int:
     # Arithmetic of the expert products: integer quants times 16-bit integer
     # activations (int8 limbs, int32 sums, fp32 scales) up to 16 tokens; bf16
     # matrix-core products of exact integer quants and split activations above
-    # (Q2_K and Q3_K experts stay on the integer path at every batch size).
-    low_bit = cfg.expert_type in ("q2_k", "q3_k") or cfg.routed_down_type in ("q2_k", "q3_k")
-    dtype = "i8xi16->i32+f32" if M <= 16 or low_bit else "bf16x2->f32"
+    # (Q2_K, Q3_K and Q6_K experts, and mixed gate/up and down types, stay on
+    # the integer path at every batch size).
+    gemv_only = ("q2_k", "q3_k", "q6_k")
+    int_path = (M <= 16 or cfg.expert_type in gemv_only or cfg.routed_down_type != cfg.expert_type)
+    dtype = "i8xi16->i32+f32" if int_path else "bf16x2->f32"
     out = {
         "metric": metric,
         "value": round(value, 1),

@@ -18,8 +18,8 @@ import torch  # load torch first: the library then binds to torch's HIP runtime
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "lib", "libsvr_moe.so")
 
-F32, Q8_0, Q4_K, Q2_K, Q3_K = 0, 1, 2, 3, 4
-_DTYPES = {"f32": F32, "q8_0": Q8_0, "q4_k": Q4_K, "q2_k": Q2_K, "q3_k": Q3_K}
+F32, Q8_0, Q4_K, Q2_K, Q3_K, Q6_K = 0, 1, 2, 3, 4, 5
+_DTYPES = {"f32": F32, "q8_0": Q8_0, "q4_k": Q4_K, "q2_k": Q2_K, "q3_k": Q3_K, "q6_k": Q6_K}
 
 OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_WORKSPACE, ERR_LAUNCH, ERR_ARG = range(7)
 

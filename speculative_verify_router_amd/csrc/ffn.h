@@ -1,6 +1,6 @@
 // Fused dequantise-and-multiply skinny GEMM for the expert FFNs.
 //
-// Routed gate/up/down are Q4_K, Q2_K, Q3_K or Q8_0 and the shared expert Q8_0
+// Routed gate/up/down are Q4_K, Q2_K, Q3_K, Q6_K or Q8_0 and the shared expert Q8_0
 // ("Step 3.7 Flash Mixed-Quant GGUF", Tensor recipe; "Step-5 Preview GGUF",
 // Precision distribution table and Tensor-type table).  At a verify batch of four tokens with 8
 // of 288-352 experts each, an expert serves about one token, so this is an
@@ -9,8 +9,8 @@
 //
 // Mapping.  A 16-byte chunk of the quant plane is the unit of loading:
 // 16 weights for Q8_0, one 32-weight sub-block for Q4_K, four 16-weight
-// sub-blocks for Q2_K and Q3_K (low bits; the high bits come from a plane
-// of their own).  A row of K
+// sub-blocks for Q2_K and Q3_K, two for Q6_K (low bits; Q3_K's and Q6_K's
+// high bits come from a plane of their own).  A row of K
 // columns has K / kWpc chunks, covered by a group of `lpr` consecutive
 // lanes (lpr | 64), lane j of the group taking chunks j, j+lpr, ...,
 // j+(CPL-1)*lpr.  A wave works on 64/lpr rows at once and every wave load
@@ -62,7 +62,9 @@ constexpr int shape_cpl(int code) { return code & 255; }
 constexpr int shape_lpr(int code) { return code >> 8; }
 
 // Tokens per pass: keep the per-lane activation slice within 64 floats.
-constexpr int wpc_for(int fmt) { return fmt == kQ8_0 ? 16 : fmt == kQ4_K ? 32 : 64; }
+constexpr int wpc_for(int fmt) {
+  return fmt == kQ8_0 ? 16 : (fmt == kQ4_K || fmt == kQ6_K) ? 32 : 64;
+}
 constexpr int tp_for(int fmt, int cpl) {
   return (cpl * wpc_for(fmt) <= 16) ? 4 : (cpl * wpc_for(fmt) <= 32) ? 2 : 1;
 }
@@ -74,7 +76,7 @@ constexpr int tp_for(int fmt, int cpl) {
 #endif
 constexpr int kRingVgprs = SVR_RING_VGPRS;
 constexpr int chunk_vgprs(int fmt) {
-  return fmt == kQ8_0 ? 5 : fmt == kQ4_K ? 8 : fmt == kQ2_K ? 6 : 8;
+  return fmt == kQ8_0 ? 5 : fmt == kQ4_K ? 8 : fmt == kQ2_K ? 6 : 8;  // Q3_K, Q6_K: 8
 }
 constexpr int nst_for(int fmt, int cpl, bool gateup) {
   return (cpl * (gateup ? 2 : 1) * chunk_vgprs(fmt) * 5 <= kRingVgprs)   ? 5

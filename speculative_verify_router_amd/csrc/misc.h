@@ -31,7 +31,9 @@ __global__ __launch_bounds__(kBlock) void k_combine(const float* __restrict__ o,
 // Dequantise rows [r0, r0 + n) of a planar tensor into out[n][cols].
 // Q8_0: d*q.  Q4_K and Q2_K: fma(d*sc, q, -(dmin*m)); d*sc and dmin*m are
 // exact in fp32, so the result is the correctly rounded block value.  Q3_K:
-// (d*(S-32))*(Q-4), exact (at most 20 significant bits).
+// (d*(S-32))*(Q-4), exact (at most 20 significant bits).  Q6_K:
+// (d*sc)*(Q-32), exact (d*sc has at most 18 significant bits and
+// |Q-32| <= 32 adds at most 5).
 __global__ __launch_bounds__(kBlock) void k_dequant(int fmt, const uint8_t* __restrict__ base,
                                                     int64_t rows, int cols, int64_t r0, int64_t n,
                                                     float* __restrict__ out) {
@@ -72,6 +74,19 @@ __global__ __launch_bounds__(kBlock) void k_dequant(int fmt, const uint8_t* __re
       const uint32_t lo = (base[loff + 64 * rec + 4 * s + (wi & 3)] >> (2 * (wi >> 2))) & 3u;
       const uint32_t hi = (base[hoff + 32 * rec + 4 * (s >> 1) + (wi & 3)] >> (4 * (s & 1) + (wi >> 2))) & 1u;
       v = (d * (float)S) * (float)((int)(lo | (hi << 2)) - 4);
+    } else if (fmt == MOE_Q6_K) {
+      const int64_t n_sb = rows * (cols >> 8);
+      const int64_t soff = (2 * n_sb + 255) & ~(int64_t)255;
+      const int64_t loff = (soff + 16 * n_sb + 255) & ~(int64_t)255;
+      const int64_t hoff = (loff + 128 * n_sb + 255) & ~(int64_t)255;
+      const int64_t rec = r * (cols >> 8) + (c >> 8);
+      const float d = f16_to_f32((uint32_t)base[2 * rec] | ((uint32_t)base[2 * rec + 1] << 8));
+      const int g = (c >> 5) & 7, wi = c & 31;
+      const int sc = (int)(int8_t)base[soff + 16 * rec + 2 * g + (wi >> 4)];
+      const uint32_t lo = (base[loff + 128 * rec + 16 * g + (wi >> 1)] >> (4 * (wi & 1))) & 15u;
+      const uint32_t hi = (base[hoff + 64 * rec + 8 * g + 4 * (wi >> 4) + ((wi & 7) >> 1)] >>
+                           (4 * ((wi >> 3) & 1) + 2 * (wi & 1))) & 3u;
+      v = (d * (float)sc) * (float)((int)(lo | (hi << 4)) - 32);
     } else {
       const int64_t ns = cols >> 8;
       const int64_t rec = r * ns + (c >> 8);

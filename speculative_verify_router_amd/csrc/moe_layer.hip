@@ -56,19 +56,31 @@ constexpr double kFlowSharedWaveBytes = 64.0 * 1024.0;
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-int wpc_of(int dtype) { return dtype == MOE_Q8_0 ? 16 : dtype == MOE_Q4_K ? 32 : 64; }
+int wpc_of(int dtype) {
+  return dtype == MOE_Q8_0 ? 16 : (dtype == MOE_Q4_K || dtype == MOE_Q6_K) ? 32 : 64;
+}
 int blk_of(int dtype) { return dtype == MOE_Q8_0 ? 32 : 256; }
-// Types of the shared expert, and of the routed experts (also Q2_K, Q3_K).
+// Types of the shared expert, and of the routed experts (also Q2_K, Q3_K,
+// Q6_K, which have GEMV kernels only).
 bool quant_type(int dtype) { return dtype == MOE_Q8_0 || dtype == MOE_Q4_K; }
-bool low_bit_type(int dtype) { return dtype == MOE_Q2_K || dtype == MOE_Q3_K; }
-bool routed_type(int dtype) { return quant_type(dtype) || low_bit_type(dtype); }
+bool gemv_only_type(int dtype) {
+  return dtype == MOE_Q2_K || dtype == MOE_Q3_K || dtype == MOE_Q6_K;
+}
+bool routed_type(int dtype) { return quant_type(dtype) || gemv_only_type(dtype); }
 int qfmt(int dtype) {
-  return dtype == MOE_Q8_0 ? kQ8_0 : dtype == MOE_Q4_K ? kQ4_K : dtype == MOE_Q2_K ? kQ2_K : kQ3_K;
+  switch (dtype) {
+    case MOE_Q8_0: return kQ8_0;
+    case MOE_Q4_K: return kQ4_K;
+    case MOE_Q2_K: return kQ2_K;
+    case MOE_Q3_K: return kQ3_K;
+    default: return kQ6_K;
+  }
 }
 
 // Lanes per row and 16-byte chunks per lane for a row of K columns.  The
 // shape keeps the per-lane activation slice within 96 floats (Q4_K: 3
-// chunks of 32, Q8_0: 6 chunks of 16, Q2_K and Q3_K: 1 chunk of 64) where possible and wastes the fewest
+// chunks of 32, Q8_0: 6 chunks of 16, Q2_K and Q3_K: 1 chunk of 64, Q6_K: 3
+// chunks of 32) where possible and wastes the fewest
 // lane positions (chunk positions past the row's end load the row's last
 // chunk against a zero activation); among equal shapes the fewest chunks
 // per lane.  Rows too long for that take 64 lanes and up to 8 chunks.
@@ -253,7 +265,7 @@ int tiles_of(const FfnArgs& a) {
 // Bytes per weight row of K columns.
 double row_bytes(int dtype, int K) {
   if (dtype == MOE_Q8_0) return K / 32 * 34.0;
-  return K / 256 * (dtype == MOE_Q4_K ? 144.0 : dtype == MOE_Q2_K ? 84.0 : 114.0);
+  return K / 256 * (dtype == MOE_Q4_K ? 144.0 : dtype == MOE_Q2_K ? 84.0 : dtype == MOE_Q3_K ? 114.0 : 210.0);
 }
 
 // Single-role launches, every (format, chunks-per-lane) pair.
@@ -285,6 +297,9 @@ bool launch_ffn(int dtype, bool gateup, FfnArgs a, int slots_max, hipStream_t st
   if (dtype == MOE_Q3_K)
     return gateup ? launch_ffn_c<kQ3_K, true>(s.cpl, a, dtype, slots_max, st)
                   : launch_ffn_c<kQ3_K, false>(s.cpl, a, dtype, slots_max, st);
+  if (dtype == MOE_Q6_K)
+    return gateup ? launch_ffn_c<kQ6_K, true>(s.cpl, a, dtype, slots_max, st)
+                  : launch_ffn_c<kQ6_K, false>(s.cpl, a, dtype, slots_max, st);
   return gateup ? launch_ffn_c<kQ4_K, true>(s.cpl, a, dtype, slots_max, st)
                 : launch_ffn_c<kQ4_K, false>(s.cpl, a, dtype, slots_max, st);
 }
@@ -374,8 +389,9 @@ bool launch_dual_keys(int akey, int bkey, hipStream_t st, const FfnArgs& a, cons
   SVR_D(kQ4_K, 2, 64, kQ8_0, 5, 16) SVR_D(kQ4_K, 2, 64, kQ8_0, 3, 32)
   SVR_D(kQ8_0, 4, 64, kQ8_0, 5, 16) SVR_D(kQ8_0, 4, 64, kQ8_0, 3, 32)
   SVR_D(kQ2_K, 1, 64, kQ8_0, 5, 16) SVR_D(kQ2_K, 1, 64, kQ8_0, 3, 32)
+  SVR_D(kQ6_K, 2, 64, kQ8_0, 5, 16)
   SVR_DG(kQ4_K, 1) SVR_DG(kQ4_K, 2) SVR_DG(kQ4_K, 3) SVR_DG(kQ8_0, 4) SVR_DG(kQ2_K, 1)
-  SVR_DG(kQ3_K, 1)
+  SVR_DG(kQ3_K, 1) SVR_DG(kQ6_K, 2)
 #undef SVR_DG
 #undef SVR_D
   return false;
@@ -421,7 +437,7 @@ bool launch_down_tok(int dtype, const FfnShape& ds, hipStream_t st, const FfnArg
     SVR_DT(kQ4_K, 1, 0) SVR_DT(kQ4_K, 2, 0) SVR_DT(kQ4_K, 3, 0) SVR_DT(kQ8_0, 1, 0)
     SVR_DT(kQ8_0, 2, 0) SVR_DT(kQ8_0, 3, 0) SVR_DT(kQ8_0, 4, 0) SVR_DT(kQ8_0, 5, 0)
     SVR_DT(kQ8_0, 6, 0) SVR_DT(kQ2_K, 1, 32) SVR_DT(kQ2_K, 1, 0) SVR_DT(kQ3_K, 1, 32)
-    SVR_DT(kQ3_K, 1, 0)
+    SVR_DT(kQ3_K, 1, 0) SVR_DT(kQ6_K, 3, 16) SVR_DT(kQ6_K, 3, 0) SVR_DT(kQ6_K, 1, 0)
   }
 #undef SVR_DT
   return false;
@@ -446,6 +462,7 @@ bool launch_down_combine_key(int k, hipStream_t st, const FfnArgs& a, const Comb
   SVR_DC(kQ4_K, 1, 0) SVR_DC(kQ4_K, 2, 0) SVR_DC(kQ4_K, 3, 0) SVR_DC(kQ8_0, 1, 0) SVR_DC(kQ8_0, 2, 0)
   SVR_DC(kQ8_0, 3, 0) SVR_DC(kQ8_0, 4, 0) SVR_DC(kQ8_0, 5, 0) SVR_DC(kQ8_0, 6, 0)
   SVR_DC(kQ2_K, 1, 32) SVR_DC(kQ2_K, 1, 0) SVR_DC(kQ3_K, 1, 32) SVR_DC(kQ3_K, 1, 0)
+  SVR_DC(kQ6_K, 3, 16) SVR_DC(kQ6_K, 3, 0)
 #undef SVR_DC
   return false;
 }
@@ -741,8 +758,8 @@ const char* const kGemmStageNames[kGemmStages] = {"route", "shared_gateup", "gat
 
 bool gemm_path(const Plan& p) {
   if (p.M <= kFusedMaxTokens) return false;
-  // no matrix-core decoder for the 2- and 3-bit types
-  if (low_bit_type(p.et) || low_bit_type(p.dt)) return false;
+  // no matrix-core decoder for the Q2_K, Q3_K and Q6_K types
+  if (gemv_only_type(p.et) || gemv_only_type(p.dt)) return false;
   if (p.dt != p.et) return false;  // the down GEMMs decode the gate/up type
   // Split activations and h are addressed with 32-bit byte offsets.
   const int64_t P = (int64_t)p.M * p.k;
@@ -1024,6 +1041,14 @@ int32_t moe_tensor_bytes(int32_t dtype, int64_t rows, int64_t cols, int64_t* byt
       const int64_t s = (int64_t)align256((size_t)(2 * n));
       const int64_t l = (int64_t)align256((size_t)(s + 16 * n));
       *bytes = (int64_t)align256((size_t)(l + 64 * n)) + 32 * n;
+      return MOE_OK;
+    }
+    case MOE_Q6_K: {
+      if (cols % 256) return MOE_ERR_SHAPE;
+      const int64_t n = rows * (cols / 256);
+      const int64_t s = (int64_t)align256((size_t)(2 * n));
+      const int64_t l = (int64_t)align256((size_t)(s + 16 * n));
+      *bytes = (int64_t)align256((size_t)(l + 128 * n)) + 64 * n;
       return MOE_OK;
     }
     default: return MOE_ERR_DTYPE;

@@ -1,4 +1,4 @@
-// Planar Q8_0 / Q4_K / Q2_K / Q3_K blocks: 16-byte chunk loads, scale
+// Planar Q8_0 / Q4_K / Q2_K / Q3_K / Q6_K blocks: 16-byte chunk loads, scale
 // decoding and the fused dequantise-and-dot of one chunk against 16-bit
 // activations.
 //
@@ -7,8 +7,10 @@
 // sc, m, 4-bit q, w = d*sc*q - dmin*m; Q2_K super-blocks of 256 with fp16
 // d, dmin and per-16 4-bit sc, m, 2-bit q, the same rule; Q3_K
 // super-blocks of 256 with fp16 d and per-16 6-bit S, 3-bit Q,
-// w = d*(S-32)*(Q-4) ("Step-5 Preview GGUF" and "Step 3.7 Flash Mixed-Quant
-// GGUF" name these tensor types; their bit layouts are this library's).
+// w = d*(S-32)*(Q-4); Q6_K super-blocks of 256 with fp16 d and per-16 int8
+// sc, 6-bit Q, w = d*sc*(Q-32) ("Step-5 Preview GGUF" and "Step 3.7 Flash
+// Mixed-Quant GGUF" name these tensor types; their bit layouts are this
+// library's).
 //
 // Dot product.  The weights' integer quants go into v_dot4_i32_i8 as they
 // are: a Q8_0 quant dword is four int8 weights; a Q4_K dword (8 nibbles,
@@ -16,7 +18,9 @@
 // weights with one AND and the odd ones with a shift and an AND; a Q2_K
 // dword is one 16-weight sub-block whose four 2-bit planes (weights
 // 4j..4j+3 in bits 2j of each byte) come out with a shift and an AND each,
-// and Q3_K adds each plane's high bits with one more shift and an AND-OR.
+// and Q3_K adds each plane's high bits with one more shift and an AND-OR;
+// Q6_K's low nibbles come out as Q4_K's and take their two high bits the
+// same way.
 // The activations enter as 16-bit integers in two int8 limbs (XSlice below),
 // so each chunk's dot product is exact in int32 and the block scales are
 // applied once per chunk in fp32.
@@ -26,7 +30,7 @@
 
 namespace svr {
 
-enum QFmt { kQ8_0 = 1, kQ4_K = 2, kQ2_K = 3, kQ3_K = 4 };
+enum QFmt { kQ8_0 = 1, kQ4_K = 2, kQ2_K = 3, kQ3_K = 4, kQ6_K = 5 };
 
 template <int FMT>
 struct QTraits;
@@ -46,6 +50,10 @@ template <>
 struct QTraits<kQ3_K> {
   static constexpr int kWpc = 64;
 };
+template <>
+struct QTraits<kQ6_K> {
+  static constexpr int kWpc = 32;  // two 16-weight sub-blocks of low nibbles
+};
 
 // The planes of one expert's rows of a stacked planar tensor, as buffer
 // resources (32-bit offsets; reads past the expert's rows return zero).
@@ -55,6 +63,8 @@ struct QTraits<kQ3_K> {
 // per row, so a row's offset there is its plane-s offset / 4.  Q3_K keeps
 // fp16 d in plane d (K/128 bytes per row: offset / 8), its low quant bits
 // in plane q and its high bits in plane h (K/8 bytes per row: offset * 2).
+// Q6_K: the same four planes with K/2 bytes of low nibbles per row in plane
+// q and K/4 bytes of high bit pairs in plane h (offset * 4).
 struct QPlanes {
   __amdgpu_buffer_rsrc_t q, s, d, h;
   uint32_t qrow, srow;  // bytes per row in planes q and s
@@ -67,10 +77,12 @@ __device__ __forceinline__ QPlanes expert_planes(const uint8_t* base, int64_t to
                                                  int64_t row0, int rows) {
   QPlanes p;
   p.srow = (uint32_t)(K >> 4);
-  p.qrow = (FMT == kQ8_0) ? (uint32_t)K : (FMT == kQ4_K) ? (uint32_t)(K >> 1) : (uint32_t)(K >> 2);
+  p.qrow = (FMT == kQ8_0)                    ? (uint32_t)K
+           : (FMT == kQ4_K || FMT == kQ6_K) ? (uint32_t)(K >> 1)
+                                            : (uint32_t)(K >> 2);
   const int64_t sbytes = total_rows * (int64_t)p.srow;
-  if constexpr (FMT == kQ3_K) {
-    const uint32_t drow = (uint32_t)(K >> 7), hrow = (uint32_t)(K >> 3);
+  if constexpr (FMT == kQ3_K || FMT == kQ6_K) {
+    const uint32_t drow = (uint32_t)(K >> 7), hrow = (uint32_t)(FMT == kQ3_K ? K >> 3 : K >> 2);
     const int64_t sstart = round256(total_rows * (int64_t)drow);
     const int64_t qstart = round256(sstart + sbytes);
     const int64_t hstart = round256(qstart + total_rows * (int64_t)p.qrow);
@@ -120,6 +132,13 @@ struct Chunk<kQ3_K> {
   uint32_t sc;   // byte k: S of sub-block k
   uint32_t d;    // fp16 d (low half)
 };
+template <>
+struct Chunk<kQ6_K> {
+  uint4 q;       // low nibbles of the 32-weight group c (as a Q4_K chunk)
+  uint2 hb;      // high bit pairs; dword t: group dwords 2t, 2t + 1
+  uint32_t sc;   // bytes 0, 1: int8 scales of sub-blocks 2c, 2c + 1
+  uint32_t d;    // fp16 d (low half)
+};
 
 // Chunk c of a row whose plane offsets are qo = row * qrow and so = row * srow.
 __device__ __forceinline__ void load_chunk(Chunk<kQ8_0>& ch, const QPlanes& p, uint32_t qo,
@@ -144,6 +163,13 @@ __device__ __forceinline__ void load_chunk(Chunk<kQ3_K>& ch, const QPlanes& p, u
   ch.hb = bload8(p.h, 2u * so + 8u * c);
   ch.sc = bload4(p.s, so + 4u * c);
   ch.d = bload2(p.d, (so >> 3) + 2u * (c >> 2));
+}
+__device__ __forceinline__ void load_chunk(Chunk<kQ6_K>& ch, const QPlanes& p, uint32_t qo,
+                                           uint32_t so, int c) {
+  ch.q = bload16(p.q, qo + 16u * c);
+  ch.hb = bload8(p.h, 4u * so + 8u * c);
+  ch.sc = bload2(p.s, so + 2u * c);
+  ch.d = bload2(p.d, (so >> 3) + 2u * (c >> 3));
 }
 
 // Activations of one chunk position for one token, as 16-bit integers.
@@ -187,6 +213,12 @@ struct XSlice<kQ3_K> {
   float s;
   int nsum4[4];  // -4 * (sum of the quantised activations) of sub-block k
 };
+template <>
+struct XSlice<kQ6_K> {
+  uint32_t h[8], l[8];  // as for Q4_K (even / odd weights of each dword)
+  float s;
+  int nsum32[2];  // -32 * (sum of the quantised activations) of sub-block k
+};
 
 constexpr float kQ16Max = 32639.0f;     // |q| bound: hi = (q + 128) >> 8 stays in int8
 constexpr float kQ16Magic = 12583040.0f;  // 1.5 * 2^23 + 128
@@ -220,14 +252,24 @@ __device__ __forceinline__ void quantize_slice(XSlice<FMT>& xs, const float (&v)
     y[i] = fmaf(v[i], inv, kQ16Magic);
     bsum += __builtin_bit_cast(uint32_t, y[i]);
   }
-  if constexpr (FMT == kQ4_K) {
+  if constexpr (FMT == kQ4_K || FMT == kQ6_K) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const float* g = y + 8 * k;
       limbs4(g[0], g[2], g[4], g[6], xs.h[2 * k], xs.l[2 * k]);
       limbs4(g[1], g[3], g[5], g[7], xs.h[2 * k + 1], xs.l[2 * k + 1]);
     }
-    xs.sum = xs.s * (float)(int32_t)(bsum - (uint32_t)N * kQ16MagicBits);
+    if constexpr (FMT == kQ4_K) {
+      xs.sum = xs.s * (float)(int32_t)(bsum - (uint32_t)N * kQ16MagicBits);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        uint32_t b = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) b += __builtin_bit_cast(uint32_t, y[16 * k + i]);
+        xs.nsum32[k] = -32 * (int32_t)(b - 16u * kQ16MagicBits);
+      }
+    }
   } else if constexpr (FMT == kQ2_K) {
 #pragma unroll
     for (int k = 0; k < 16; ++k) limbs4(y[4 * k], y[4 * k + 1], y[4 * k + 2], y[4 * k + 3], xs.h[k], xs.l[k]);
@@ -296,7 +338,7 @@ __device__ __forceinline__ void load_x_shared(XSlice<FMT>& xs, const float* base
 
 template <int FMT>
 __device__ __forceinline__ void zero_x(XSlice<FMT>& xs) {
-  constexpr int D = (FMT == kQ2_K || FMT == kQ3_K) ? 16 : FMT == kQ4_K ? 8 : 4;
+  constexpr int D = (FMT == kQ2_K || FMT == kQ3_K) ? 16 : (FMT == kQ4_K || FMT == kQ6_K) ? 8 : 4;
 #pragma unroll
   for (int i = 0; i < D; ++i) xs.h[i] = xs.l[i] = 0u;
   xs.s = 0.f;
@@ -306,6 +348,8 @@ __device__ __forceinline__ void zero_x(XSlice<FMT>& xs) {
   } else if constexpr (FMT == kQ3_K) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) xs.nsum4[k] = 0;
+  } else if constexpr (FMT == kQ6_K) {
+    xs.nsum32[0] = xs.nsum32[1] = 0;
   } else {
     xs.sum = 0.f;
   }
@@ -363,6 +407,10 @@ __device__ __forceinline__ ChunkScale decode_scale(const Chunk<kQ2_K>& ch, int /
 
 // Q3_K: a = d (the 6-bit scales are applied inside chunk_fma).
 __device__ __forceinline__ ChunkScale decode_scale(const Chunk<kQ3_K>& ch, int /*sub*/) {
+  return {f16_lo(ch.d), 0.f};
+}
+// Q6_K: a = d (the 8-bit scales are applied inside chunk_fma).
+__device__ __forceinline__ ChunkScale decode_scale(const Chunk<kQ6_K>& ch, int /*sub*/) {
   return {f16_lo(ch.d), 0.f};
 }
 
@@ -466,6 +514,41 @@ __device__ __forceinline__ float chunk_fma(const Chunk<kQ3_K>& ch, const ChunkSc
     tot += __builtin_amdgcn_sbfe(dsub, 0, 24) * sc;
   }
   return fmaf(k.a * xs.s, (float)tot, acc);
+}
+
+// Q6_K: dword k of the group's low nibbles gives its even / odd weights as
+// Q4_K does; their high bit pairs sit at bits 4 (k % 2) / 4 (k % 2) + 2 of
+// every byte of high dword k / 2 and move to bits 4..5 with one shift and
+// one AND-OR, so one v_dot4 per limb takes four 6-bit quants Q.  Per
+// sub-block (dwords 2t, 2t + 1) the exact integer sum of (Q - 32) x16 is
+// 256 H + L - 32 sum x16 (|.| <= 16*32*32639 < 2^24, exact in fp32); the
+// signed scales weight the two sub-blocks in fp32 and d*s the chunk.
+__device__ __forceinline__ float chunk_fma(const Chunk<kQ6_K>& ch, const ChunkScale& k,
+                                           const XSlice<kQ6_K>& xs, float acc) {
+  const uint32_t w[4] = {ch.q.x, ch.q.y, ch.q.z, ch.q.w};
+  const uint32_t hw[2] = {ch.hb.x, ch.hb.y};
+  float v = 0.f;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const uint32_t H = hw[t];
+    int h = 0, l = 0;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int d = 2 * t + kk;
+      const uint32_t he = (kk == 0 ? (H << 4) : H) & 0x30303030u;
+      const uint32_t ho = (kk == 0 ? (H << 2) : (H >> 2)) & 0x30303030u;
+      const int e = (int)((w[d] & 0x0F0F0F0Fu) | he);
+      const int o = (int)(((w[d] >> 4) & 0x0F0F0F0Fu) | ho);
+      h = __builtin_amdgcn_sdot4(e, (int)xs.h[2 * d], h, false);
+      h = __builtin_amdgcn_sdot4(o, (int)xs.h[2 * d + 1], h, false);
+      l = __builtin_amdgcn_sdot4(e, (int)xs.l[2 * d], l, false);
+      l = __builtin_amdgcn_sdot4(o, (int)xs.l[2 * d + 1], l, false);
+    }
+    const int dsub = h * 256 + l + xs.nsum32[t];
+    const int sc = __builtin_amdgcn_sbfe((int)ch.sc, 8 * t, 8);
+    v = fmaf((float)sc, (float)dsub, v);
+  }
+  return fmaf(k.a * xs.s, v, acc);
 }
 
 }  // namespace svr

@@ -76,6 +76,8 @@ def test_missing_library_fails_loudly(monkeypatch):
                                              ("q2_k", 1, 256), ("q2_k", 3, 512),
                                              ("q2_k", 352 * 4096, 1536), ("q3_k", 1, 256),
                                              ("q3_k", 5, 768), ("q3_k", 352 * 4096, 1536),
+                                             ("q6_k", 1, 256), ("q6_k", 3, 1280),
+                                             ("q6_k", 288 * 1280, 4096),
                                              ("f32", 3, 5)])
 def test_tensor_bytes_match_the_generator(dtype, rows, cols):
     assert svr.moe_tensor_bytes(dtype, rows, cols) == synth.tensor_bytes(dtype, rows, cols)
@@ -121,6 +123,8 @@ def test_workspace_grows_with_tokens():
     (dict(expert_type="q2_k", ffn=1000), B.ERR_SHAPE),
     (dict(expert_type="q2_k", hidden=65536, shared_ffn=0), B.ERR_SHAPE),  # > 512 chunks a row
     (dict(shared_type="q3_k"), B.ERR_DTYPE),
+    (dict(shared_type="q6_k"), B.ERR_DTYPE),
+    (dict(expert_type="q6_k", hidden=32768, shared_ffn=0), B.ERR_SHAPE),  # > 512 chunks a row
     (dict(expert_type="q2_k", down_type="q3_k", ffn=1000), B.ERR_SHAPE),
     (dict(expert_type="q8_0", down_type="q4_k", ffn=96), B.ERR_SHAPE),  # Q8_0 F fits, Q4_K does not
 ])
@@ -145,6 +149,7 @@ def test_routed_down_type_selects_the_path():
         assert svr.moe_workspace_bytes(mixed, M) > 0
     L = svr.lib()
     assert L.moe_stage_count(ctypes.byref(mixed.c()), 512) == 3
+    assert L.moe_stage_count(ctypes.byref(_desc(expert_type="q6_k").c()), 512) == 3
     # down_type 0 is the gate/up type; a different down type leaves the
     # matrix-core path and the single launch
     assert L.moe_stage_count(ctypes.byref(_desc(down_type="q4_k").c()), 512) == 5

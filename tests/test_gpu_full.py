@@ -4,7 +4,8 @@ benchmark times (same shapes, same token counts, one moe_layer_forward).
 Step-3.5-Flash-shaped decode (M=1, Q8_0), the same layer as the 4-token
 verify batch (Q4_K routed), the Step-5-shaped verify batch with the four
 tokens on disjoint experts (Q4_K, Q2_K, and the Q2_K-Protected2 pairing of
-Q2_K gate/up with Q3_K down), and the 512-token prefill micro-batch, whose
+Q2_K gate/up with Q3_K down), the Step-3.5 verify batch with Q6_K routed
+experts, and the 512-token prefill micro-batch, whose
 FFN outputs the oracle computes for a sample of tokens.
 """
 
@@ -25,7 +26,7 @@ SAMPLE_TOKENS = [0, 1, 2, 255, 256, 400, 510, 511]
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["step35_decode_m1", "step35_verify_m4", "step5_verify_m4",
                                   "step5_q2k_verify_m4", "step5_q2kp2_verify_m4",
-                                  "step5_prefill_m512"])
+                                  "step35_q6k_verify_m4", "step5_prefill_m512"])
 def test_full_config(name):
     cfg = synth.CONFIGS[name]
     log(f"[{name}] drawing layer")
