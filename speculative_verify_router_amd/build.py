@@ -18,9 +18,12 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libsvr_moe.so")
-SOURCES = [os.path.join(CSRC, "moe_layer.hip"), os.path.join(CSRC, "accept.hip")]
+# Translation units, compiled in parallel (the expert-kernel families are
+# split out of moe_layer.hip so that no one unit holds every instantiation).
+SOURCES = [os.path.join(CSRC, f) for f in ("moe_layer.hip", "launch_expert.hip", "launch_ffn.hip",
+                                           "accept.hip")]
 HEADERS = [os.path.join(CSRC, f) for f in ("common.h", "quant.h", "route.h", "ffn.h", "phases.h", "misc.h",
-                                           "flow.h", "gemm.h")] + [
+                                           "flow.h", "gemm.h", "launch.h")] + [
     os.path.join(ROOT, "include", h) for h in ("moe_layer.h", "moe_accept.h")]
 
 ARCH = "gfx950"
@@ -35,7 +38,7 @@ def hipcc() -> str:
 
 def compile_flags(extra=()) -> list:
     return [
-        "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-shared",
+        "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC",
         # No packed-FP32 instructions anywhere in the device code.
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         # MFMA results straight into VGPRs (no AGPR round trip).
@@ -45,21 +48,36 @@ def compile_flags(extra=()) -> list:
     ]
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    os.makedirs(LIBDIR, exist_ok=True)
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *compile_flags(extra), "-o", tmp, *SOURCES]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
+def _report(res, what: str, verbose: bool) -> None:
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed with status {res.returncode}")
+        raise RuntimeError(f"{what} failed with status {res.returncode}")
     if verbose and res.stderr.strip():
         # hipcc's host pass warns that it does not know the packed-fp32 feature.
         lines = [l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l]
         if lines:
             sys.stderr.write("\n".join(lines) + "\n")
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    objdir = os.path.join(LIBDIR, "obj")
+    os.makedirs(objdir, exist_ok=True)
+    objs, procs = [], []
+    for src in SOURCES:
+        obj = os.path.join(objdir, os.path.splitext(os.path.basename(src))[0] + ".o")
+        cmd = [hipcc(), *compile_flags(extra), "-c", "-o", obj, src]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append(subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True))
+        objs.append(obj)
+    for src, p in zip(SOURCES, procs):
+        out, err = p.communicate()
+        _report(subprocess.CompletedProcess(p.args, p.returncode, out, err), f"hipcc {src}", verbose)
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    _report(subprocess.run(cmd, capture_output=True, text=True), "link", verbose)
     os.replace(tmp, LIB)
     return LIB
 

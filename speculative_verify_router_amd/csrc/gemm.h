@@ -66,7 +66,7 @@ __device__ __forceinline__ void split8(const float (&v)[8], uint4& hi, uint4& lo
 }
 
 // x[rows][K] fp32 -> xs[rows][K] split.  One thread per 8 columns.
-__global__ __launch_bounds__(kBlock) void k_split_act(const float* __restrict__ x, int64_t n8,
+static __global__ __launch_bounds__(kBlock) void k_split_act(const float* __restrict__ x, int64_t n8,
                                                       uint4* __restrict__ xs) {
   const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
   if (i >= n8) return;
@@ -90,7 +90,7 @@ struct TileList {
 
 // One workgroup; E <= kMaxExperts.  Exclusive scan of ceil(count / 16)
 // over the experts, then each expert writes its tiles.
-__global__ __launch_bounds__(kBlock) void k_tiles(const int32_t* __restrict__ offsets, int E,
+static __global__ __launch_bounds__(kBlock) void k_tiles(const int32_t* __restrict__ offsets, int E,
                                                   TileList tl) {
   __shared__ int s_wave[kWavesPerBlock];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid >> 6;
@@ -516,7 +516,7 @@ __global__ __launch_bounds__(kBlock) void k_gemm(GemmArgs a) {
 // 16-token x 16-expert tile; its four waves take quarters of H and their
 // partial tiles are added in LDS in a fixed order.
 
-__global__ __launch_bounds__(kBlock) void k_router_mfma(const float* __restrict__ wr,
+static __global__ __launch_bounds__(kBlock) void k_router_mfma(const float* __restrict__ wr,
                                                         const float* __restrict__ x,
                                                         float* __restrict__ logits, int H, int E,
                                                         int M) {

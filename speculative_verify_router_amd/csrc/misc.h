@@ -7,7 +7,7 @@ namespace svr {
 
 // y[t][h] = s[t][h] + sum_{j=0..k-1} w[t][j] * o[t*k + j][h], in slot order.
 // One thread per 4 consecutive outputs (float4 loads/stores).
-__global__ __launch_bounds__(kBlock) void k_combine(const float* __restrict__ o,
+static __global__ __launch_bounds__(kBlock) void k_combine(const float* __restrict__ o,
                                                     const float* __restrict__ s,
                                                     const float* __restrict__ w,
                                                     float* __restrict__ y, int M, int H, int k) {
@@ -34,7 +34,7 @@ __global__ __launch_bounds__(kBlock) void k_combine(const float* __restrict__ o,
 // (d*(S-32))*(Q-4), exact (at most 20 significant bits).  Q6_K:
 // (d*sc)*(Q-32), exact (d*sc has at most 18 significant bits and
 // |Q-32| <= 32 adds at most 5).
-__global__ __launch_bounds__(kBlock) void k_dequant(int fmt, const uint8_t* __restrict__ base,
+static __global__ __launch_bounds__(kBlock) void k_dequant(int fmt, const uint8_t* __restrict__ base,
                                                     int64_t rows, int cols, int64_t r0, int64_t n,
                                                     float* __restrict__ out) {
   const int64_t total = n * cols;

@@ -34,8 +34,10 @@
 #include "misc.h"
 #include "phases.h"
 #include "route.h"
+#include "launch.h"
 
 using namespace svr;
+using namespace svr::host;
 
 namespace {
 
@@ -53,62 +55,6 @@ constexpr int kFlowTokens = 4;
 // expert item streams (its waves take different tokens over the same rows).
 constexpr double kFlowItemBytes = 256.0 * 1024.0;
 constexpr double kFlowSharedWaveBytes = 64.0 * 1024.0;
-
-inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
-
-int wpc_of(int dtype) {
-  return dtype == MOE_Q8_0 ? 16 : (dtype == MOE_Q4_K || dtype == MOE_Q6_K) ? 32 : 64;
-}
-int blk_of(int dtype) { return dtype == MOE_Q8_0 ? 32 : 256; }
-// Types of the shared expert, and of the routed experts (also Q2_K, Q3_K,
-// Q6_K, which have GEMV kernels only).
-bool quant_type(int dtype) { return dtype == MOE_Q8_0 || dtype == MOE_Q4_K; }
-bool gemv_only_type(int dtype) {
-  return dtype == MOE_Q2_K || dtype == MOE_Q3_K || dtype == MOE_Q6_K;
-}
-bool routed_type(int dtype) { return quant_type(dtype) || gemv_only_type(dtype); }
-int qfmt(int dtype) {
-  switch (dtype) {
-    case MOE_Q8_0: return kQ8_0;
-    case MOE_Q4_K: return kQ4_K;
-    case MOE_Q2_K: return kQ2_K;
-    case MOE_Q3_K: return kQ3_K;
-    default: return kQ6_K;
-  }
-}
-
-// Lanes per row and 16-byte chunks per lane for a row of K columns.  The
-// shape keeps the per-lane activation slice within 96 floats (Q4_K: 3
-// chunks of 32, Q8_0: 6 chunks of 16, Q2_K and Q3_K: 1 chunk of 64, Q6_K: 3
-// chunks of 32) where possible and wastes the fewest
-// lane positions (chunk positions past the row's end load the row's last
-// chunk against a zero activation); among equal shapes the fewest chunks
-// per lane.  Rows too long for that take 64 lanes and up to 8 chunks.
-struct FfnShape {
-  int lpr, cpl;
-};
-bool ffn_shape(int dtype, int K, FfnShape* s) {
-  if (K <= 0 || K % blk_of(dtype)) return false;
-  const int chunks = K / wpc_of(dtype);
-  const int cap = 96 / wpc_of(dtype);
-  double best = 0.0;
-  for (int lpr = 64; lpr >= 1; lpr >>= 1) {
-    const int cpl = (chunks + lpr - 1) / lpr;
-    if (cpl > cap) continue;
-    const double eff = (double)chunks / (double)(lpr * cpl);
-    if (eff > best + 1e-12) {
-      best = eff;
-      s->lpr = lpr;
-      s->cpl = cpl;
-    }
-  }
-  if (best > 0.0) return true;
-  const int cpl = (chunks + kWave - 1) / kWave;
-  if (cpl > kMaxChunksPerLane) return false;
-  s->lpr = kWave;
-  s->cpl = cpl;
-  return true;
-}
 
 struct Plan {
   int H, E, k, F, Fs, et, st, dt, M, flags;  // dt: routed down type
@@ -180,138 +126,6 @@ int make_plan(const moe_layer_desc* d, int M, Plan* p) {
   return MOE_OK;
 }
 
-// --------------------------------------------------------------------------
-// Work split.  Every launch is sized to about one round of resident
-// workgroups (CUs x workgroups per CU for that kernel), since a partial
-// second round costs a whole extra pass of latency.  A role's rows are cut
-// into tiles of a whole number of wave steps.
-// --------------------------------------------------------------------------
-int device_cus() {
-  static int cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (!cache[dev]) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
-      n = 256;
-    cache[dev] = n;
-  }
-  return cache[dev];
-}
-
-// Workgroups of `kernel` resident at once on the device: CUs x the
-// occupancy query, cached per kernel.
-template <typename K>
-int resident_blocks(K kernel) {
-  static std::mutex mu;
-  static std::unordered_map<const void*, int> per_cu;
-  const void* key = reinterpret_cast<const void*>(kernel);
-  int v = 0;
-  {
-    std::lock_guard<std::mutex> lock(mu);
-    auto it = per_cu.find(key);
-    if (it != per_cu.end()) v = it->second;
-  }
-  if (!v) {
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, kernel, kBlock, 0) != hipSuccess || v < 1)
-      v = 1;
-    std::lock_guard<std::mutex> lock(mu);
-    per_cu[key] = v;
-  }
-  return v * device_cus();
-}
-
-// Rows per workgroup for `blocks` workgroups over `slots` experts.
-void size_role(FfnArgs& a, int dtype, int slots, int64_t blocks) {
-  FfnShape s;
-  ffn_shape(dtype, a.K, &s);
-  a.lpr = s.lpr;
-  const int G = kWave / s.lpr;  // rows per wave step
-  const int unit_step = a.split_tokens ? G : kWavesPerBlock * G;
-  int64_t tiles = blocks / (slots > 0 ? slots : 1);
-  // Workgroups go to the 8 XCDs round-robin by linear index (tile fastest):
-  // with a multiple of 8 tiles, every slot's tile t runs on XCD t % 8, so
-  // slots that stream the same expert share that XCD's L2.  Rounded down
-  // only where that leaves at most 1/8 of the round idle.
-  if (tiles >= 8 && tiles % 8 <= tiles / 8) tiles -= tiles % 8;
-  if (tiles < 1) tiles = 1;
-  int64_t upb = (a.rows_per_expert + tiles - 1) / tiles;
-  upb = (upb + unit_step - 1) / unit_step * unit_step;
-  a.units_per_block = (int)upb;
-}
-
-// Shared-expert tiles of phase 1: the workgroup slots of one resident round
-// that the router rows leave free (at least a quarter of the round), each
-// taking an equal share of the rows.  A wave's token group of 4 / M waves
-// shares a tile's rows (see ffn_tile_tokens), so a tile is a whole number
-// of that group's steps.
-void size_shared_tiles(FfnArgs& a, int dtype, int64_t blocks) {
-  FfnShape s;
-  ffn_shape(dtype, a.K, &s);
-  a.lpr = s.lpr;
-  const int G = kWave / s.lpr;
-  const int rg = a.n_tokens < kWavesPerBlock ? kWavesPerBlock / a.n_tokens : 1;
-  const int unit = rg * G;
-  if (blocks < 1) blocks = 1;
-  int64_t rows = (a.rows_per_expert + blocks - 1) / blocks;
-  rows = (rows + unit - 1) / unit * unit;
-  a.units_per_block = (int)rows;
-}
-
-int tiles_of(const FfnArgs& a) {
-  return (a.rows_per_expert + a.units_per_block - 1) / a.units_per_block;
-}
-
-// Bytes per weight row of K columns.
-double row_bytes(int dtype, int K) {
-  if (dtype == MOE_Q8_0) return K / 32 * 34.0;
-  return K / 256 * (dtype == MOE_Q4_K ? 144.0 : dtype == MOE_Q2_K ? 84.0 : dtype == MOE_Q3_K ? 114.0 : 210.0);
-}
-
-// Single-role launches, every (format, chunks-per-lane) pair.
-template <int FMT, bool GU>
-bool launch_ffn_c(int cpl, FfnArgs a, int dtype, int slots, hipStream_t st) {
-  switch (cpl) {
-#define SVR_CASE(C)                                                                   \
-  case C: {                                                                           \
-    auto k = k_ffn<FMT, C, GU>;                                                       \
-    size_role(a, dtype, slots, resident_blocks(k));                                   \
-    hipLaunchKernelGGL(k, dim3(tiles_of(a), slots), dim3(kBlock), 0, st, a);          \
-    return true;                                                                      \
-  }
-    SVR_CASE(1) SVR_CASE(2) SVR_CASE(3) SVR_CASE(4) SVR_CASE(5) SVR_CASE(6) SVR_CASE(7) SVR_CASE(8)
-#undef SVR_CASE
-    default: return false;
-  }
-}
-
-bool launch_ffn(int dtype, bool gateup, FfnArgs a, int slots_max, hipStream_t st) {
-  FfnShape s;
-  ffn_shape(dtype, a.K, &s);
-  if (dtype == MOE_Q8_0)
-    return gateup ? launch_ffn_c<kQ8_0, true>(s.cpl, a, dtype, slots_max, st)
-                  : launch_ffn_c<kQ8_0, false>(s.cpl, a, dtype, slots_max, st);
-  if (dtype == MOE_Q2_K)
-    return gateup ? launch_ffn_c<kQ2_K, true>(s.cpl, a, dtype, slots_max, st)
-                  : launch_ffn_c<kQ2_K, false>(s.cpl, a, dtype, slots_max, st);
-  if (dtype == MOE_Q3_K)
-    return gateup ? launch_ffn_c<kQ3_K, true>(s.cpl, a, dtype, slots_max, st)
-                  : launch_ffn_c<kQ3_K, false>(s.cpl, a, dtype, slots_max, st);
-  if (dtype == MOE_Q6_K)
-    return gateup ? launch_ffn_c<kQ6_K, true>(s.cpl, a, dtype, slots_max, st)
-                  : launch_ffn_c<kQ6_K, false>(s.cpl, a, dtype, slots_max, st);
-  return gateup ? launch_ffn_c<kQ4_K, true>(s.cpl, a, dtype, slots_max, st)
-                : launch_ffn_c<kQ4_K, false>(s.cpl, a, dtype, slots_max, st);
-}
-
-// Fused instantiations.  A key packs (format, shape code); each launcher
-// tries the exact lane shape first (lanes per row fixed at compile time),
-// then a generic instantiation with the same chunks per lane that reads the
-// lanes per row at run time.
-constexpr int key(int fmt, int code) { return fmt * 65536 + code; }
-int exact_key(int dtype, const FfnShape& s) { return key(qfmt(dtype), shape_code(s.cpl, s.lpr)); }
-int generic_key(int dtype, const FfnShape& s) { return key(qfmt(dtype), shape_code(s.cpl, 0)); }
-
 // Phase 1: router rows (NC float4 per lane) + shared gate/up tiles in the
 // rest of one resident round.
 template <int NC>
@@ -352,125 +166,6 @@ bool launch_phase1(int H, bool shared, int sdtype, const FfnShape& sshape, hipSt
   if (!shared) return launch_phase1_k(H, 0, st, r, s, sdtype);
   return launch_phase1_k(H, exact_key(sdtype, sshape), st, r, s, sdtype) ||
          launch_phase1_k(H, generic_key(sdtype, sshape), st, r, s, sdtype);
-}
-
-// Phase 2: routed gate/up (A) + shared down (B) in one grid.  The resident
-// round is split in proportion to the bytes each side's waves stream: the
-// shared side's waves each take one token over the same rows.
-struct DualPlan {
-  int64_t a_work, b_work;  // bytes streamed by all waves of each side
-  int slots;               // routed expert slots
-  int adtype, bdtype;
-};
-
-template <int FA, int SA, int FB, int SB>
-void launch_dual_t(hipStream_t st, FfnArgs a, FfnArgs b, const DualPlan& d) {
-  auto k = k_dual<FA, SA, true, FB, SB, false>;
-  const int64_t cap = resident_blocks(k);
-  int64_t bb = (int64_t)((double)cap * d.b_work / (double)(d.a_work + d.b_work) + 0.5);
-  if (bb < 1) bb = 1;
-  if (bb > cap / 2) bb = cap / 2;
-  size_role(a, d.adtype, d.slots, cap - bb);
-  size_role(b, d.bdtype, 1, bb);
-  const int at = tiles_of(a), na = at * d.slots;
-  hipLaunchKernelGGL(k, dim3(na + tiles_of(b)), dim3(kBlock), 0, st, a, at, na, b);
-}
-
-bool launch_dual_keys(int akey, int bkey, hipStream_t st, const FfnArgs& a, const FfnArgs& b,
-                      const DualPlan& d) {
-#define SVR_D(FA, CA, LA, FB, CB, LB)                                                   \
-  if (akey == key(FA, shape_code(CA, LA)) && bkey == key(FB, shape_code(CB, LB))) {    \
-    launch_dual_t<FA, shape_code(CA, LA), FB, shape_code(CB, LB)>(st, a, b, d);        \
-    return true;                                                                         \
-  }
-#define SVR_DG(FA, CA)                                                                  \
-  SVR_D(FA, CA, 0, kQ8_0, 1, 0) SVR_D(FA, CA, 0, kQ8_0, 2, 0) SVR_D(FA, CA, 0, kQ8_0, 3, 0) \
-  SVR_D(FA, CA, 0, kQ8_0, 5, 0)
-  SVR_D(kQ4_K, 2, 64, kQ8_0, 5, 16) SVR_D(kQ4_K, 2, 64, kQ8_0, 3, 32)
-  SVR_D(kQ8_0, 4, 64, kQ8_0, 5, 16) SVR_D(kQ8_0, 4, 64, kQ8_0, 3, 32)
-  SVR_D(kQ2_K, 1, 64, kQ8_0, 5, 16) SVR_D(kQ2_K, 1, 64, kQ8_0, 3, 32)
-  SVR_D(kQ6_K, 2, 64, kQ8_0, 5, 16)
-  SVR_DG(kQ4_K, 1) SVR_DG(kQ4_K, 2) SVR_DG(kQ4_K, 3) SVR_DG(kQ8_0, 4) SVR_DG(kQ2_K, 1)
-  SVR_DG(kQ3_K, 1) SVR_DG(kQ6_K, 2)
-#undef SVR_DG
-#undef SVR_D
-  return false;
-}
-
-bool launch_dual(int adtype, const FfnShape& as, int bdtype, const FfnShape& bs, hipStream_t st,
-                 const FfnArgs& a, const FfnArgs& b, const DualPlan& d) {
-  return launch_dual_keys(exact_key(adtype, as), exact_key(bdtype, bs), st, a, b, d) ||
-         launch_dual_keys(generic_key(adtype, as), generic_key(bdtype, bs), st, a, b, d);
-}
-
-// Phase 3 with pair slots: one workgroup per (token, row tile), one
-// resident round of them (the rows of a tile a whole number of wave steps,
-// at most one per thread).
-template <int F, int S>
-bool launch_down_tok_t(hipStream_t st, FfnArgs a, const CombineArgs& c, int dtype) {
-  auto k = k_down_tok<F, S>;
-  FfnShape s;
-  ffn_shape(dtype, a.K, &s);
-  a.lpr = s.lpr;
-  const int G = kWave / s.lpr;
-  int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kDownTokThreads, 0) != hipSuccess ||
-      per_cu < 1)
-    per_cu = 1;
-  int64_t tiles = (int64_t)per_cu * device_cus() / (c.M > 0 ? c.M : 1);
-  if (tiles < 1) tiles = 1;
-  int64_t upb = (a.rows_per_expert + tiles - 1) / tiles;
-  upb = (upb + G - 1) / G * G;
-  if (upb > kDownTokRows) upb = kDownTokRows / G * G;
-  a.units_per_block = (int)upb;
-  const int nt = (a.rows_per_expert + a.units_per_block - 1) / a.units_per_block;
-  hipLaunchKernelGGL(k, dim3((unsigned)(nt * c.M)), dim3(kDownTokThreads), 0, st, a, c, nt);
-  return true;
-}
-
-bool launch_down_tok(int dtype, const FfnShape& ds, hipStream_t st, const FfnArgs& a,
-                     const CombineArgs& c) {
-#define SVR_DT(F, C, L) \
-  if (key(F, shape_code(C, L)) == kk) return launch_down_tok_t<F, shape_code(C, L)>(st, a, c, dtype);
-  for (int kk : {exact_key(dtype, ds), generic_key(dtype, ds)}) {
-    SVR_DT(kQ4_K, 3, 16) SVR_DT(kQ8_0, 5, 16) SVR_DT(kQ8_0, 3, 32)
-    SVR_DT(kQ4_K, 1, 0) SVR_DT(kQ4_K, 2, 0) SVR_DT(kQ4_K, 3, 0) SVR_DT(kQ8_0, 1, 0)
-    SVR_DT(kQ8_0, 2, 0) SVR_DT(kQ8_0, 3, 0) SVR_DT(kQ8_0, 4, 0) SVR_DT(kQ8_0, 5, 0)
-    SVR_DT(kQ8_0, 6, 0) SVR_DT(kQ2_K, 1, 32) SVR_DT(kQ2_K, 1, 0) SVR_DT(kQ3_K, 1, 32)
-    SVR_DT(kQ3_K, 1, 0) SVR_DT(kQ6_K, 3, 16) SVR_DT(kQ6_K, 3, 0) SVR_DT(kQ6_K, 1, 0)
-  }
-#undef SVR_DT
-  return false;
-}
-
-// Phase 3: routed down + combine, one resident round of row tiles x slots.
-template <int F, int S>
-bool launch_down_combine_t(hipStream_t st, FfnArgs a, const CombineArgs& c, int dtype, int slots) {
-  auto k = k_down_combine<F, S>;
-  size_role(a, dtype, slots, resident_blocks(k));
-  const int tiles = tiles_of(a);
-  if (tiles > kMaxTiles) return false;
-  hipLaunchKernelGGL(k, dim3(tiles, slots), dim3(kBlock), 0, st, a, c);
-  return true;
-}
-
-bool launch_down_combine_key(int k, hipStream_t st, const FfnArgs& a, const CombineArgs& c,
-                             int dtype, int slots) {
-#define SVR_DC(F, C, L) \
-  if (k == key(F, shape_code(C, L))) return launch_down_combine_t<F, shape_code(C, L)>(st, a, c, dtype, slots);
-  SVR_DC(kQ4_K, 3, 16) SVR_DC(kQ8_0, 5, 16)
-  SVR_DC(kQ4_K, 1, 0) SVR_DC(kQ4_K, 2, 0) SVR_DC(kQ4_K, 3, 0) SVR_DC(kQ8_0, 1, 0) SVR_DC(kQ8_0, 2, 0)
-  SVR_DC(kQ8_0, 3, 0) SVR_DC(kQ8_0, 4, 0) SVR_DC(kQ8_0, 5, 0) SVR_DC(kQ8_0, 6, 0)
-  SVR_DC(kQ2_K, 1, 32) SVR_DC(kQ2_K, 1, 0) SVR_DC(kQ3_K, 1, 32) SVR_DC(kQ3_K, 1, 0)
-  SVR_DC(kQ6_K, 3, 16) SVR_DC(kQ6_K, 3, 0)
-#undef SVR_DC
-  return false;
-}
-
-bool launch_down_combine(int dtype, const FfnShape& ds, hipStream_t st, const FfnArgs& a,
-                         const CombineArgs& c, int slots) {
-  return launch_down_combine_key(exact_key(dtype, ds), st, a, c, dtype, slots) ||
-         launch_down_combine_key(generic_key(dtype, ds), st, a, c, dtype, slots);
 }
 
 // --------------------------------------------------------------------------

@@ -90,7 +90,7 @@ __device__ __forceinline__ void router_row_block(const float* __restrict__ route
 
 // Router GEMV for any batch size (prefill): one wave per router row, tokens
 // four at a time, the row re-read from L2 per group.
-__global__ __launch_bounds__(kBlock) void k_router_logits(const float* __restrict__ router,
+static __global__ __launch_bounds__(kBlock) void k_router_logits(const float* __restrict__ router,
                                                           const float* __restrict__ x,
                                                           float* __restrict__ logits, int H,
                                                           int E, int M) {
@@ -216,7 +216,7 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ row, int32_
     topk_token_nv<COHERENT, kMaxExperts / kWave>(row, ids, wts, E, k);
 }
 
-__global__ __launch_bounds__(kBlock) void k_topk(const float* __restrict__ logits,
+static __global__ __launch_bounds__(kBlock) void k_topk(const float* __restrict__ logits,
                                                  int32_t* __restrict__ ids,
                                                  float* __restrict__ wts, int E, int k, int M) {
   const int t = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
@@ -323,7 +323,7 @@ __device__ void bucket_block(const int32_t* __restrict__ ids, int n_pairs, int E
   }
 }
 
-__global__ __launch_bounds__(kBlock) void k_bucket(const int32_t* __restrict__ ids, int n_pairs,
+static __global__ __launch_bounds__(kBlock) void k_bucket(const int32_t* __restrict__ ids, int n_pairs,
                                                    int E, BucketOut o) {
   bucket_block(ids, n_pairs, E, o);
 }
@@ -334,7 +334,7 @@ __global__ __launch_bounds__(kBlock) void k_bucket(const int32_t* __restrict__ i
 constexpr int kWideWaves = 16;
 constexpr int kWideBlock = kWideWaves * kWave;
 
-__global__ __launch_bounds__(kWideBlock) void k_bucket_wide(const int32_t* __restrict__ ids,
+static __global__ __launch_bounds__(kWideBlock) void k_bucket_wide(const int32_t* __restrict__ ids,
                                                             int n_pairs, int E, BucketOut o) {
   __shared__ int32_t s_hist[kWideWaves][kMaxExperts];  // per-chunk counts, then cursors
   __shared__ int32_t s_wc[kWideWaves], s_wa[kWideWaves];
