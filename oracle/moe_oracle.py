@@ -31,7 +31,7 @@ block layouts.  Readings taken here:
 * expert FFN: SwiGLU, h = silu(Wg x) * (Wu x), o = Wd h, silu(g) = g/(1+e^-g);
 * shared expert: the same FFN, ungated, added with weight one;
 * output y_t = s_t + sum_j w_tj o_tj, summed in slot order j = 0..k-1;
-* block layouts: the planar Q8_0 / Q4_K / Q2_K layouts documented in
+* block layouts: the planar Q8_0 / Q4_K / Q2_K / Q3_K / Q6_K layouts documented in
   include/moe_layer.h; Q2_K is read as the K-quant family's 2-bit member:
   256-weight super-blocks with fp16 d and dmin, sixteen 16-weight
   sub-blocks with a 4-bit scale and a 4-bit min, 2-bit quants,

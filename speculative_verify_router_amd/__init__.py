@@ -1,6 +1,6 @@
 """Routed mixture-of-experts verify layer for AMD Instinct MI355X (gfx950).
 
-One routed-MoE FFN block (F32 softmax top-k router, Q4_K / Q8_0 experts,
+One routed-MoE FFN block (F32 softmax top-k router, Q8_0 / Q4_K / Q2_K / Q3_K / Q6_K experts,
 SwiGLU, a shared expert and a weighted combine) applied to the verify batch
 of MTP speculative decoding, implemented as hand-written HIP kernels behind
 the C ABI of ``include/moe_layer.h``, plus greedy MTP verify/accept
