@@ -53,6 +53,7 @@ struct FfnArgs {
   const int32_t* pair_expert;  // pair slots: slot p is pair p, expert pair_expert[p]
   int n_pairs;                 // number of pair slots (pair_expert != NULL)
   int coherent_in;  // 1: act and pair_expert were written earlier in this launch
+  int max_rows;     // host side: cap on units_per_block (0: none)
 };
 
 // A role's lane shape as one template argument: chunks per lane | lanes

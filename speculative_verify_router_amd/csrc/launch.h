@@ -131,6 +131,8 @@ inline void size_role(FfnArgs& a, int dtype, int slots, int64_t blocks) {
   if (tiles < 1) tiles = 1;
   int64_t upb = (a.rows_per_expert + tiles - 1) / tiles;
   upb = (upb + unit_step - 1) / unit_step * unit_step;
+  if (a.max_rows > 0 && upb > a.max_rows)
+    upb = std::max<int64_t>(unit_step, a.max_rows / unit_step * unit_step);
   a.units_per_block = (int)upb;
 }
 

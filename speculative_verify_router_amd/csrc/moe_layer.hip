@@ -357,6 +357,13 @@ FfnArgs routed_args(const Plan& p, const Buffers& b, bool gateup, const moe_laye
     a.act_by_pair = 1;
     a.out = b.o;
   }
+  // Batches above the fused sizes (types without a matrix-core path) make
+  // one token pass per token of an expert over the same rows: tiles of
+  // about 64 KB of weights stay in L2 from pass to pass.
+  if (p.M > kFusedMaxTokens) {
+    const double rb = gateup ? 2.0 * row_bytes(p.et, p.H) : row_bytes(p.dt, p.F);
+    a.max_rows = (int)std::max(1.0, 65536.0 / rb);
+  }
   return a;
 }
 
