@@ -25,6 +25,12 @@
 //   a = 128 d sc,  c = a + dmin m.
 // X comes from the same MFMA with an all-ones B operand, in the D layout.
 // Q8_0 weights are the int8 values converted to bf16 (exact), sum w x = d P.
+// Q2_K weights enter as 1 + sc q/128 (sc q <= 45, so the product fits the
+// seven mantissa bits): a 32-column step holds two 16-weight sub-blocks
+// (operand lanes g < 2 and g >= 2), and with X0 / X1 the activation sums of
+// the two halves (all-ones B operands masked to those lanes)
+//   sum w x = 128 d (P - X0 - X1) - dmin (m0 X0 + m1 X1) = a P - c0 X0 - c1 X1,
+//   a = 128 d,  c0 = a + dmin m0,  c1 = a + dmin m1.
 #pragma once
 
 #include "common.h"
@@ -176,6 +182,21 @@ __device__ __forceinline__ u32x4 q4k_operand(uint32_t w, uint32_t one) {
   return b;
 }
 
+// One Q2_K sub-block dword, shifted so that the lane's eight weights are the
+// 2-bit fields at bits 8t and 8t + 2 of byte t (t = 0..3) -> B operand
+// elements 1 + sc q/128 in the order 0,4,1,5,2,6,3,7.  The pair (q_t,
+// q_t+4) is packed into the two halves first and multiplied by sc once
+// (sc q <= 45: no carry between the halves).
+__device__ __forceinline__ u32x4 q2k_operand(uint32_t u, uint32_t sc) {
+  u32x4 b;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const uint32_t pr = __builtin_amdgcn_ubfe(u, 8 * t, 2) | (__builtin_amdgcn_ubfe(u, 8 * t + 2, 2) << 16);
+    b[t] = (pr * sc) | 0x3F803F80u;
+  }
+  return b;
+}
+
 // v, in a VGPR, as a value unknown to the optimiser (emits no instruction).
 __device__ __forceinline__ uint32_t opaque_vgpr(uint32_t v) {
   asm volatile("" : "+v"(v));
@@ -215,7 +236,7 @@ constexpr int kActSlabBytes = kSlab * 2 * 4 * 16 * 16;
 
 // 16-byte weight loads per lane, row tile and slab (128 / 256 bytes per row).
 template <int FMT>
-constexpr int slab_loads() { return FMT == kQ4_K ? 2 : 4; }
+constexpr int slab_loads() { return FMT == kQ4_K ? 2 : FMT == kQ2_K ? 1 : 4; }
 
 template <int FMT, int NM, int RTR>
 struct Slab {
@@ -251,7 +272,8 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, int e, int pos0, i
                                            GemmLds<FMT, GATEUP, RTR>& L) {
   constexpr int NM = GATEUP ? 2 : 1;
   constexpr int NQ = slab_loads<FMT>();
-  constexpr uint32_t kSlabRowBytes = FMT == kQ4_K ? 128u : 256u;  // quant bytes per row and slab
+  // quant bytes per row and slab
+  constexpr uint32_t kSlabRowBytes = FMT == kQ4_K ? 128u : FMT == kQ2_K ? 64u : 256u;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int S = a.K >> 5;  // sub-blocks
@@ -290,6 +312,7 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, int e, int pos0, i
   // arrays, not one: a select between them must not become an indexed
   // load from scratch memory).
   uint4 hg0[NM][RTR], hg1[NM][RTR];
+  uint32_t dg0[NM][RTR], dg1[NM][RTR];  // Q2_K: d | dmin << 16 of the same slabs
   auto load_group = [&](int q) {
 #pragma unroll
     for (int m = 0; m < NM; ++m)
@@ -302,7 +325,7 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, int e, int pos0, i
           // other Q8_0 rows (K / 16 bytes of scales) take their eight fp16
           // scales one by one.
           uint4 v;
-          if (FMT == kQ4_K || q8_aligned) {
+          if (FMT != kQ8_0 || q8_aligned) {
             v = bload16(P[m].s, o);
           } else {
             uint32_t h[8];
@@ -313,6 +336,12 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, int e, int pos0, i
           }
           if (t == 0) hg0[m][rt] = v;
           else hg1[m][rt] = v;
+          if constexpr (FMT == kQ2_K) {
+            // d-plane offset of a row = its scale-plane offset / 4
+            const uint32_t dv = bload4(P[m].d, (o >> 2));
+            if (t == 0) dg0[m][rt] = dv;
+            else dg1[m][rt] = dv;
+          }
         }
   };
   auto load_slab = [&](Slab<FMT, NM, RTR>& sl, int k) {
@@ -335,9 +364,17 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, int e, int pos0, i
     for (int rt = 0; rt < RTR; ++rt) acc[m][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const uint32_t one = opaque_vgpr(0x3F803F80u);
   const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  // Q2_K: all-ones B operands over the first / second 16 columns of a step
+  // (operand lanes g < 2 hold columns 0..15).
+  const uint32_t one0 = g < 2 ? 0x3F803F80u : 0u, one1 = g < 2 ? 0u : 0x3F803F80u;
+  const u32x4 ones0 = {one0, one0, one0, one0}, ones1 = {one1, one1, one1, one1};
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   uint4* const wl = L.w[wv];
   float2* const scl = L.sc[wv];
+  // Q2_K: the current slab's 16 scale/min bytes and a = 128 d of each row
+  // (every lane of row n holds row n's).
+  uint4 hks[NM][RTR];
+  float aq[NM][RTR];
 
   // Slab k: stage it in LDS, issue the loads of slab k + 1 into the
   // registers it leaves free, compute its eight steps.
@@ -363,8 +400,23 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, int e, int pos0, i
                                     odd ? hg1[m][rt].z : hg0[m][rt].z, odd ? hg1[m][rt].w : hg0[m][rt].w);
         const uint4 hk = lane_fetch(hsrc, hv);
         float2 ac2[2];
+        if constexpr (FMT == kQ2_K) {
+          const uint32_t dk =
+              (uint32_t)__builtin_amdgcn_ds_bpermute(4 * hsrc, (int)(odd ? dg1[m][rt] : dg0[m][rt]));
+          const float a128 = 128.0f * f16_lo(dk), dmin = f16_hi(dk);
+          hks[m][rt] = hk;
+          aq[m][rt] = a128;
+          // steps 2g, 2g + 1: sub-blocks 4g .. 4g + 3, mins in the high nibbles
+          const uint32_t mw = g == 0 ? hk.x : g == 1 ? hk.y : g == 2 ? hk.z : hk.w;
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+          for (int t = 0; t < 2; ++t) {
+            const float m0 = (float)__builtin_amdgcn_ubfe(mw, 16 * t + 4, 4);
+            const float m1 = (float)__builtin_amdgcn_ubfe(mw, 16 * t + 12, 4);
+            ac2[t] = make_float2(fmaf(dmin, m0, a128), fmaf(dmin, m1, a128));
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < 2 && FMT != kQ2_K; ++t) {
           const int i = 2 * g + t;
           float2 ac;
           if constexpr (FMT == kQ4_K) {
@@ -389,18 +441,27 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, int e, int pos0, i
     }
 
     const uint32_t* wl32 = reinterpret_cast<const uint32_t*>(wl);
-    // acc += a P - c X for one step's products (row scale pair ac = (a, c)).
-    f32x4 pp[NM][RTR], Xp;
+    // acc += a P - c X for one step's products (row scale pair ac = (a, c));
+    // Q2_K: acc += a P - c0 X0 - c1 X1 with ac = (c0, c1) and a per slab.
+    f32x4 pp[NM][RTR], Xp, Xp1;
     float2 acp[NM][RTR];
-    auto apply = [&](const f32x4 (&pv)[NM][RTR], const f32x4& Xv, const float2 (&acv)[NM][RTR]) {
+    auto apply = [&](const f32x4 (&pv)[NM][RTR], const f32x4& Xv, const f32x4& Xv1,
+                     const float2 (&acv)[NM][RTR]) {
 #pragma unroll
       for (int m = 0; m < NM; ++m)
 #pragma unroll
         for (int rt = 0; rt < RTR; ++rt)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            float v = fmaf(acv[m][rt].x, pv[m][rt][j], acc[m][rt][j]);
-            if constexpr (FMT == kQ4_K) v = fmaf(-acv[m][rt].y, Xv[j], v);
+            float v;
+            if constexpr (FMT == kQ2_K) {
+              v = fmaf(aq[m][rt], pv[m][rt][j], acc[m][rt][j]);
+              v = fmaf(-acv[m][rt].x, Xv[j], v);
+              v = fmaf(-acv[m][rt].y, Xv1[j], v);
+            } else {
+              v = fmaf(acv[m][rt].x, pv[m][rt][j], acc[m][rt][j]);
+              if constexpr (FMT == kQ4_K) v = fmaf(-acv[m][rt].y, Xv[j], v);
+            }
             acc[m][rt][j] = v;
           }
     };
@@ -418,6 +479,14 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, int e, int pos0, i
           const int base = (m * RTR + rt) * NQ;
           if constexpr (FMT == kQ4_K) {
             b[m][rt] = q4k_operand(wl32[((base + (i >> 2)) * 64 + (i & 3) * 16 + n) * 4 + g], one);
+          } else if constexpr (FMT == kQ2_K) {
+            // Sub-block s = 2i + g/2 of the slab: its quant dword (bytes 4s of
+            // the row's 64, held by loading lane s/4 of the row) and scale.
+            const int s2 = 2 * i + (g >> 1);
+            const uint32_t qd = wl32[(base * 64 + (s2 >> 2) * 16 + n) * 4 + (s2 & 3)];
+            const uint32_t sw = (i >> 1) == 0 ? hks[m][rt].x : (i >> 1) == 1 ? hks[m][rt].y
+                              : (i >> 1) == 2 ? hks[m][rt].z : hks[m][rt].w;
+            b[m][rt] = q2k_operand(qd >> (4 * (g & 1)), __builtin_amdgcn_ubfe(sw, 8 * (s2 & 3), 4));
           } else {
             const int u = 2 * i + (g >> 1);
             const uint2 w = reinterpret_cast<const uint2*>(wl)[((base + (i >> 1)) * 64 + (u & 3) * 16 + n) * 2 + (g & 1)];
@@ -426,19 +495,27 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, int e, int pos0, i
         }
       // hi terms for every row tile first, then lo terms, so that no MFMA
       // waits on the one just issued.
-      f32x4 p[NM][RTR], X = zero;
+      f32x4 p[NM][RTR], X = zero, X1 = zero;
 #pragma unroll
       for (int m = 0; m < NM; ++m)
 #pragma unroll
         for (int rt = 0; rt < RTR; ++rt) p[m][rt] = mfma_bf16(ahi, b[m][rt], zero);
       if constexpr (FMT == kQ4_K) X = mfma_bf16(ahi, ones, zero);
+      if constexpr (FMT == kQ2_K) {
+        X = mfma_bf16(ahi, ones0, zero);
+        X1 = mfma_bf16(ahi, ones1, zero);
+      }
 #pragma unroll
       for (int m = 0; m < NM; ++m)
 #pragma unroll
         for (int rt = 0; rt < RTR; ++rt) p[m][rt] = mfma_bf16(alo, b[m][rt], p[m][rt]);
       if constexpr (FMT == kQ4_K) X = mfma_bf16(alo, ones, X);
+      if constexpr (FMT == kQ2_K) {
+        X = mfma_bf16(alo, ones0, X);
+        X1 = mfma_bf16(alo, ones1, X1);
+      }
       // Scale the previous step's products while this step's MFMAs run.
-      if (i > 0) apply(pp, Xp, acp);
+      if (i > 0) apply(pp, Xp, Xp1, acp);
 #pragma unroll
       for (int m = 0; m < NM; ++m)
 #pragma unroll
@@ -447,8 +524,9 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, int e, int pos0, i
           acp[m][rt] = scl[(((m * RTR + rt) * 4 + (i >> 1)) * 16 + n) * 2 + (i & 1)];
         }
       Xp = X;
+      Xp1 = X1;
     }
-    apply(pp, Xp, acp);
+    apply(pp, Xp, Xp1, acp);
   };
   Slab<FMT, NM, RTR> sl;
   load_group(0);

@@ -460,8 +460,9 @@ const char* const kGemmStageNames[kGemmStages] = {"route", "shared_gateup", "gat
 
 bool gemm_path(const Plan& p) {
   if (p.M <= kFusedMaxTokens) return false;
-  // no matrix-core decoder for the Q2_K, Q3_K and Q6_K types
-  if (gemv_only_type(p.et) || gemv_only_type(p.dt)) return false;
+  // matrix-core decoders exist for Q8_0, Q4_K and Q2_K
+  auto mfma_type = [](int t) { return t == MOE_Q8_0 || t == MOE_Q4_K || t == MOE_Q2_K; };
+  if (!mfma_type(p.et) || !mfma_type(p.dt)) return false;
   if (p.dt != p.et) return false;  // the down GEMMs decode the gate/up type
   // Split activations and h are addressed with 32-bit byte offsets.
   const int64_t P = (int64_t)p.M * p.k;
@@ -480,7 +481,10 @@ void launch_gemm_t(GemmArgs a, int tiles_cap, hipStream_t st) {
 }
 
 void launch_gemm(int dtype, bool gateup, const GemmArgs& a, int tiles_cap, hipStream_t st) {
-  if (dtype == MOE_Q4_K) {
+  if (dtype == MOE_Q2_K) {
+    if (gateup) launch_gemm_t<kQ2_K, true, kGemmGateUpRtr>(a, tiles_cap, st);
+    else launch_gemm_t<kQ2_K, false, kGemmDownRtr>(a, tiles_cap, st);
+  } else if (dtype == MOE_Q4_K) {
     if (gateup) launch_gemm_t<kQ4_K, true, kGemmGateUpRtr>(a, tiles_cap, st);
     else launch_gemm_t<kQ4_K, false, kGemmDownRtr>(a, tiles_cap, st);
   } else {

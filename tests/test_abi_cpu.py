@@ -137,9 +137,9 @@ def test_bad_descriptors_are_rejected(kw, status):
 def test_q2_k_routed_experts_are_accepted():
     for M in (1, 4, 16, 512):
         assert svr.moe_workspace_bytes(_desc(expert_type="q2_k"), M) > 0
-    # no matrix-core decoder for 2-bit experts: large batches take the three stages
+    # 2-bit experts have a matrix-core decoder: large batches take the five stages
     d = _desc(expert_type="q2_k").c()
-    assert svr.lib().moe_stage_count(ctypes.byref(d), 512) == 3
+    assert svr.lib().moe_stage_count(ctypes.byref(d), 512) == 5
     assert svr.lib().moe_stage_count(ctypes.byref(_desc().c()), 512) == 5
 
 

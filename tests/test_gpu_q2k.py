@@ -5,7 +5,8 @@ Q2_K is the 2-bit type of the routed matrices in the 2-bit Step-5 recipes
 bit-exact; layers must match the oracle's ids exactly, routing weights
 within 1e-6 and outputs within 2e-3 x RMS, on every launch sequence the
 type can take: pair slots (1 to 4 tokens), expert lists (5 to 16), and the
-staged path beyond 16 tokens (no matrix-core decoder for this type).
+grouped GEMMs on the matrix cores beyond 16 tokens (sc q as bf16 operands,
+split activation sums for the two 16-column halves of each step).
 """
 
 import numpy as np
@@ -63,6 +64,14 @@ def test_small_q2_k_with_shared(M):
     # H = 1024: 16 chunks of 64 per gate/up row; F = 512: 8 chunks per down row.
     cfg = small_config(hidden=1024, n_experts=16, top_k=4, ffn=512, shared_ffn=256,
                        expert_type="q2_k", n_tokens=M, router_std=0.2, seed_index=700 + M)
+    _case(cfg)
+
+
+@pytest.mark.parametrize("M,E,k", [(200, 16, 4), (96, 40, 8)])
+def test_q2_k_batched_matrix_core_path(M, E, k):
+    # several token tiles per expert, partial tiles, every expert active
+    cfg = small_config(hidden=1024, n_experts=E, top_k=k, ffn=512, shared_ffn=256,
+                       expert_type="q2_k", n_tokens=M, router_std=0.2, seed_index=720 + M)
     _case(cfg)
 
 
