@@ -234,8 +234,8 @@ int32_t moe_route(const moe_layer_desc* desc, const float* router, const float* 
  * integer quants, fp32 scales and activations split into two bf16 terms,
  * in five stages ("route", "shared_gateup", "gateup", "shared_down",
  * "down_combine"; the shared stages are empty without a shared expert);
- * with Q2_K, Q3_K or Q6_K routed matrices they run the three stages of the
- * small batches instead (no matrix-core path for those types).  The single
+ * with Q6_K routed matrices they run the three stages of the small batches
+ * instead (no matrix-core path for that type).  The single
  * launch needs down_type equal to expert_type.
  * moe_stage_count / moe_stage_name say which. */
 int32_t moe_layer_forward(const moe_layer_desc* desc, const moe_layer_weights* weights,

@@ -31,6 +31,10 @@
 // the two halves (all-ones B operands masked to those lanes)
 //   sum w x = 128 d (P - X0 - X1) - dmin (m0 X0 + m1 X1) = a P - c0 X0 - c1 X1,
 //   a = 128 d,  c0 = a + dmin m0,  c1 = a + dmin m1.
+// Q3_K weights enter as 1 + Q/128 (Q the unsigned 3-bit quant) against
+// activations masked to one half of the step at a time (P0, X0 over
+// columns 0..15, P1, X1 over 16..31), and with D_h = d (S_h - 32)
+//   sum w x = sum_h D_h (128 P_h - 132 X_h)   (Q - 4 = 128 (1 + Q/128) - 132).
 #pragma once
 
 #include "common.h"
@@ -197,6 +201,19 @@ __device__ __forceinline__ u32x4 q2k_operand(uint32_t u, uint32_t sc) {
   return b;
 }
 
+// Q3_K: low bits as in q2k_operand (u), high bits of the lane's weights at
+// bits 8t and 8t + 1 of hv -> B operand elements 1 + Q/128, Q = low | high << 2.
+__device__ __forceinline__ u32x4 q3k_operand(uint32_t u, uint32_t hv) {
+  u32x4 b;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const uint32_t q0 = __builtin_amdgcn_ubfe(u, 8 * t, 2) | (__builtin_amdgcn_ubfe(hv, 8 * t, 1) << 2);
+    const uint32_t q1 = __builtin_amdgcn_ubfe(u, 8 * t + 2, 2) | (__builtin_amdgcn_ubfe(hv, 8 * t + 1, 1) << 2);
+    b[t] = (q0 | (q1 << 16)) | 0x3F803F80u;
+  }
+  return b;
+}
+
 // v, in a VGPR, as a value unknown to the optimiser (emits no instruction).
 __device__ __forceinline__ uint32_t opaque_vgpr(uint32_t v) {
   asm volatile("" : "+v"(v));
@@ -236,7 +253,7 @@ constexpr int kActSlabBytes = kSlab * 2 * 4 * 16 * 16;
 
 // 16-byte weight loads per lane, row tile and slab (128 / 256 bytes per row).
 template <int FMT>
-constexpr int slab_loads() { return FMT == kQ4_K ? 2 : FMT == kQ2_K ? 1 : 4; }
+constexpr int slab_loads() { return FMT == kQ4_K || FMT == kQ3_K ? 2 : FMT == kQ2_K ? 1 : 4; }
 
 template <int FMT, int NM, int RTR>
 struct Slab {
@@ -273,7 +290,7 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, int e, int pos0, i
   constexpr int NM = GATEUP ? 2 : 1;
   constexpr int NQ = slab_loads<FMT>();
   // quant bytes per row and slab
-  constexpr uint32_t kSlabRowBytes = FMT == kQ4_K ? 128u : FMT == kQ2_K ? 64u : 256u;
+  constexpr uint32_t kSlabRowBytes = FMT == kQ4_K ? 128u : (FMT == kQ2_K || FMT == kQ3_K) ? 64u : 256u;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int S = a.K >> 5;  // sub-blocks
@@ -299,12 +316,15 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, int e, int pos0, i
   QPlanes P[NM];
   P[0] = expert_planes<FMT>(a.w0, a.total_rows, a.K, (int64_t)e * a.rows, a.rows);
   if (GATEUP) P[NM - 1] = expert_planes<FMT>(a.w1, a.total_rows, a.K, (int64_t)e * a.rows, a.rows);
-  uint32_t qo[RTR], so[RTR];
+  uint32_t qo[RTR], so[RTR], ho[RTR];
 #pragma unroll
   for (int rt = 0; rt < RTR; ++rt) {
     const uint32_t r = (uint32_t)(r0 + 16 * rt + n);
     qo[rt] = r * P[0].qrow + 16u * (uint32_t)g;
     so[rt] = r * P[0].srow;
+    // Q3_K high bits: K / 8 bytes per row (2 x the scale plane), 32 per
+    // slab; lanes g and g + 2 load the same 16 bytes.
+    ho[rt] = 2u * so[rt] + 16u * (uint32_t)(g & 1);
   }
 
   const bool q8_aligned = (a.K & 255) == 0;
@@ -336,9 +356,10 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, int e, int pos0, i
           }
           if (t == 0) hg0[m][rt] = v;
           else hg1[m][rt] = v;
-          if constexpr (FMT == kQ2_K) {
-            // d-plane offset of a row = its scale-plane offset / 4
-            const uint32_t dv = bload4(P[m].d, (o >> 2));
+          if constexpr (FMT == kQ2_K || FMT == kQ3_K) {
+            // d-plane offset of a row = its scale-plane offset / 4 (Q2_K:
+            // d | dmin) or / 8 (Q3_K: d)
+            const uint32_t dv = FMT == kQ2_K ? bload4(P[m].d, o >> 2) : bload2(P[m].d, o >> 3);
             if (t == 0) dg0[m][rt] = dv;
             else dg1[m][rt] = dv;
           }
@@ -351,9 +372,14 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, int e, int pos0, i
     for (int m = 0; m < NM; ++m)
 #pragma unroll
       for (int rt = 0; rt < RTR; ++rt) {
+        if constexpr (FMT == kQ3_K) {
+          sl.q[m][rt][0] = bload16(P[m].q, qo[rt] + kSlabRowBytes * (uint32_t)k);
+          sl.q[m][rt][1] = bload16(P[m].h, ho[rt] + 32u * (uint32_t)k);
+        } else {
 #pragma unroll
-        for (int j = 0; j < NQ; ++j)
-          sl.q[m][rt][j] = bload16(P[m].q, qo[rt] + kSlabRowBytes * (uint32_t)k + 64u * j);
+          for (int j = 0; j < NQ; ++j)
+            sl.q[m][rt][j] = bload16(P[m].q, qo[rt] + kSlabRowBytes * (uint32_t)k + 64u * j);
+        }
       }
   };
 
@@ -415,8 +441,22 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, int e, int pos0, i
             ac2[t] = make_float2(fmaf(dmin, m0, a128), fmaf(dmin, m1, a128));
           }
         }
+        if constexpr (FMT == kQ3_K) {
+          // steps 2g, 2g + 1: sub-blocks 4g .. 4g + 3; D_h = d (S_h - 32)
+          const uint32_t dk =
+              (uint32_t)__builtin_amdgcn_ds_bpermute(4 * hsrc, (int)(odd ? dg1[m][rt] : dg0[m][rt]));
+          const float d = f16_lo(dk);
+          const uint32_t sw = (g == 0 ? hk.x : g == 1 ? hk.y : g == 2 ? hk.z : hk.w) ^ 0x20202020u;
 #pragma unroll
-        for (int t = 0; t < 2 && FMT != kQ2_K; ++t) {
+          for (int t = 0; t < 2; ++t) {
+            // held in ints: converted as signed values
+            const int s0 = __builtin_amdgcn_sbfe((int)sw, 16 * t, 6);
+            const int s1 = __builtin_amdgcn_sbfe((int)sw, 16 * t + 8, 6);
+            ac2[t] = make_float2(d * (float)s0, d * (float)s1);
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < 2 && FMT != kQ2_K && FMT != kQ3_K; ++t) {
           const int i = 2 * g + t;
           float2 ac;
           if constexpr (FMT == kQ4_K) {
@@ -443,10 +483,10 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, int e, int pos0, i
     const uint32_t* wl32 = reinterpret_cast<const uint32_t*>(wl);
     // acc += a P - c X for one step's products (row scale pair ac = (a, c));
     // Q2_K: acc += a P - c0 X0 - c1 X1 with ac = (c0, c1) and a per slab.
-    f32x4 pp[NM][RTR], Xp, Xp1;
+    f32x4 pp[NM][RTR], pp1[NM][RTR], Xp, Xp1;
     float2 acp[NM][RTR];
-    auto apply = [&](const f32x4 (&pv)[NM][RTR], const f32x4& Xv, const f32x4& Xv1,
-                     const float2 (&acv)[NM][RTR]) {
+    auto apply = [&](const f32x4 (&pv)[NM][RTR], const f32x4 (&pv1)[NM][RTR], const f32x4& Xv,
+                     const f32x4& Xv1, const float2 (&acv)[NM][RTR]) {
 #pragma unroll
       for (int m = 0; m < NM; ++m)
 #pragma unroll
@@ -454,7 +494,10 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, int e, int pos0, i
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             float v;
-            if constexpr (FMT == kQ2_K) {
+            if constexpr (FMT == kQ3_K) {
+              v = fmaf(acv[m][rt].x, fmaf(128.0f, pv[m][rt][j], -132.0f * Xv[j]), acc[m][rt][j]);
+              v = fmaf(acv[m][rt].y, fmaf(128.0f, pv1[m][rt][j], -132.0f * Xv1[j]), v);
+            } else if constexpr (FMT == kQ2_K) {
               v = fmaf(aq[m][rt], pv[m][rt][j], acc[m][rt][j]);
               v = fmaf(-acv[m][rt].x, Xv[j], v);
               v = fmaf(-acv[m][rt].y, Xv1[j], v);
@@ -487,6 +530,14 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, int e, int pos0, i
             const uint32_t sw = (i >> 1) == 0 ? hks[m][rt].x : (i >> 1) == 1 ? hks[m][rt].y
                               : (i >> 1) == 2 ? hks[m][rt].z : hks[m][rt].w;
             b[m][rt] = q2k_operand(qd >> (4 * (g & 1)), __builtin_amdgcn_ubfe(sw, 8 * (s2 & 3), 4));
+          } else if constexpr (FMT == kQ3_K) {
+            // Low bits of sub-block s = 2i + g/2 (load 0, as Q2_K); high bits
+            // of the sub-block pair i (bytes 4i of the row's 32: load 1, lane
+            // i/4 of the row), sub-block s in nibble s % 2.
+            const int s2 = 2 * i + (g >> 1);
+            const uint32_t qd = wl32[(base * 64 + (s2 >> 2) * 16 + n) * 4 + (s2 & 3)];
+            const uint32_t hw = wl32[((base + 1) * 64 + (i >> 2) * 16 + n) * 4 + (i & 3)];
+            b[m][rt] = q3k_operand(qd >> (4 * (g & 1)), hw >> (4 * (g >> 1) + 2 * (g & 1)));
           } else {
             const int u = 2 * i + (g >> 1);
             const uint2 w = reinterpret_cast<const uint2*>(wl)[((base + (i >> 1)) * 64 + (u & 3) * 16 + n) * 2 + (g & 1)];
@@ -495,11 +546,35 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, int e, int pos0, i
         }
       // hi terms for every row tile first, then lo terms, so that no MFMA
       // waits on the one just issued.
-      f32x4 p[NM][RTR], X = zero, X1 = zero;
+      f32x4 p[NM][RTR], p1[NM][RTR], X = zero, X1 = zero;
+      if constexpr (FMT == kQ3_K) {
+        // the two 16-column halves of the step, each against its own
+        // activations (the other half's lanes zeroed)
+        const u32x4 ahi0 = g < 2 ? ahi : u32x4{0u, 0u, 0u, 0u}, ahi1 = g < 2 ? u32x4{0u, 0u, 0u, 0u} : ahi;
+        const u32x4 alo0 = g < 2 ? alo : u32x4{0u, 0u, 0u, 0u}, alo1 = g < 2 ? u32x4{0u, 0u, 0u, 0u} : alo;
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+          for (int rt = 0; rt < RTR; ++rt) {
+            p[m][rt] = mfma_bf16(ahi0, b[m][rt], zero);
+            p1[m][rt] = mfma_bf16(ahi1, b[m][rt], zero);
+          }
+        X = mfma_bf16(ahi0, ones, zero);
+        X1 = mfma_bf16(ahi1, ones, zero);
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+          for (int rt = 0; rt < RTR; ++rt) {
+            p[m][rt] = mfma_bf16(alo0, b[m][rt], p[m][rt]);
+            p1[m][rt] = mfma_bf16(alo1, b[m][rt], p1[m][rt]);
+          }
+        X = mfma_bf16(alo0, ones, X);
+        X1 = mfma_bf16(alo1, ones, X1);
+      }
 #pragma unroll
       for (int m = 0; m < NM; ++m)
 #pragma unroll
-        for (int rt = 0; rt < RTR; ++rt) p[m][rt] = mfma_bf16(ahi, b[m][rt], zero);
+        for (int rt = 0; rt < RTR && FMT != kQ3_K; ++rt) p[m][rt] = mfma_bf16(ahi, b[m][rt], zero);
       if constexpr (FMT == kQ4_K) X = mfma_bf16(ahi, ones, zero);
       if constexpr (FMT == kQ2_K) {
         X = mfma_bf16(ahi, ones0, zero);
@@ -508,25 +583,26 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, int e, int pos0, i
 #pragma unroll
       for (int m = 0; m < NM; ++m)
 #pragma unroll
-        for (int rt = 0; rt < RTR; ++rt) p[m][rt] = mfma_bf16(alo, b[m][rt], p[m][rt]);
+        for (int rt = 0; rt < RTR && FMT != kQ3_K; ++rt) p[m][rt] = mfma_bf16(alo, b[m][rt], p[m][rt]);
       if constexpr (FMT == kQ4_K) X = mfma_bf16(alo, ones, X);
       if constexpr (FMT == kQ2_K) {
         X = mfma_bf16(alo, ones0, X);
         X1 = mfma_bf16(alo, ones1, X1);
       }
       // Scale the previous step's products while this step's MFMAs run.
-      if (i > 0) apply(pp, Xp, Xp1, acp);
+      if (i > 0) apply(pp, pp1, Xp, Xp1, acp);
 #pragma unroll
       for (int m = 0; m < NM; ++m)
 #pragma unroll
         for (int rt = 0; rt < RTR; ++rt) {
           pp[m][rt] = p[m][rt];
+          pp1[m][rt] = p1[m][rt];
           acp[m][rt] = scl[(((m * RTR + rt) * 4 + (i >> 1)) * 16 + n) * 2 + (i & 1)];
         }
       Xp = X;
       Xp1 = X1;
     }
-    apply(pp, Xp, Xp1, acp);
+    apply(pp, pp1, Xp, Xp1, acp);
   };
   Slab<FMT, NM, RTR> sl;
   load_group(0);

@@ -460,10 +460,9 @@ const char* const kGemmStageNames[kGemmStages] = {"route", "shared_gateup", "gat
 
 bool gemm_path(const Plan& p) {
   if (p.M <= kFusedMaxTokens) return false;
-  // matrix-core decoders exist for Q8_0, Q4_K and Q2_K
-  auto mfma_type = [](int t) { return t == MOE_Q8_0 || t == MOE_Q4_K || t == MOE_Q2_K; };
-  if (!mfma_type(p.et) || !mfma_type(p.dt)) return false;
-  if (p.dt != p.et) return false;  // the down GEMMs decode the gate/up type
+  // matrix-core decoders exist for every routed type but Q6_K; gate/up and
+  // down may differ
+  if (p.et == MOE_Q6_K || p.dt == MOE_Q6_K) return false;
   // Split activations and h are addressed with 32-bit byte offsets.
   const int64_t P = (int64_t)p.M * p.k;
   if (P * std::max(p.H, p.F) * 4 >= (1ll << 31)) return false;
@@ -484,6 +483,10 @@ void launch_gemm(int dtype, bool gateup, const GemmArgs& a, int tiles_cap, hipSt
   if (dtype == MOE_Q2_K) {
     if (gateup) launch_gemm_t<kQ2_K, true, kGemmGateUpRtr>(a, tiles_cap, st);
     else launch_gemm_t<kQ2_K, false, kGemmDownRtr>(a, tiles_cap, st);
+  } else if (dtype == MOE_Q3_K) {
+    // Q3_K keeps two product tiles per row tile (one per 16-column half)
+    if (gateup) launch_gemm_t<kQ3_K, true, 1>(a, tiles_cap, st);
+    else launch_gemm_t<kQ3_K, false, 2>(a, tiles_cap, st);
   } else if (dtype == MOE_Q4_K) {
     if (gateup) launch_gemm_t<kQ4_K, true, kGemmGateUpRtr>(a, tiles_cap, st);
     else launch_gemm_t<kQ4_K, false, kGemmDownRtr>(a, tiles_cap, st);
@@ -571,7 +574,7 @@ void forward_gemm(const Plan& p, const moe_layer_weights* wt, const float* x, fl
     a.slots = b.slots;
     a.top_k = p.k;
     a.out_scatter = 1;
-    launch_gemm(p.et, false, a, p.tiles_cap, st);
+    launch_gemm(p.dt, false, a, p.tiles_cap, st);
   }
   const int64_t n4 = (int64_t)p.M * (p.H / 4);
   hipLaunchKernelGGL(k_combine, dim3((unsigned)((n4 + kBlock - 1) / kBlock)), dim3(kBlock), 0, st,

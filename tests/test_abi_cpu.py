@@ -148,12 +148,13 @@ def test_routed_down_type_selects_the_path():
     for M in (1, 4, 16, 512):
         assert svr.moe_workspace_bytes(mixed, M) > 0
     L = svr.lib()
-    assert L.moe_stage_count(ctypes.byref(mixed.c()), 512) == 3
+    # matrix-core path for every type but Q6_K, gate/up and down types apart
+    assert L.moe_stage_count(ctypes.byref(mixed.c()), 512) == 5
     assert L.moe_stage_count(ctypes.byref(_desc(expert_type="q6_k").c()), 512) == 3
-    # down_type 0 is the gate/up type; a different down type leaves the
-    # matrix-core path and the single launch
+    assert L.moe_stage_count(ctypes.byref(_desc(down_type="q6_k").c()), 512) == 3
     assert L.moe_stage_count(ctypes.byref(_desc(down_type="q4_k").c()), 512) == 5
-    assert L.moe_stage_count(ctypes.byref(_desc(down_type="q8_0").c()), 512) == 3
+    assert L.moe_stage_count(ctypes.byref(_desc(down_type="q8_0").c()), 512) == 5
+    # the single launch needs one type for gate/up and down
     one = _desc(single_launch=True)
     assert L.moe_stage_count(ctypes.byref(one.c()), 4) == 1
     assert L.moe_stage_count(ctypes.byref(_desc(single_launch=True, down_type="q8_0").c()), 4) == 3

@@ -5,8 +5,9 @@ The Q2_K-Protected2 recipe stores routed gate/up in Q2_K and routed down in
 Q3_K ("Step-5 Preview GGUF", Tensor-type table).  Block decoding must be
 bit-exact; layers must match the oracle's ids exactly, routing weights
 within 1e-6 and outputs within 2e-3 x RMS on every launch sequence: pair
-slots (1 to 4 tokens), expert lists (5 to 16) and the staged path beyond
-16 tokens (no matrix-core decoder for these types, nor for mixed types).
+slots (1 to 4 tokens), expert lists (5 to 16) and the grouped GEMMs on the
+matrix cores beyond 16 tokens (1 + Q/128 bf16 operands against activations
+masked to each 16-column half of a step; gate/up and down types apart).
 """
 
 import numpy as np
@@ -70,7 +71,15 @@ def test_q2_k_gate_up_q3_k_down(M):
     _case(cfg)
 
 
-@pytest.mark.parametrize("M", [1, 4, 6])
+@pytest.mark.parametrize("M,E,k", [(200, 16, 4), (96, 40, 8)])
+def test_q2_k_gate_up_q3_k_down_batched(M, E, k):
+    cfg = small_config(hidden=1024, n_experts=E, top_k=k, ffn=512, shared_ffn=256,
+                       expert_type="q2_k", down_type="q3_k", n_tokens=M, router_std=0.2,
+                       seed_index=820 + M)
+    _case(cfg)
+
+
+@pytest.mark.parametrize("M", [1, 4, 6, 33])
 def test_all_q3_k(M):
     cfg = small_config(hidden=512, n_experts=8, top_k=2, ffn=256, shared_ffn=128,
                        expert_type="q3_k", n_tokens=M, router_std=0.3, seed_index=850 + M)
