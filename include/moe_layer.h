@@ -233,9 +233,8 @@ int32_t moe_route(const moe_layer_desc* desc, const float* router, const float* 
  * the expert FFNs as grouped GEMMs on the bf16 matrix cores with exact
  * integer quants, fp32 scales and activations split into two bf16 terms,
  * in five stages ("route", "shared_gateup", "gateup", "shared_down",
- * "down_combine"; the shared stages are empty without a shared expert);
- * with Q6_K routed matrices they run the three stages of the small batches
- * instead (no matrix-core path for that type).  The single
+ * "down_combine"; the shared stages are empty without a shared expert),
+ * for every routed type and pairing of gate/up and down types.  The single
  * launch needs down_type equal to expert_type.
  * moe_stage_count / moe_stage_name say which. */
 int32_t moe_layer_forward(const moe_layer_desc* desc, const moe_layer_weights* weights,

@@ -35,6 +35,8 @@
 // activations masked to one half of the step at a time (P0, X0 over
 // columns 0..15, P1, X1 over 16..31), and with D_h = d (S_h - 32)
 //   sum w x = sum_h D_h (128 P_h - 132 X_h)   (Q - 4 = 128 (1 + Q/128) - 132).
+// Q6_K the same way with its 6-bit Q (<= 63), D_h = d sc_h and
+//   sum w x = sum_h D_h (128 P_h - 160 X_h)   (Q - 32 = 128 (1 + Q/128) - 160).
 #pragma once
 
 #include "common.h"
@@ -214,6 +216,20 @@ __device__ __forceinline__ u32x4 q3k_operand(uint32_t u, uint32_t hv) {
   return b;
 }
 
+// Q6_K: low-nibble dword w of the lane's eight weights (Q4_K order) and
+// their high bit pairs in hv (weight t and t + 4 at bits 8 (t / 2) + 2 (t % 2)
+// and 16 more) -> B operand elements 1 + Q/128, Q = low | high << 4.
+__device__ __forceinline__ u32x4 q6k_operand(uint32_t w, uint32_t hv) {
+  u32x4 b;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const uint32_t lo = (w >> (4 * t)) & 0x000F000Fu;
+    const uint32_t hi = (hv >> (8 * (t >> 1) + 2 * (t & 1))) & 0x00030003u;
+    b[t] = lo | (hi << 4) | 0x3F803F80u;
+  }
+  return b;
+}
+
 // v, in a VGPR, as a value unknown to the optimiser (emits no instruction).
 __device__ __forceinline__ uint32_t opaque_vgpr(uint32_t v) {
   asm volatile("" : "+v"(v));
@@ -253,7 +269,13 @@ constexpr int kActSlabBytes = kSlab * 2 * 4 * 16 * 16;
 
 // 16-byte weight loads per lane, row tile and slab (128 / 256 bytes per row).
 template <int FMT>
-constexpr int slab_loads() { return FMT == kQ4_K || FMT == kQ3_K ? 2 : FMT == kQ2_K ? 1 : 4; }
+constexpr int slab_loads() {
+  return FMT == kQ4_K || FMT == kQ3_K ? 2 : FMT == kQ2_K ? 1 : FMT == kQ6_K ? 3 : 4;
+}
+// Formats whose 16-weight sub-block scales split each 32-column step in two
+// (products against activations masked to each half).
+template <int FMT>
+constexpr bool split_steps() { return FMT == kQ3_K || FMT == kQ6_K; }
 
 template <int FMT, int NM, int RTR>
 struct Slab {
@@ -290,7 +312,8 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, int e, int pos0, i
   constexpr int NM = GATEUP ? 2 : 1;
   constexpr int NQ = slab_loads<FMT>();
   // quant bytes per row and slab
-  constexpr uint32_t kSlabRowBytes = FMT == kQ4_K ? 128u : (FMT == kQ2_K || FMT == kQ3_K) ? 64u : 256u;
+  constexpr uint32_t kSlabRowBytes =
+      (FMT == kQ4_K || FMT == kQ6_K) ? 128u : (FMT == kQ2_K || FMT == kQ3_K) ? 64u : 256u;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int S = a.K >> 5;  // sub-blocks
@@ -323,8 +346,9 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, int e, int pos0, i
     qo[rt] = r * P[0].qrow + 16u * (uint32_t)g;
     so[rt] = r * P[0].srow;
     // Q3_K high bits: K / 8 bytes per row (2 x the scale plane), 32 per
-    // slab; lanes g and g + 2 load the same 16 bytes.
-    ho[rt] = 2u * so[rt] + 16u * (uint32_t)(g & 1);
+    // slab, lanes g and g + 2 load the same 16 bytes; Q6_K: K / 4 bytes per
+    // row, 64 per slab, lane g loads bytes 16 g.
+    ho[rt] = FMT == kQ6_K ? 4u * so[rt] + 16u * (uint32_t)g : 2u * so[rt] + 16u * (uint32_t)(g & 1);
   }
 
   const bool q8_aligned = (a.K & 255) == 0;
@@ -356,9 +380,9 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, int e, int pos0, i
           }
           if (t == 0) hg0[m][rt] = v;
           else hg1[m][rt] = v;
-          if constexpr (FMT == kQ2_K || FMT == kQ3_K) {
+          if constexpr (FMT == kQ2_K || FMT == kQ3_K || FMT == kQ6_K) {
             // d-plane offset of a row = its scale-plane offset / 4 (Q2_K:
-            // d | dmin) or / 8 (Q3_K: d)
+            // d | dmin) or / 8 (Q3_K, Q6_K: d)
             const uint32_t dv = FMT == kQ2_K ? bload4(P[m].d, o >> 2) : bload2(P[m].d, o >> 3);
             if (t == 0) dg0[m][rt] = dv;
             else dg1[m][rt] = dv;
@@ -375,6 +399,10 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, int e, int pos0, i
         if constexpr (FMT == kQ3_K) {
           sl.q[m][rt][0] = bload16(P[m].q, qo[rt] + kSlabRowBytes * (uint32_t)k);
           sl.q[m][rt][1] = bload16(P[m].h, ho[rt] + 32u * (uint32_t)k);
+        } else if constexpr (FMT == kQ6_K) {
+          sl.q[m][rt][0] = bload16(P[m].q, qo[rt] + kSlabRowBytes * (uint32_t)k);
+          sl.q[m][rt][1] = bload16(P[m].q, qo[rt] + kSlabRowBytes * (uint32_t)k + 64u);
+          sl.q[m][rt][2] = bload16(P[m].h, ho[rt] + 64u * (uint32_t)k);
         } else {
 #pragma unroll
           for (int j = 0; j < NQ; ++j)
@@ -455,8 +483,21 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, int e, int pos0, i
             ac2[t] = make_float2(d * (float)s0, d * (float)s1);
           }
         }
+        if constexpr (FMT == kQ6_K) {
+          // steps 2g, 2g + 1: sub-blocks 4g .. 4g + 3; D_h = d sc_h (int8)
+          const uint32_t dk =
+              (uint32_t)__builtin_amdgcn_ds_bpermute(4 * hsrc, (int)(odd ? dg1[m][rt] : dg0[m][rt]));
+          const float d = f16_lo(dk);
+          const uint32_t sw = g == 0 ? hk.x : g == 1 ? hk.y : g == 2 ? hk.z : hk.w;
 #pragma unroll
-        for (int t = 0; t < 2 && FMT != kQ2_K && FMT != kQ3_K; ++t) {
+          for (int t = 0; t < 2; ++t) {
+            const int s0 = __builtin_amdgcn_sbfe((int)sw, 16 * t, 8);
+            const int s1 = __builtin_amdgcn_sbfe((int)sw, 16 * t + 8, 8);
+            ac2[t] = make_float2(d * (float)s0, d * (float)s1);
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < 2 && FMT != kQ2_K && !split_steps<FMT>(); ++t) {
           const int i = 2 * g + t;
           float2 ac;
           if constexpr (FMT == kQ4_K) {
@@ -494,9 +535,10 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, int e, int pos0, i
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             float v;
-            if constexpr (FMT == kQ3_K) {
-              v = fmaf(acv[m][rt].x, fmaf(128.0f, pv[m][rt][j], -132.0f * Xv[j]), acc[m][rt][j]);
-              v = fmaf(acv[m][rt].y, fmaf(128.0f, pv1[m][rt][j], -132.0f * Xv1[j]), v);
+            if constexpr (split_steps<FMT>()) {
+              constexpr float kX = FMT == kQ3_K ? -132.0f : -160.0f;
+              v = fmaf(acv[m][rt].x, fmaf(128.0f, pv[m][rt][j], kX * Xv[j]), acc[m][rt][j]);
+              v = fmaf(acv[m][rt].y, fmaf(128.0f, pv1[m][rt][j], kX * Xv1[j]), v);
             } else if constexpr (FMT == kQ2_K) {
               v = fmaf(aq[m][rt], pv[m][rt][j], acc[m][rt][j]);
               v = fmaf(-acv[m][rt].x, Xv[j], v);
@@ -538,6 +580,13 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, int e, int pos0, i
             const uint32_t qd = wl32[(base * 64 + (s2 >> 2) * 16 + n) * 4 + (s2 & 3)];
             const uint32_t hw = wl32[((base + 1) * 64 + (i >> 2) * 16 + n) * 4 + (i & 3)];
             b[m][rt] = q3k_operand(qd >> (4 * (g & 1)), hw >> (4 * (g >> 1) + 2 * (g & 1)));
+          } else if constexpr (FMT == kQ6_K) {
+            // Low nibbles of group i as in Q4_K (loads 0, 1); its 8 high
+            // bytes at 8 i of the row's 64 (load 2, lane i / 2), the lane's
+            // columns in high dword g / 2 of the group, pair g % 2.
+            const uint32_t lw = wl32[((base + (i >> 2)) * 64 + (i & 3) * 16 + n) * 4 + g];
+            const uint32_t hw = wl32[((base + 2) * 64 + (i >> 1) * 16 + n) * 4 + 2 * (i & 1) + (g >> 1)];
+            b[m][rt] = q6k_operand(lw, hw >> (4 * (g & 1)));
           } else {
             const int u = 2 * i + (g >> 1);
             const uint2 w = reinterpret_cast<const uint2*>(wl)[((base + (i >> 1)) * 64 + (u & 3) * 16 + n) * 2 + (g & 1)];
@@ -547,7 +596,7 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, int e, int pos0, i
       // hi terms for every row tile first, then lo terms, so that no MFMA
       // waits on the one just issued.
       f32x4 p[NM][RTR], p1[NM][RTR], X = zero, X1 = zero;
-      if constexpr (FMT == kQ3_K) {
+      if constexpr (split_steps<FMT>()) {
         // the two 16-column halves of the step, each against its own
         // activations (the other half's lanes zeroed)
         const u32x4 ahi0 = g < 2 ? ahi : u32x4{0u, 0u, 0u, 0u}, ahi1 = g < 2 ? u32x4{0u, 0u, 0u, 0u} : ahi;
@@ -574,7 +623,7 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, int e, int pos0, i
 #pragma unroll
       for (int m = 0; m < NM; ++m)
 #pragma unroll
-        for (int rt = 0; rt < RTR && FMT != kQ3_K; ++rt) p[m][rt] = mfma_bf16(ahi, b[m][rt], zero);
+        for (int rt = 0; rt < RTR && !split_steps<FMT>(); ++rt) p[m][rt] = mfma_bf16(ahi, b[m][rt], zero);
       if constexpr (FMT == kQ4_K) X = mfma_bf16(ahi, ones, zero);
       if constexpr (FMT == kQ2_K) {
         X = mfma_bf16(ahi, ones0, zero);
@@ -583,7 +632,7 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, int e, int pos0, i
 #pragma unroll
       for (int m = 0; m < NM; ++m)
 #pragma unroll
-        for (int rt = 0; rt < RTR && FMT != kQ3_K; ++rt) p[m][rt] = mfma_bf16(alo, b[m][rt], p[m][rt]);
+        for (int rt = 0; rt < RTR && !split_steps<FMT>(); ++rt) p[m][rt] = mfma_bf16(alo, b[m][rt], p[m][rt]);
       if constexpr (FMT == kQ4_K) X = mfma_bf16(alo, ones, X);
       if constexpr (FMT == kQ2_K) {
         X = mfma_bf16(alo, ones0, X);

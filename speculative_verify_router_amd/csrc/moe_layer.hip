@@ -460,9 +460,7 @@ const char* const kGemmStageNames[kGemmStages] = {"route", "shared_gateup", "gat
 
 bool gemm_path(const Plan& p) {
   if (p.M <= kFusedMaxTokens) return false;
-  // matrix-core decoders exist for every routed type but Q6_K; gate/up and
-  // down may differ
-  if (p.et == MOE_Q6_K || p.dt == MOE_Q6_K) return false;
+  // every routed type has a matrix-core decoder; gate/up and down may differ
   // Split activations and h are addressed with 32-bit byte offsets.
   const int64_t P = (int64_t)p.M * p.k;
   if (P * std::max(p.H, p.F) * 4 >= (1ll << 31)) return false;
@@ -484,9 +482,12 @@ void launch_gemm(int dtype, bool gateup, const GemmArgs& a, int tiles_cap, hipSt
     if (gateup) launch_gemm_t<kQ2_K, true, kGemmGateUpRtr>(a, tiles_cap, st);
     else launch_gemm_t<kQ2_K, false, kGemmDownRtr>(a, tiles_cap, st);
   } else if (dtype == MOE_Q3_K) {
-    // Q3_K keeps two product tiles per row tile (one per 16-column half)
+    // Q3_K and Q6_K keep two product tiles per row tile (one per half step)
     if (gateup) launch_gemm_t<kQ3_K, true, 1>(a, tiles_cap, st);
     else launch_gemm_t<kQ3_K, false, 2>(a, tiles_cap, st);
+  } else if (dtype == MOE_Q6_K) {
+    if (gateup) launch_gemm_t<kQ6_K, true, 1>(a, tiles_cap, st);
+    else launch_gemm_t<kQ6_K, false, 2>(a, tiles_cap, st);
   } else if (dtype == MOE_Q4_K) {
     if (gateup) launch_gemm_t<kQ4_K, true, kGemmGateUpRtr>(a, tiles_cap, st);
     else launch_gemm_t<kQ4_K, false, kGemmDownRtr>(a, tiles_cap, st);

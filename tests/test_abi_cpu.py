@@ -148,10 +148,11 @@ def test_routed_down_type_selects_the_path():
     for M in (1, 4, 16, 512):
         assert svr.moe_workspace_bytes(mixed, M) > 0
     L = svr.lib()
-    # matrix-core path for every type but Q6_K, gate/up and down types apart
+    # matrix-core path for every routed type, gate/up and down types apart
     assert L.moe_stage_count(ctypes.byref(mixed.c()), 512) == 5
-    assert L.moe_stage_count(ctypes.byref(_desc(expert_type="q6_k").c()), 512) == 3
-    assert L.moe_stage_count(ctypes.byref(_desc(down_type="q6_k").c()), 512) == 3
+    assert L.moe_stage_count(ctypes.byref(_desc(expert_type="q6_k").c()), 512) == 5
+    assert L.moe_stage_count(ctypes.byref(_desc(down_type="q6_k").c()), 512) == 5
+    assert L.moe_stage_count(ctypes.byref(_desc(expert_type="q6_k").c()), 16) == 3
     assert L.moe_stage_count(ctypes.byref(_desc(down_type="q4_k").c()), 512) == 5
     assert L.moe_stage_count(ctypes.byref(_desc(down_type="q8_0").c()), 512) == 5
     # the single launch needs one type for gate/up and down

@@ -77,10 +77,23 @@ def test_q6_k_partial_lane_groups_and_q4_k_down(M):
     _case(cfg.replace(down_type="q4_k", seed_index=950 + M))
 
 
-def test_q6_k_zero_and_subnormal_scales():
+@pytest.mark.parametrize("M,E,k,down", [(200, 16, 4, None), (96, 40, 8, "q2_k"), (33, 8, 2, "q4_k")])
+def test_q6_k_batched(M, E, k, down):
+    # more than 16 tokens: the matrix-core grouped GEMMs decode Q6_K (and
+    # Q6_K gate/up with another down type)
+    cfg = small_config(hidden=1024, n_experts=E, top_k=k, ffn=512, shared_ffn=256,
+                       expert_type="q6_k", down_type=down, n_tokens=M, router_std=0.2,
+                       seed_index=970 + M)
+    _case(cfg)
+    if down is None:
+        _case(cfg.replace(expert_type="q4_k", down_type="q6_k", seed_index=975 + M))
+
+
+@pytest.mark.parametrize("M", [3, 40])
+def test_q6_k_zero_and_subnormal_scales(M):
     F = 256
     cfg = small_config(hidden=512, n_experts=4, top_k=2, ffn=F, shared_ffn=64,
-                       expert_type="q6_k", n_tokens=3, router_std=0.2, seed_index=960)
+                       expert_type="q6_k", n_tokens=M, router_std=0.2, seed_index=960 + M)
     inp = synth.draw_layer(cfg)
     for name, rows, cols in (("gate", 4 * F, 512), ("up", 4 * F, 512), ("down", 4 * 512, F)):
         buf = getattr(inp, name).copy()
