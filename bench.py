@@ -450,11 +450,9 @@ def main(argv=None) -> int:
         metric = f"MoE layer tokens/s + achieved HBM GB/s, {cfg.name} ({M} tokens), 1 MI355X"
     # Arithmetic of the expert products: integer quants times 16-bit integer
     # activations (int8 limbs, int32 sums, fp32 scales) up to 16 tokens; bf16
-    # matrix-core products of exact integer quants and split activations above
-    # (Q2_K, Q3_K and Q6_K experts, and mixed gate/up and down types, stay on
-    # the integer path at every batch size).
-    gemv_only = ("q2_k", "q3_k", "q6_k")
-    int_path = (M <= 16 or cfg.expert_type in gemv_only or cfg.routed_down_type != cfg.expert_type)
+    # matrix-core products of exact integer quants and split activations above,
+    # for every routed type and pairing of gate/up and down types.
+    int_path = M <= 16
     dtype = "i8xi16->i32+f32" if int_path else "bf16x2->f32"
     out = {
         "metric": metric,

@@ -101,7 +101,7 @@ class LayerConfig:
         return dataclasses.replace(self, **kw)
 
 
-# The five workloads.  Index 1..5 keys the seed.
+# The workloads; the last positional index keys the seed.
 CONFIGS = {
     # Tiny seed-generated layer (parity only): H 256, 8 experts, top-2, F 128.
     "tiny": LayerConfig("tiny", 256, 8, 2, 128, 0, "q8_0", "q8_0", 1, 0.5, 0.02, "iid", 1),
@@ -132,6 +132,13 @@ CONFIGS = {
     # Tensor-type table).
     "step35_q6k_verify_m4": LayerConfig(
         "step35_q6k_verify_m4", 4096, 288, 8, 1280, 1280, "q6_k", "q8_0", 4, 0.02, 0.02, "iid", 8),
+    # The Step-5 prefill micro-batch with the Q2_K-Protected2 routed types
+    # (Q2_K gate/up, Q3_K down) and with Q6_K routed experts.
+    "step5_q2kp2_prefill_m512": LayerConfig(
+        "step5_q2kp2_prefill_m512", 4096, 352, 8, 1536, 1536, "q2_k", "q8_0", 512, 0.02, 0.02, "iid",
+        9, "q3_k"),
+    "step5_q6k_prefill_m512": LayerConfig(
+        "step5_q6k_prefill_m512", 4096, 352, 8, 1536, 1536, "q6_k", "q8_0", 512, 0.02, 0.02, "iid", 10),
 }
 
 

@@ -26,7 +26,8 @@ SAMPLE_TOKENS = [0, 1, 2, 255, 256, 400, 510, 511]
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["step35_decode_m1", "step35_verify_m4", "step5_verify_m4",
                                   "step5_q2k_verify_m4", "step5_q2kp2_verify_m4",
-                                  "step35_q6k_verify_m4", "step5_prefill_m512"])
+                                  "step35_q6k_verify_m4", "step5_prefill_m512",
+                                  "step5_q2kp2_prefill_m512", "step5_q6k_prefill_m512"])
 def test_full_config(name):
     cfg = synth.CONFIGS[name]
     log(f"[{name}] drawing layer")
