@@ -10,12 +10,14 @@ router.  Calls rotate over R independent layer instances so that no call
 finds its weights in the 256 MB Infinity Cache left by the previous one.
 
 Prints one JSON line.  `roofline` reports the dominant kernel against the
-8 TB/s HBM peak: the single-launch layer (k_flow, every byte of the layer)
-when it is selected; otherwise the routed gate/up stage (k_dual, which also
-streams the shared down projection, for up to 16 tokens; the routed gate/up
-grouped GEMM k_gemm for larger batches).  Its time comes from HIP events recorded by the library on
-the launch stream; `cpu_baseline` times the CPU oracle on a
-bounded sample (repeated layer calls, about 12 s) on the host.
+8 TB/s HBM peak: the routed gate/up stage (k_dual, which also streams the
+shared down projection, for up to 16 tokens; the routed gate/up grouped
+GEMM k_gemm for larger batches).  Its time comes from HIP events recorded by the library on
+the launch stream; `layer_us` is the median (and spread) of per-call
+event times in a second pass; for batches above 16 tokens `mfma` gives the
+matrix-core utilisation; `cpu_baseline` times the CPU oracle on a bounded
+sample (repeated layer calls, about 10 s on every host core and 10 s on
+one core) on the host.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--instances 4]
                     [--events dominant|all] [--graph] [--copy-calibration MIB]
@@ -38,11 +40,10 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "step35_verify_m4"
-# Dominant stage -> its kernel.  The single-launch path runs the whole layer
-# as one launch (stage "layer"); the staged path (up to 16 tokens) has three
+# Dominant stage -> its kernel.  The staged path (up to 16 tokens) has three
 # stages, the batched path five (its first is "route"); in both "gateup"
 # moves the most bytes.
-KERNEL_OF_STAGE = {"layer": "k_flow", "gateup": "k_dual"}
+KERNEL_OF_STAGE = {"gateup": "k_dual"}
 BATCHED_KERNEL = "k_gemm"
 
 
@@ -78,6 +79,36 @@ def layer_bytes(cfg, distinct: int, batched: bool = False) -> dict:
     return dict(total=total, layer=total, gateup=gateup)
 
 
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
+
+
+def mfma_utilisation(cfg, ids_per_instance, t_us: float) -> dict:
+    """Matrix-core use of a batched call: the method's FLOP (routed and
+    shared expert products and the router) over the call time, against the
+    dense bf16 peak; and the issued fraction of the expert GEMMs, which
+    pad each expert's tokens to tiles of 16 and run every product twice
+    (bf16 hi and lo activation terms).  The all-ones MFMAs that give the
+    activation sums are not counted."""
+    H, F, Fs, M, k, E = (cfg.hidden, cfg.ffn, cfg.shared_ffn, cfg.n_tokens, cfg.top_k,
+                         cfg.n_experts)
+    routed = 2.0 * M * k * 3 * H * F
+    shared = 2.0 * M * 3 * H * Fs
+    router = 2.0 * M * E * H
+    flop = routed + shared + router
+    pads = []
+    for ids in ids_per_instance:
+        cnt = np.bincount(np.asarray(ids).reshape(-1), minlength=E)
+        pads.append(float(np.sum((cnt + 15) // 16 * 16)) / (M * k))
+    pad = float(np.mean(pads))
+    issued = 2.0 * (routed * pad + shared * ((M + 15) // 16 * 16) / M)
+    t = t_us * 1e-6
+    peak = BF16_PEAK_TFLOPS * 1e12
+    return {"flop": flop, "peak_tflops": BF16_PEAK_TFLOPS, "t_us": round(t_us, 2),
+            "util": round(flop / (t * peak), 4),
+            "issued_flop": issued, "issued_util": round(issued / (t * peak), 4),
+            "token_tile_padding": round(pad, 4)}
+
+
 def source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "speculative_verify_router_amd", "csrc")
@@ -100,32 +131,69 @@ def traffic_for(kernel: str, workload: str):
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(cfg, inp, x) -> dict:
-    """The oracle as it stands on whole layer calls of the workload, BLAS on one thread."""
-    from oracle import moe_oracle as om
+def cpu_model() -> str:
+    """The host CPU's model name from /proc/cpuinfo (empty if unreadable)."""
     try:
-        from threadpoolctl import threadpool_limits
-        limiter = threadpool_limits(1)
-    except Exception:  # pragma: no cover
-        limiter = None
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
+
+def host_cores() -> int:
+    """Cores this process may run on (the machine's CPU share, not the machine's)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        return os.cpu_count() or 1
+
+
+def _time_oracle_calls(cfg, inp, x, threads: int, budget_s: float, tokens=None):
+    """Repeat layer calls of the oracle with `threads` threads (its expert
+    loop) until about `budget_s` seconds are timed; `tokens` restricts the
+    expert FFNs to those tokens (the routing is always computed for all)."""
+    from oracle import moe_oracle as om
+    from threadpoolctl import threadpool_limits
     kw = dict(top_k=cfg.top_k, ffn=cfg.ffn, expert_type=cfg.expert_type, down_type=cfg.down_type)
     if cfg.shared_ffn:
         kw.update(shared=(inp.shared_gate, inp.shared_up, inp.shared_down),
                   shared_ffn=cfg.shared_ffn, shared_type=cfg.shared_type)
-    # Repeat whole layer calls on the same weights and tokens until about
-    # 12 s of CPU work have been timed (at least one call, at most 30).
-    calls, t0 = 0, time.perf_counter()
-    while True:
-        om.moe_layer(x, inp.router, inp.gate, inp.up, inp.down, **kw)
-        calls += 1
-        dt = time.perf_counter() - t0
-        if dt >= 12.0 or calls >= 30:
-            break
-    if limiter is not None:
-        limiter.unregister()
-    return {"value": calls * cfg.n_tokens / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{calls} layer call(s) of {cfg.name} ({cfg.n_tokens} tokens each, "
-                      f"instance 0), float64 NumPy on one thread, {dt:.1f} s"}
+    # One BLAS thread per oracle thread (the expert loop is what spreads over
+    # the cores; nested BLAS pools would oversubscribe them).
+    with threadpool_limits(1):
+        calls, t0 = 0, time.perf_counter()
+        while True:
+            om.moe_layer(x, inp.router, inp.gate, inp.up, inp.down, workers=threads,
+                         tokens=tokens, **kw)
+            calls += 1
+            dt = time.perf_counter() - t0
+            if dt >= budget_s or calls >= 30:
+                break
+    return calls, dt
+
+
+def cpu_baseline(cfg, inp, x) -> dict:
+    """The oracle as it stands on whole layer calls of the workload: on every
+    host core (its expert loop on that many threads), then on one core.  On
+    one core a batch above 16 tokens is sampled: the FFNs of its first 16
+    tokens (the routing of the whole batch is still computed)."""
+    cores = host_cores()
+    n_all, t_all = _time_oracle_calls(cfg, inp, x, cores, 10.0)
+    one_tokens = None if cfg.n_tokens <= 16 else list(range(16))
+    n_one, t_one = _time_oracle_calls(cfg, inp, x, 1, 10.0, tokens=one_tokens)
+    per_call_one = cfg.n_tokens if one_tokens is None else len(one_tokens)
+    one_what = "layer call(s)" if one_tokens is None else "calls on the first 16 tokens"
+    return {"value": n_all * cfg.n_tokens / t_all, "unit": "tokens/s", "cores": cores,
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "sample": f"{n_all} layer call(s) of {cfg.name} ({cfg.n_tokens} tokens each, "
+                      f"instance 0), float64 NumPy, expert loop on {cores} threads, "
+                      f"{t_all:.1f} s",
+            "single_core": {"value": n_one * per_call_one / t_one, "unit": "tokens/s",
+                            "cores": 1,
+                            "sample": f"{n_one} {one_what}, one thread, {t_one:.1f} s"}}
 
 
 def _counter_rows(path: str):
@@ -192,6 +260,7 @@ def cpu_baseline_accept(batch) -> dict:
             break
     M, V = batch.logits.shape
     return {"value": calls / dt, "unit": "batches/s", "cores": 1, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{calls} oracle calls on one verify batch ({M} rows x {V} logits, "
                       f"NumPy on one thread), {dt:.1f} s"}
 
@@ -288,8 +357,6 @@ def main(argv=None) -> int:
     ap.add_argument("--event-every", type=int, default=5, metavar="N",
                     help="record the stage events on every N-th timed step only (the markers "
                          "delay the next launch; the other steps run without them)")
-    ap.add_argument("--single-launch", action="store_true",
-                    help="run the layer as one kernel launch (MOE_SINGLE_LAUNCH)")
     ap.add_argument("--graph", action="store_true",
                     help="also time the same steps replayed from a captured HIP graph")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -324,8 +391,7 @@ def main(argv=None) -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     desc = svr.LayerDesc(cfg.hidden, cfg.n_experts, cfg.top_k, cfg.ffn, cfg.shared_ffn,
-                         cfg.expert_type, cfg.shared_type, single_launch=args.single_launch,
-                         down_type=cfg.down_type)
+                         cfg.expert_type, cfg.shared_type, down_type=cfg.down_type)
     M, k = cfg.n_tokens, cfg.top_k
     R = max(1, args.instances)
 
@@ -364,7 +430,7 @@ def main(argv=None) -> int:
 
     nst = svr.moe_stage_count(desc, M)
     names = [svr.moe_stage_name(desc, M, j) for j in range(nst)]
-    DOMINANT = "layer" if "layer" in names else "gateup"
+    DOMINANT = "gateup"
     batched = names[0] == "route"
     kernel = BATCHED_KERNEL if batched else KERNEL_OF_STAGE[DOMINANT]
     K = args.steps
@@ -431,6 +497,21 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         graph_ms = (time.perf_counter() - t1) * 1e3 / (reps * R)
 
+    # Per-call layer time: each call bracketed by two events on the launch
+    # stream (a separate pass, so the whole-job timing above has no markers).
+    call_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(K)]
+    for a, b in call_ev:
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    for s in range(K):
+        call_ev[s][0].record(stream)
+        calls[s % R]()
+        call_ev[s][1].record(stream)
+    torch.cuda.synchronize()
+    per_call_us = np.array([a.elapsed_time(b) for a, b in call_ev]) * 1e3
+
     if args.copy_calibration:
         n = args.copy_calibration << 18  # floats
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -484,6 +565,13 @@ def main(argv=None) -> int:
             "avg_launch_us": round(dom_ms * 1e3 / len(timed), 3), "timed_launches": len(timed),
         },
     }
+    out["layer_us"] = {"median": round(float(np.median(per_call_us)), 2),
+                       "p10": round(float(np.percentile(per_call_us, 10)), 2),
+                       "p90": round(float(np.percentile(per_call_us, 90)), 2),
+                       "calls": K, "how": "HIP events around each call, separate pass"}
+    if batched:
+        out["mfma"] = mfma_utilisation(cfg, [t.cpu().numpy() for t in ids],
+                                       float(np.median(per_call_us)))
     if args.events == "all":
         out["stage_us"] = {n: round(v * 1e3 / len(timed), 2) for n, v in zip(names, stage_ms)}
     if graph_ms is not None:

@@ -158,14 +158,10 @@ typedef struct moe_layer_desc {
                           routed gate/up, and down unless down_type says
                           otherwise */
   int32_t shared_type; /* MOE_Q8_0 or MOE_Q4_K: shared gate/up/down */
-  int32_t flags;       /* 0 or MOE_SINGLE_LAUNCH; other bits: MOE_ERR_ARG */
+  int32_t flags;       /* reserved: must be 0 (other values: MOE_ERR_ARG) */
   int32_t down_type;   /* routed down: 0 = expert_type, else one of the types
                           expert_type takes */
 } moe_layer_desc;
-
-/* desc->flags: run batches of 1 to 4 tokens as one kernel launch where the
- * shapes have a single-launch instantiation (see moe_layer_forward). */
-#define MOE_SINGLE_LAUNCH 1
 
 /* Device pointers to the layer's tensors (layouts above). */
 typedef struct moe_layer_weights {
@@ -196,10 +192,7 @@ int32_t moe_tensor_bytes(int32_t dtype, int64_t rows, int64_t cols, int64_t* byt
  * activations and the token-tile list of the grouped GEMMs.  The counter area (the first 16384 bytes) must be
  * zero before the first call that uses the workspace; every call leaves it
  * zero again, so zero-fill a workspace once when it is allocated.  Calls that
- * share a workspace must not overlap in time.  One exception: in the
- * single-launch path every device-side wait is bounded, and if one ever gave
- * up, the 32-bit word at byte offset 1280 of the page becomes nonzero and stays
- * so (that call's outputs are then undefined); it is zero in normal use. */
+ * share a workspace must not overlap in time. */
 int32_t moe_workspace_bytes(const moe_layer_desc* desc, int32_t max_tokens, size_t* bytes);
 
 /* Routing only (steps: router GEMV, top-k with renormalised softmax weights,
@@ -222,20 +215,14 @@ int32_t moe_route(const moe_layer_desc* desc, const float* router, const float* 
  * topk_w [M][k] receive the routing if non-NULL.  workspace must hold
  * moe_workspace_bytes(desc, n_tokens) bytes (device, 256-byte aligned,
  * counter page zero as described above).
- * With MOE_SINGLE_LAUNCH in desc->flags, batches of 1 to 4 tokens whose
- * shapes have a single-launch instantiation run as ONE kernel launch (stage
- * "layer"): a work queue in dependency order
- * (router rows; shared gate/up; routed gate/up per (token, slot) pair;
- * shared down; routed down, each output row tile combined by the last item
- * to finish it).  Other calls of up to 16 tokens run three stages
+ * Calls of up to 16 tokens run three stages
  * ("route_shared_gateup", "gateup", "down_combine").  Larger batches (a
  * prefill micro-batch, "Step-5 Preview GGUF": 512-token micro-batches) run
  * the expert FFNs as grouped GEMMs on the bf16 matrix cores with exact
  * integer quants, fp32 scales and activations split into two bf16 terms,
  * in five stages ("route", "shared_gateup", "gateup", "shared_down",
  * "down_combine"; the shared stages are empty without a shared expert),
- * for every routed type and pairing of gate/up and down types.  The single
- * launch needs down_type equal to expert_type.
+ * for every routed type and pairing of gate/up and down types.
  * moe_stage_count / moe_stage_name say which. */
 int32_t moe_layer_forward(const moe_layer_desc* desc, const moe_layer_weights* weights,
                           const float* x, int32_t n_tokens, float* y,

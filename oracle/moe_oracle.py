@@ -45,6 +45,8 @@ block layouts.  Readings taken here:
 
 from __future__ import annotations
 
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 # ---------------------------------------------------------------------------
@@ -404,7 +406,7 @@ def swiglu_ffn(Wg, Wu, Wd, xs) -> np.ndarray:
 
 def moe_layer(x, router, gate, up, down, *, top_k: int, ffn: int, expert_type: str,
               shared=None, shared_ffn: int = 0, shared_type: str = "q8_0",
-              tokens=None, down_type=None) -> dict:
+              tokens=None, down_type=None, workers: int = 1) -> dict:
     """The routed-MoE layer on x [M][H] (float32 input), in float64.
 
     ``gate``/``up`` are stacked E*F x H tensors in the planar layout of
@@ -413,6 +415,11 @@ def moe_layer(x, router, gate, up, down, *, top_k: int, ffn: int, expert_type: s
     shared expert (Fs x H, Fs x H, H x Fs) or None.  ``tokens`` restricts
     the FFN part to a subset of tokens (routing is always computed for all).
     Returns the routing of ``route`` plus y [len(tokens)][H].
+
+    ``workers`` > 1 evaluates the selected experts' FFNs on that many
+    threads (NumPy releases the interpreter lock inside its array
+    operations).  Each expert's arithmetic and the final slot-order sum are
+    the same either way, so the result does not depend on it.
     """
     X = np.atleast_2d(np.asarray(x, dtype=np.float32)).astype(np.float64)
     M, H = X.shape
@@ -436,13 +443,21 @@ def moe_layer(x, router, gate, up, down, *, top_k: int, ffn: int, expert_type: s
         for j in range(top_k):
             need.setdefault(int(ids[t, j]), []).append((ti, j))
     o = np.zeros((len(toks), top_k, H), dtype=np.float64)
-    for e in sorted(need):
+
+    def expert_out(e):
         Wg = dequant(expert_type, gate, E * F, H, e * F, F)
         Wu = dequant(expert_type, up, E * F, H, e * F, F)
         Wd = dequant(down_type or expert_type, down, E * H, F, e * H, H)
-        pairs = need[e]
-        out = swiglu_ffn(Wg, Wu, Wd, X[[toks[ti] for ti, _ in pairs]])
-        for (ti, j), row in zip(pairs, out):
+        return swiglu_ffn(Wg, Wu, Wd, X[[toks[ti] for ti, _ in need[e]]])
+
+    experts = sorted(need)
+    if workers > 1 and len(experts) > 1:
+        with ThreadPoolExecutor(max_workers=workers) as pool:
+            outs = list(pool.map(expert_out, experts))
+    else:
+        outs = [expert_out(e) for e in experts]
+    for e, out in zip(experts, outs):
+        for (ti, j), row in zip(need[e], out):
             o[ti, j] = row
     for ti, t in enumerate(toks):
         for j in range(top_k):

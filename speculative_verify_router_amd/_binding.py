@@ -30,9 +30,6 @@ class MoeError(RuntimeError):
         self.status = status
 
 
-SINGLE_LAUNCH = 1  # MOE_SINGLE_LAUNCH
-
-
 class _Desc(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("n_experts", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("ffn", ctypes.c_int32),
@@ -56,13 +53,11 @@ class LayerDesc:
     shared_ffn: int = 0
     expert_type: str = "q4_k"
     shared_type: str = "q8_0"
-    single_launch: bool = False  # MOE_SINGLE_LAUNCH
     down_type: Optional[str] = None  # routed down; None: expert_type
 
     def c(self) -> _Desc:
         return _Desc(self.hidden, self.n_experts, self.top_k, self.ffn, self.shared_ffn,
-                     _DTYPES[self.expert_type], _DTYPES[self.shared_type],
-                     SINGLE_LAUNCH if self.single_launch else 0,
+                     _DTYPES[self.expert_type], _DTYPES[self.shared_type], 0,
                      _DTYPES[self.down_type] if self.down_type else 0)
 
 

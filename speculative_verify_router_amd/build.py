@@ -12,6 +12,7 @@ import os
 import shutil
 import subprocess
 import sys
+import time
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -20,10 +21,12 @@ LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libsvr_moe.so")
 # Translation units, compiled in parallel (the expert-kernel families are
 # split out of moe_layer.hip so that no one unit holds every instantiation).
-SOURCES = [os.path.join(CSRC, f) for f in ("moe_layer.hip", "launch_expert.hip", "launch_ffn.hip",
-                                           "accept.hip")]
+SOURCES = [os.path.join(CSRC, f) for f in (
+    "moe_layer.hip", "launch_expert.hip", "launch_ffn.hip", "launch_ffn_q8_0.hip",
+    "launch_ffn_q4_k.hip", "launch_ffn_q2_k.hip", "launch_ffn_q3_k.hip", "launch_ffn_q6_k.hip",
+    "accept.hip")]
 HEADERS = [os.path.join(CSRC, f) for f in ("common.h", "quant.h", "route.h", "ffn.h", "phases.h", "misc.h",
-                                           "flow.h", "gemm.h", "launch.h")] + [
+                                           "gemm.h", "launch.h", "launch_ffn.h")] + [
     os.path.join(ROOT, "include", h) for h in ("moe_layer.h", "moe_accept.h")]
 
 ARCH = "gfx950"
@@ -63,6 +66,7 @@ def build(verbose: bool = False, extra=()) -> str:
     objdir = os.path.join(LIBDIR, "obj")
     os.makedirs(objdir, exist_ok=True)
     objs, procs = [], []
+    t0 = time.time()
     for src in SOURCES:
         obj = os.path.join(objdir, os.path.splitext(os.path.basename(src))[0] + ".o")
         cmd = [hipcc(), *compile_flags(extra), "-c", "-o", obj, src]
@@ -73,6 +77,8 @@ def build(verbose: bool = False, extra=()) -> str:
     for src, p in zip(SOURCES, procs):
         out, err = p.communicate()
         _report(subprocess.CompletedProcess(p.args, p.returncode, out, err), f"hipcc {src}", verbose)
+        if verbose:
+            print(f"# {os.path.basename(src)} compiled by {time.time() - t0:.0f} s", flush=True)
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:

@@ -3,10 +3,7 @@
 // selection and the launch sequence on the caller's HIP stream.
 //
 // Two launch sequences:
-//  * flow (MOE_SINGLE_LAUNCH, 1 to 4 tokens, shapes with a k_flow
-//    instantiation): the whole layer is one launch of k_flow, a
-//    dependency-ordered work queue; one stage, "layer".
-//  * staged (everything else), three stages, each one launch where a fused
+//  * staged (up to 16 tokens), three stages, each one launch where a fused
 //    instantiation exists:
 //      1 route_shared_gateup  router GEMV + shared gate/up; last router
 //                             workgroup: top-k, weights, bucketing
@@ -29,7 +26,6 @@
 
 #include "common.h"
 #include "ffn.h"
-#include "flow.h"
 #include "gemm.h"
 #include "misc.h"
 #include "phases.h"
@@ -49,12 +45,6 @@ constexpr int kPairSlotTokens = 4;
 
 enum Stage { kStPhase1 = 0, kStPhase2, kStPhase3, kNumStages };
 const char* const kStageNames[kNumStages] = {"route_shared_gateup", "gateup", "down_combine"};
-const char* const kFlowStageName = "layer";
-constexpr int kFlowTokens = 4;
-// Weight bytes a routed flow item streams, and bytes each wave of a shared
-// expert item streams (its waves take different tokens over the same rows).
-constexpr double kFlowItemBytes = 256.0 * 1024.0;
-constexpr double kFlowSharedWaveBytes = 64.0 * 1024.0;
 
 struct Plan {
   int H, E, k, F, Fs, et, st, dt, M, flags;  // dt: routed down type
@@ -67,7 +57,7 @@ int check_desc(const moe_layer_desc* d) {
   if (!d) return MOE_ERR_NULL;
   if (d->hidden <= 0 || d->n_experts <= 0 || d->top_k <= 0 || d->ffn <= 0 || d->shared_ffn < 0)
     return MOE_ERR_SHAPE;
-  if (d->flags & ~MOE_SINGLE_LAUNCH) return MOE_ERR_ARG;
+  if (d->flags != 0) return MOE_ERR_ARG;
   if (!routed_type(d->expert_type)) return MOE_ERR_DTYPE;
   if (d->down_type != 0 && !routed_type(d->down_type)) return MOE_ERR_DTYPE;
   if (d->shared_ffn > 0 && !quant_type(d->shared_type)) return MOE_ERR_DTYPE;
@@ -166,69 +156,6 @@ bool launch_phase1(int H, bool shared, int sdtype, const FfnShape& sshape, hipSt
   if (!shared) return launch_phase1_k(H, 0, st, r, s, sdtype);
   return launch_phase1_k(H, exact_key(sdtype, sshape), st, r, s, sdtype) ||
          launch_phase1_k(H, generic_key(sdtype, sshape), st, r, s, sdtype);
-}
-
-// --------------------------------------------------------------------------
-// Flow path.
-// --------------------------------------------------------------------------
-int router_nc(int H) { return H <= 1024 ? 1 : H <= 2048 ? 2 : H <= 4096 ? 4 : H <= 8192 ? 8 : 0; }
-
-struct FlowKey {
-  int nc, sf, sgc, sdc, rf, gc, dc;
-  bool operator==(const FlowKey& o) const {
-    return nc == o.nc && sf == o.sf && sgc == o.sgc && sdc == o.sdc && rf == o.rf && gc == o.gc &&
-           dc == o.dc;
-  }
-};
-
-bool flow_key(const Plan& p, FlowKey* k) {
-  if (!(p.flags & MOE_SINGLE_LAUNCH)) return false;
-  if (p.M < 1 || p.M > kFlowTokens || p.M * p.k > kFlowMaxPairs) return false;
-  if (p.dt != p.et) return false;
-  FfnShape a{}, b{};
-  if (!(k->nc = router_nc(p.H))) return false;
-  if (!ffn_shape(p.et, p.H, &a) || !ffn_shape(p.et, p.F, &b)) return false;
-  k->rf = qfmt(p.et);
-  k->gc = shape_code(a.cpl, a.lpr);
-  k->dc = shape_code(b.cpl, b.lpr);
-  k->sf = 0;
-  k->sgc = k->sdc = shape_code(1, 0);
-  if (p.Fs > 0) {
-    if (!ffn_shape(p.st, p.H, &a) || !ffn_shape(p.st, p.Fs, &b)) return false;
-    k->sf = qfmt(p.st);
-    k->sgc = shape_code(a.cpl, a.lpr);
-    k->sdc = shape_code(b.cpl, b.lpr);
-  }
-  return true;
-}
-
-// One workgroup per item.
-template <int NC, int SF, int SGC, int SDC, int RF, int GC, int DC>
-void launch_flow_t(const FlowArgs& f, hipStream_t st) {
-  const int64_t total = (int64_t)f.n_r + f.n_sg + f.n_g + f.n_sd + f.n_d;
-  hipLaunchKernelGGL((k_flow<NC, SF, SGC, SDC, RF, GC, DC>), dim3((unsigned)total), dim3(kBlock),
-                     0, st, f);
-}
-
-// True if `key` has an instantiation; launches it when f is given.
-bool flow_dispatch(const FlowKey& key, const FlowArgs* f, hipStream_t st) {
-#define SVR_FLOW_CASE(A, B, C, D, E, G, H)                    \
-  if (key == FlowKey{A, B, C, D, E, G, H}) {                 \
-    if (f) launch_flow_t<A, B, C, D, E, G, H>(*f, st);       \
-    return true;                                             \
-  }
-  SVR_FLOW_VARIANTS(SVR_FLOW_CASE)
-#undef SVR_FLOW_CASE
-  return false;
-}
-
-// Rows per item: about kFlowItemBytes of weights, a whole number of steps.
-int flow_rows(double row_bytes_, int step, int rows, double bytes = kFlowItemBytes) {
-  int r = (int)(bytes / row_bytes_) / step * step;
-  if (r < step) r = step;
-  const int all = (rows + step - 1) / step * step;
-  r = r < all ? r : all;
-  return r <= kFlowLdsOut ? r : kFlowLdsOut / step * step;
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -365,87 +292,6 @@ FfnArgs routed_args(const Plan& p, const Buffers& b, bool gateup, const moe_laye
     a.max_rows = (int)std::max(1.0, 65536.0 / rb);
   }
   return a;
-}
-
-// Work items of the flow path (see flow.h).  Returns false if the shapes
-// do not fit it; fills f (pointers from b) if given.
-bool flow_args(const Plan& p, const moe_layer_weights* wt, const float* x, float* y,
-               const Buffers& b, FlowArgs* f) {
-  FlowKey key;
-  if (!flow_key(p, &key) || !flow_dispatch(key, nullptr, nullptr)) return false;
-  const bool shared = p.Fs > 0;
-  FfnShape gs, ds, sgs{}, sds{};
-  ffn_shape(p.et, p.H, &gs);
-  ffn_shape(p.et, p.F, &ds);
-  if (shared) {
-    ffn_shape(p.st, p.H, &sgs);
-    ffn_shape(p.st, p.Fs, &sds);
-  }
-  const int n_pairs = p.M * p.k;
-  // Routed gate/up: the four waves of an item take different rows.
-  const int g_step = kWavesPerBlock * (kWave / gs.lpr);
-  const int g_rows = flow_rows(2.0 * row_bytes(p.et, p.H), g_step, p.F);
-  // Routed down: output row tiles, which the combine follows.
-  const int d_step = kWavesPerBlock * (kWave / ds.lpr);
-  const int d_rows = flow_rows(row_bytes(p.et, p.F), d_step, p.H);
-  const int d_tiles = (p.H + d_rows - 1) / d_rows;
-  if (d_tiles > kFlowMaxTiles) return false;
-  // Shared expert items: the waves of one token split its rows (4 / M
-  // waves per token), about kFlowSharedWaveBytes per wave.  Shared down
-  // items divide an output row tile into sd_per_tile parts.
-  int sg_rows = 0, sd_rows = 0, sd_per_tile = 1;
-  if (shared) {
-    const int rg = kWavesPerBlock / p.M;
-    const int sg_step = rg * (kWave / sgs.lpr), sd_step = rg * (kWave / sds.lpr);
-    sg_rows = flow_rows(2.0 * row_bytes(p.st, p.H), sg_step, p.Fs, kFlowSharedWaveBytes * rg);
-    if (sg_rows * p.M > kFlowLdsOut) sg_rows = kFlowLdsOut / p.M / sg_step * sg_step;
-    const double sd_target = kFlowSharedWaveBytes * rg / row_bytes(p.st, p.Fs);
-    sd_per_tile = 0;
-    for (int n = 1; n <= d_rows; ++n) {
-      const int rows = d_rows / n;
-      if (d_rows % n || rows % sd_step) continue;
-      if (rows * p.M <= kFlowLdsOut && rows <= sd_target) {
-        sd_per_tile = n;
-        break;
-      }
-    }
-    if (!sd_per_tile || sg_rows < sg_step) return false;
-    sd_rows = d_rows / sd_per_tile;
-  }
-  if (!f) return true;
-
-  *f = FlowArgs{};
-  f->r = RouteArgs{wt->router, x, b.logits, b.ids, b.w, BucketOut{}, p.H, p.E, p.k, p.M, p.E,
-                   nullptr, 0};
-  f->n_pairs = n_pairs;
-  f->g = routed_args(p, b, true, wt, x, true);
-  f->g.lpr = gs.lpr;
-  f->g.units_per_block = g_rows;
-  f->g.coherent_in = 1;  // pair experts come from the top-k
-  f->g_tiles = (p.F + g_rows - 1) / g_rows;
-  f->d = routed_args(p, b, false, wt, x, true);
-  f->d.lpr = ds.lpr;
-  f->d.units_per_block = d_rows;
-  f->d.coherent_in = 1;
-  f->d_tiles = d_tiles;
-  f->sd_per_tile = sd_per_tile;
-  if (shared) {
-    f->sg = shared_gateup_args(p, wt, x, b);
-    f->sg.lpr = sgs.lpr;
-    f->sg.units_per_block = sg_rows;
-    f->n_sg = (p.Fs + sg_rows - 1) / sg_rows;
-    f->sd = shared_down_args(p, wt, b);
-    f->sd.lpr = sds.lpr;
-    f->sd.units_per_block = sd_rows;
-    f->sd.coherent_in = 1;
-    f->n_sd = d_tiles * sd_per_tile;
-  }
-  f->c = CombineArgs{b.o, shared ? b.s : nullptr, b.w, y, p.M, p.H, p.k, nullptr};
-  f->ctr = reinterpret_cast<FlowCounters*>(b.ctr);
-  f->n_r = p.E;
-  f->n_g = n_pairs * f->g_tiles;
-  f->n_d = n_pairs * d_tiles;
-  return true;
 }
 
 // ---- Batched path: grouped GEMMs on the matrix cores.
@@ -590,9 +436,7 @@ int forward_impl(const moe_layer_desc* desc, const moe_layer_weights* wt, const 
   Plan p;
   int rc = make_plan(desc, n_tokens, &p);
   if (rc != MOE_OK) return rc;
-  const Buffers nob{};
-  const bool flow = flow_args(p, wt, x, y, nob, nullptr);
-  const int n_stages = flow ? 1 : gemm_path(p) ? kGemmStages : kNumStages;
+  const int n_stages = gemm_path(p) ? kGemmStages : kNumStages;
   if (events && n_events != n_stages + 1) return MOE_ERR_ARG;
   hipStream_t st = (hipStream_t)hip_stream;
   hipEvent_t* ev = events ? (hipEvent_t*)events : nullptr;
@@ -615,17 +459,6 @@ int forward_impl(const moe_layer_desc* desc, const moe_layer_weights* wt, const 
   if (gemm_path(p)) {
     (void)hipGetLastError();
     forward_gemm(p, wt, x, y, b, st, ev);
-    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
-  }
-  if (flow) {
-    FlowArgs f;
-    flow_args(p, wt, x, y, b, &f);
-    FlowKey key;
-    flow_key(p, &key);
-    (void)hipGetLastError();
-    mark(ev, 0, st);
-    flow_dispatch(key, &f, st);
-    mark(ev, 1, st);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
   }
   const BucketOut bo{b.counts, b.offsets, b.slots, b.active, b.nactive};
@@ -778,15 +611,12 @@ int32_t moe_stage_count(const moe_layer_desc* desc, int32_t n_tokens) {
   Plan p;
   const int rc = make_plan(desc, n_tokens, &p);
   if (rc != MOE_OK) return -rc;
-  const Buffers nob{};
-  if (flow_args(p, nullptr, nullptr, nullptr, nob, nullptr)) return 1;
   return gemm_path(p) ? kGemmStages : kNumStages;
 }
 
 const char* moe_stage_name(const moe_layer_desc* desc, int32_t n_tokens, int32_t i) {
   const int n = moe_stage_count(desc, n_tokens);
   if (n <= 0 || i < 0 || i >= n) return nullptr;
-  if (n == 1) return kFlowStageName;
   Plan p;
   make_plan(desc, n_tokens, &p);
   return gemm_path(p) ? kGemmStageNames[i] : kStageNames[i];

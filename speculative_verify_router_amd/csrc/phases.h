@@ -181,7 +181,11 @@ __global__ __launch_bounds__(kDownTokThreads) void k_down_tok(FfnArgs a, Combine
   constexpr int CPL = shape_cpl(S), LPR = shape_lpr(S);
   __shared__ float s_o[kDownTokWaves * kDownTokRows];
   const int t = blockIdx.x / tiles, tile = blockIdx.x - t * tiles;
-  const int wv = threadIdx.x >> 6;
+  // The wave index, and with it the pair and its expert, is uniform over
+  // the wave; saying so keeps the expert's buffer resources in scalar
+  // registers (a per-lane resource turns every load into a readfirstlane
+  // loop).
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ub = tile * a.units_per_block;
   const int ue = min(ub + a.units_per_block, a.rows_per_expert);
   const int r = ub + (int)threadIdx.x;  // the row this thread combines
@@ -194,8 +198,9 @@ __global__ __launch_bounds__(kDownTokThreads) void k_down_tok(FfnArgs a, Combine
     if (j < c.k) {  // wave-uniform
       const int p = t * c.k + j;
       const int ids1[1] = {p}, slot1[1] = {wv};
+      const int e = __builtin_amdgcn_readfirstlane(a.pair_expert[p]);
       ffn_pass<FMT, CPL, 1, false, kDownNst, true, LPR>(
-          a, a.pair_expert[p], ids1, ub, G, ue, LdsOut{s_o, ub, kDownTokRows}, slot1);
+          a, e, ids1, ub, G, ue, LdsOut{s_o, ub, kDownTokRows}, slot1);
     }
     __syncthreads();
     if (own) {

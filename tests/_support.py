@@ -52,9 +52,20 @@ def oracle_kwargs(inp) -> dict:
     return kw
 
 
-def run_oracle(inp, x, tokens=None) -> dict:
-    return om.moe_layer(x, inp.router, inp.gate, inp.up, inp.down, tokens=tokens,
-                        **oracle_kwargs(inp))
+def oracle_workers() -> int:
+    """Threads for the oracle's per-expert loop: the host's cores, at most 16."""
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def run_oracle(inp, x, tokens=None, workers: int = 1) -> dict:
+    if workers <= 1:
+        return om.moe_layer(x, inp.router, inp.gate, inp.up, inp.down, tokens=tokens,
+                            **oracle_kwargs(inp))
+    # One BLAS thread per oracle thread: nested BLAS pools oversubscribe the host.
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(1):
+        return om.moe_layer(x, inp.router, inp.gate, inp.up, inp.down, tokens=tokens,
+                            workers=workers, **oracle_kwargs(inp))
 
 
 def routing_predicate(router, k: int, margin: float = 1e-4, disjoint: bool = False):

@@ -43,21 +43,16 @@ def _stage_names(desc, M):
 
 
 def test_stage_lists_follow_the_launch_path():
-    # Step-3.5-shaped verify layer: with the single-launch flag one launch for
-    # 1..4 tokens, three stages above; three stages without the flag.
-    d = svr.LayerDesc(4096, 288, 8, 1280, 1280, "q4_k", "q8_0", single_launch=True)
-    for M in (1, 2, 3, 4):
-        assert _stage_names(d, M) == ["layer"]
-        assert _stage_names(svr.LayerDesc(4096, 288, 8, 1280, 1280, "q4_k", "q8_0"), M) == [
-            "route_shared_gateup", "gateup", "down_combine"]
-    for M in (5, 16):
+    # Step-3.5-shaped verify layer: three stages up to 16 tokens.
+    d = svr.LayerDesc(4096, 288, 8, 1280, 1280, "q4_k", "q8_0")
+    for M in (1, 2, 3, 4, 5, 16):
         assert _stage_names(d, M) == ["route_shared_gateup", "gateup", "down_combine"]
     # Batches above 16 tokens: the grouped-GEMM path.
     for M in (17, 512):
         assert _stage_names(d, M) == ["route", "shared_gateup", "gateup", "shared_down",
                                       "down_combine"]
-    # Shapes without a single-launch instantiation take the staged path.
-    odd = svr.LayerDesc(640, 5, 2, 96, 160, "q8_0", "q8_0", single_launch=True)
+    # Shapes without a fused instantiation take the same three stages.
+    odd = svr.LayerDesc(640, 5, 2, 96, 160, "q8_0", "q8_0")
     assert _stage_names(odd, 2) == ["route_shared_gateup", "gateup", "down_combine"]
     assert svr.moe_stage_name(d, 4, -1) is None and svr.moe_stage_name(d, 4, 1) is None
     with pytest.raises(svr.MoeError):
@@ -155,10 +150,7 @@ def test_routed_down_type_selects_the_path():
     assert L.moe_stage_count(ctypes.byref(_desc(expert_type="q6_k").c()), 16) == 3
     assert L.moe_stage_count(ctypes.byref(_desc(down_type="q4_k").c()), 512) == 5
     assert L.moe_stage_count(ctypes.byref(_desc(down_type="q8_0").c()), 512) == 5
-    # the single launch needs one type for gate/up and down
-    one = _desc(single_launch=True)
-    assert L.moe_stage_count(ctypes.byref(one.c()), 4) == 1
-    assert L.moe_stage_count(ctypes.byref(_desc(single_launch=True, down_type="q8_0").c()), 4) == 3
+    assert L.moe_stage_count(ctypes.byref(_desc(down_type="q8_0").c()), 4) == 3
     out = ctypes.c_size_t()
     bad = _desc().c()
     bad.down_type = 9
@@ -235,13 +227,13 @@ def test_route_and_dequant_error_paths():
     assert L.moe_dequant_rows(1, None, 10, 64, 0, 0, None, None) == B.OK    # empty range
 
 
-def test_unknown_flag_bits_are_rejected():
+def test_reserved_flags_must_be_zero():
     d = _desc().c()
-    d.flags = 2
     out = ctypes.c_size_t()
-    assert svr.lib().moe_workspace_bytes(ctypes.byref(d), 4, ctypes.byref(out)) == B.ERR_ARG
-    d.flags = B.SINGLE_LAUNCH
     assert svr.lib().moe_workspace_bytes(ctypes.byref(d), 4, ctypes.byref(out)) == B.OK
+    for bad in (1, 2, -1):
+        d.flags = bad
+        assert svr.lib().moe_workspace_bytes(ctypes.byref(d), 4, ctypes.byref(out)) == B.ERR_ARG
 
 
 # --- include/moe_accept.h ---------------------------------------------------

@@ -578,3 +578,20 @@ def test_disjoint_predicate_gives_disjoint_sets():
     x, _ = synth.draw_tokens(cfg, accept=pred)
     ids = om.route(inp.router, x, 8)["ids"]
     assert len(set(ids.reshape(-1).tolist())) == 32
+
+
+@pytest.mark.parametrize("expert_type", ["q8_0", "q4_k"])
+def test_threaded_expert_loop_gives_the_same_layer(expert_type):
+    # The oracle's optional thread pool only changes where each expert's FFN
+    # runs: outputs, ids and weights equal the one-thread evaluation bit for bit.
+    cfg = small_config(n_experts=12, top_k=3, n_tokens=9, expert_type=expert_type,
+                       ffn=256, shared_ffn=64)
+    inp = synth.draw_layer(cfg, threads=1)
+    x, _ = synth.draw_tokens(cfg)
+    kw = oracle_kwargs(inp)
+    one = om.moe_layer(x, inp.router, inp.gate, inp.up, inp.down, **kw)
+    many = om.moe_layer(x, inp.router, inp.gate, inp.up, inp.down, workers=4, **kw)
+    assert np.array_equal(one["ids"], many["ids"])
+    assert np.array_equal(one["w"], many["w"])
+    assert np.array_equal(one["y"], many["y"])
+    assert len(one["active"]) > 3
