@@ -229,6 +229,25 @@ int32_t moe_layer_forward(const moe_layer_desc* desc, const moe_layer_weights* w
                           int32_t* topk_ids, float* topk_w,
                           void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * moe_layer_forward without a workspace argument.  The workspace is a
+ * device array inside the library of MOE_NOALLOC_MAX_WORKSPACE bytes, one
+ * per GPU, held until the process ends; the call allocates nothing (no
+ * hipMalloc, no hipFree).  A call whose moe_workspace_bytes(desc, n_tokens)
+ * exceeds MOE_NOALLOC_MAX_WORKSPACE returns MOE_ERR_WORKSPACE before
+ * enqueueing anything (at H = 4096 batches up to 16 tokens fit; 512-token
+ * prefill batches do not).  The first call on a device looks up the array's
+ * address and clears its counter page on hip_stream.  Every call on a GPU
+ * shares that GPU's array, so calls that overlap in time on one GPU (other
+ * streams, other threads) race and must be serialised by the caller.
+ * Arguments, outputs and the other status codes are those of
+ * moe_layer_forward. */
+#define MOE_NOALLOC_MAX_WORKSPACE (8u << 20)
+int32_t moe_layer_forward_noalloc(const moe_layer_desc* desc, const moe_layer_weights* weights,
+                                  const float* x, int32_t n_tokens, float* y,
+                                  int32_t* topk_ids, float* topk_w, void* hip_stream);
+
 /* Number of stages a moe_layer_forward call with this desc and n_tokens
  * enqueues (1, 3 or 5; the negated status code if desc is invalid), and the
  * name of stage i (static string; NULL if i or desc is invalid). */

@@ -14,6 +14,7 @@ from ._binding import (  # noqa: F401
     LIB_PATH,
     LayerDesc,
     LayerWeights,
+    NOALLOC_MAX_WORKSPACE,
     MoeError,
     PreparedForward,
     accept_workspace,
@@ -21,6 +22,7 @@ from ._binding import (  # noqa: F401
     moe_accept_workspace_bytes,
     moe_dequant_rows,
     moe_layer_forward,
+    moe_layer_forward_noalloc,
     moe_layer_forward_timed,
     moe_route,
     moe_stage_count,

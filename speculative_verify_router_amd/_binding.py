@@ -100,6 +100,7 @@ def lib():
             "moe_layer_forward": (i32, [D, W, vp, i32, vp, vp, vp, vp, sz, vp]),
             "moe_layer_forward_timed": (i32, [D, W, vp, i32, vp, vp, vp, vp, sz, vp,
                                               ctypes.POINTER(vp), i32]),
+            "moe_layer_forward_noalloc": (i32, [D, W, vp, i32, vp, vp, vp, vp]),
             "moe_stage_count": (i32, [D, i32]),
             "moe_stage_name": (ctypes.c_char_p, [D, i32, i32]),
             "moe_dequant_rows": (i32, [i32, vp, i64, i32, i64, i64, vp, vp]),
@@ -116,7 +117,8 @@ def lib():
 
 # Exported names of the C ABI (the header declares exactly these).
 C_SYMBOLS = ("moe_version", "moe_strerror", "moe_tensor_bytes", "moe_workspace_bytes",
-             "moe_route", "moe_layer_forward", "moe_layer_forward_timed", "moe_stage_count",
+             "moe_route", "moe_layer_forward", "moe_layer_forward_timed",
+             "moe_layer_forward_noalloc", "moe_stage_count",
              "moe_stage_name", "moe_dequant_rows", "moe_accept_workspace_bytes",
              "moe_verify_accept")
 
@@ -238,6 +240,21 @@ def moe_layer_forward_timed(desc: LayerDesc, weights: LayerWeights, x: torch.Ten
                                        _ptr(topk_w, torch.float32), _ptr(ws, torch.uint8),
                                        ws.numel(), _stream(stream), arr, len(events))
     _check(st, "moe_layer_forward_timed")
+
+
+# Workspace bytes that moe_layer_forward_noalloc holds per GPU (MOE_NOALLOC_MAX_WORKSPACE).
+NOALLOC_MAX_WORKSPACE = 8 << 20
+
+
+def moe_layer_forward_noalloc(desc: LayerDesc, weights: LayerWeights, x: torch.Tensor,
+                              y: torch.Tensor, topk_ids=None, topk_w=None, stream=None):
+    """moe_layer_forward with the library's own per-GPU workspace (no allocation)."""
+    M = x.shape[0]
+    d, w = desc.c(), weights.c()
+    st = lib().moe_layer_forward_noalloc(ctypes.byref(d), ctypes.byref(w), _ptr(x, torch.float32),
+                                         M, _ptr(y, torch.float32), _ptr(topk_ids, torch.int32),
+                                         _ptr(topk_w, torch.float32), _stream(stream))
+    _check(st, "moe_layer_forward_noalloc")
 
 
 class PreparedForward:

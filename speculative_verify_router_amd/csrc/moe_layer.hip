@@ -539,6 +539,43 @@ int forward_impl(const moe_layer_desc* desc, const moe_layer_weights* wt, const 
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }
 
+// ---- Allocation-free entry point.  Its workspace is this file-scope device
+// array: every GPU the library runs on holds one copy until the process
+// ends, and every call on that GPU shares it.  Host code must not pass the
+// array's name to a kernel (that is a host-side stand-in): the device
+// address comes from hipGetSymbolAddress, taken once per device with that
+// device current, and is used everywhere the host needs the array.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_MAX_WORKSPACE];
+
+// Fill kernel for the scratch counter page (no memset node, so that a
+// caller may capture the first call in a graph).
+static __global__ __launch_bounds__(kBlock) void k_zero_words(uint32_t* p, int n) {
+  for (int i = blockIdx.x * kBlock + threadIdx.x; i < n; i += gridDim.x * kBlock) p[i] = 0u;
+}
+
+constexpr int kMaxDevices = 64;
+
+// Device address of `scratch` on the current device: looked up on the first
+// call on each device, when its counter page is also cleared on `st`.
+int scratch_address(hipStream_t st, void** out) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_LAUNCH;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(k_zero_words, dim3(kCounterBytes / 4 / kBlock), dim3(kBlock), 0, st,
+                       (uint32_t*)p, kCounterBytes / 4);
+    if (hipGetLastError() != hipSuccess) return MOE_ERR_LAUNCH;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -647,6 +684,22 @@ int32_t moe_layer_forward(const moe_layer_desc* desc, const moe_layer_weights* w
                           void* hip_stream) {
   return forward_impl(desc, weights, x, n_tokens, y, topk_ids, topk_w, workspace, workspace_bytes,
                       hip_stream, nullptr, 0);
+}
+
+int32_t moe_layer_forward_noalloc(const moe_layer_desc* desc, const moe_layer_weights* weights,
+                                  const float* x, int32_t n_tokens, float* y, int32_t* topk_ids,
+                                  float* topk_w, void* hip_stream) {
+  if (!desc || !weights) return MOE_ERR_NULL;
+  Plan p;
+  const int rc = make_plan(desc, n_tokens, &p);
+  if (rc != MOE_OK) return rc;
+  if (p.total > (size_t)MOE_NOALLOC_MAX_WORKSPACE) return MOE_ERR_WORKSPACE;
+  if (n_tokens == 0) return MOE_OK;
+  void* ws = nullptr;
+  const int rs = scratch_address((hipStream_t)hip_stream, &ws);
+  if (rs != MOE_OK) return rs;
+  return forward_impl(desc, weights, x, n_tokens, y, topk_ids, topk_w, ws,
+                      (size_t)MOE_NOALLOC_MAX_WORKSPACE, hip_stream, nullptr, 0);
 }
 
 int32_t moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_weights* weights,

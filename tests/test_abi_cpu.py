@@ -54,7 +54,7 @@ def test_stage_lists_follow_the_launch_path():
     # Shapes without a fused instantiation take the same three stages.
     odd = svr.LayerDesc(640, 5, 2, 96, 160, "q8_0", "q8_0")
     assert _stage_names(odd, 2) == ["route_shared_gateup", "gateup", "down_combine"]
-    assert svr.moe_stage_name(d, 4, -1) is None and svr.moe_stage_name(d, 4, 1) is None
+    assert svr.moe_stage_name(d, 4, -1) is None and svr.moe_stage_name(d, 4, 3) is None
     with pytest.raises(svr.MoeError):
         svr.moe_stage_count(svr.LayerDesc(4096, 288, 8, 1000, 0, "q4_k", "q8_0"), 4)
 
@@ -279,3 +279,24 @@ def test_accept_error_paths():
     assert _accept(ws=FAKE + 16) == B.ERR_ARG            # misaligned workspace
     assert _accept(logits=FAKE + 2) == B.ERR_ARG         # logits not 4-byte aligned
     assert _accept(M=0, logits=None, ws=None) == B.OK    # empty batch: nothing enqueued
+
+
+def test_noalloc_limit_matches_header_and_rejects_large_batches():
+    text = open(os.path.join(INCLUDE, "moe_layer.h")).read()
+    m = re.search(r"#define MOE_NOALLOC_MAX_WORKSPACE \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == svr.NOALLOC_MAX_WORKSPACE
+    L = svr.lib()
+    step5 = svr.LayerDesc(4096, 352, 8, 1536, 1536, "q4_k", "q8_0")
+    # A 16-token verify batch fits the library's workspace; a 512-token
+    # prefill batch does not, and is refused before anything is enqueued.
+    assert svr.moe_workspace_bytes(step5, 16) <= svr.NOALLOC_MAX_WORKSPACE
+    assert svr.moe_workspace_bytes(step5, 512) > svr.NOALLOC_MAX_WORKSPACE
+    w = B._Weights()
+    assert L.moe_layer_forward_noalloc(ctypes.byref(step5.c()), ctypes.byref(w), None, 512, None,
+                                       None, None, None) == B.ERR_WORKSPACE
+    assert L.moe_layer_forward_noalloc(None, ctypes.byref(w), None, 4, None, None, None,
+                                       None) == B.ERR_NULL
+    bad = step5.c()
+    bad.flags = 1
+    assert L.moe_layer_forward_noalloc(ctypes.byref(bad), ctypes.byref(w), None, 4, None, None,
+                                       None, None) == B.ERR_ARG
