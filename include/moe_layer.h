@@ -186,13 +186,20 @@ const char* moe_strerror(int32_t status);
 int32_t moe_tensor_bytes(int32_t dtype, int64_t rows, int64_t cols, int64_t* bytes);
 
 /* Device workspace, in *bytes, that moe_layer_forward and moe_route need for
- * up to max_tokens tokens: 16 KiB of hand-off counters, router logits,
- * routing lists, the SwiGLU activations of every (token, slot) pair, the
- * per-pair expert outputs, and for batches above 16 tokens the split
- * activations and the token-tile list of the grouped GEMMs.  The counter area (the first 16384 bytes) must be
- * zero before the first call that uses the workspace; every call leaves it
- * zero again, so zero-fill a workspace once when it is allocated.  Calls that
- * share a workspace must not overlap in time. */
+ * up to max_tokens tokens: hand-off areas, router logits, routing lists,
+ * the SwiGLU activations of every (token, slot) pair, the per-pair expert
+ * outputs, and for batches above 16 tokens the split activations and the
+ * token-tile list of the grouped GEMMs.  The hand-off areas at the start
+ * (16384 bytes of counters, then E*64 bytes of routing keys rounded up to a
+ * multiple of 256) must be zero before the first call that uses the
+ * workspace; every call leaves them zero again, so zero-fill a workspace
+ * once when it is allocated.  Calls that share a workspace must not overlap
+ * in time.  The routing step of calls of up to 16 tokens waits, with a
+ * bounded poll, for router results of workgroups that the GPU dispatches
+ * before it, so the wait always ends in normal operation; if it ever gave
+ * up, that call's routing weights (and so its outputs) are NaN and the
+ * first 32-bit word of the workspace is set nonzero (the kernels never read
+ * it; the caller may check and clear it). */
 int32_t moe_workspace_bytes(const moe_layer_desc* desc, int32_t max_tokens, size_t* bytes);
 
 /* Routing only (steps: router GEMV, top-k with renormalised softmax weights,

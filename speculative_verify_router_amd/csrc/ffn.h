@@ -52,7 +52,6 @@ struct FfnArgs {
   int coherent_out;         // 1: outputs are read by other workgroups of this launch
   const int32_t* pair_expert;  // pair slots: slot p is pair p, expert pair_expert[p]
   int n_pairs;                 // number of pair slots (pair_expert != NULL)
-  int coherent_in;  // 1: act and pair_expert were written earlier in this launch
   int max_rows;     // host side: cap on units_per_block (0: none)
 };
 
@@ -160,8 +159,10 @@ __device__ __forceinline__ void compute_stage(const Stage<FMT, CPL, GATEUP>& s,
 // the NT tokens whose pair ids are given (LDSOUT: outputs to lo, token t of
 // the pass in slot lds_slot[t]).
 // NSTD: ring depth (0: nst_for); LPR: lanes per row when known at compile
-// time (0: a.lpr).
-template <int FMT, int CPL, int NT, bool GATEUP, int NSTD = 0, bool LDSOUT = false, int LPR = 0>
+// time (0: a.lpr); XCOH: the activations were written earlier in this
+// launch (read past L2).
+template <int FMT, int CPL, int NT, bool GATEUP, int NSTD = 0, bool LDSOUT = false, int LPR = 0,
+          bool XCOH = false>
 __device__ __forceinline__ void ffn_pass(const FfnArgs& a, int expert, const int* pair_ids,
                                          int first, int step, int ue, LdsOut lo = LdsOut{},
                                          const int* lds_slot = nullptr) {
@@ -182,25 +183,13 @@ __device__ __forceinline__ void ffn_pass(const FfnArgs& a, int expert, const int
 #pragma unroll
   for (int ci = 0; ci < CPL; ++ci) cc[ci] = min(j + lpr * ci, nchunks - 1);
 
-  XSlice<FMT> xs[NT][CPL];
-  int out_row[NT], slot[NT];
+  int out_row[NT], slot[NT], xrow[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const int p = pair_ids[t];
     out_row[t] = p;
     slot[t] = LDSOUT ? lds_slot[t] : 0;
-    const int xrow = a.act_by_pair ? p : p / a.top_k;
-#pragma unroll
-    for (int ci = 0; ci < CPL; ++ci) {
-      if (j + lpr * ci < nchunks) {
-        if (a.coherent_in)
-          load_x_shared<FMT>(xs[t][ci], a.act, xrow * a.K, j + lpr * ci);
-        else
-          load_x<FMT>(xs[t][ci], a.act + (int64_t)xrow * a.K, j + lpr * ci);
-      } else {
-        zero_x<FMT>(xs[t][ci]);
-      }
-    }
+    xrow[t] = a.act_by_pair ? p : p / a.top_k;
   }
 
   // Row of lane group g at step base: base + g.  The loop is branch-free
@@ -220,6 +209,13 @@ __device__ __forceinline__ void ffn_pass(const FfnArgs& a, int expert, const int
     q_pre += q_step;
     s_pre += s_step;
   }
+  // The activations after the weights' first stages: both round trips
+  // overlap, and the slices are quantised while the weights are in flight
+  // (the scheduling barrier keeps the compiler from sinking the weight
+  // loads below the quantisation).
+  __builtin_amdgcn_sched_barrier(0);
+  XSlice<FMT> xs[NT][CPL];
+  load_slices<FMT, NT, CPL, XCOH>(xs, a.act, xrow, a.K, j, lpr, nchunks);
   for (int base = first; base < ue; base += NST * step) {
 #pragma unroll
     for (int s = 0; s < NST; ++s) {
@@ -258,7 +254,7 @@ __device__ __forceinline__ void ffn_tile_pair(const FfnArgs& a, int slot, int ti
   if (ub >= ue) return;
   const int G = kWave / (LPR ? LPR : a.lpr);
   const int ids1[1] = {slot}, slot0[1] = {0};
-  const int e = a.coherent_in ? load_shared(a.pair_expert + slot) : a.pair_expert[slot];
+  const int e = a.pair_expert[slot];
   ffn_pass<FMT, CPL, 1, GATEUP, NSTD, LDSOUT, LPR>(a, e, ids1, ub + (threadIdx.x >> 6) * G,
                                                    kWavesPerBlock * G, ue,
                                                    LdsOut{lds, ub, a.units_per_block}, slot0);
@@ -270,23 +266,24 @@ __device__ __forceinline__ void ffn_tile_pair(const FfnArgs& a, int slot, int ti
 // (M = 3: one wave idles); with more, wave w takes tokens w, w + 4, ...
 // over all rows.  So the rows are fetched from HBM once per workgroup and
 // idle waves of a small batch still stream.
-template <int FMT, int CPL, bool GATEUP, int NSTD = 0, int LPR = 0>
+template <int FMT, int CPL, bool GATEUP, int NSTD = 0, int LPR = 0, bool XCOH = false>
 __device__ __forceinline__ void ffn_tile_tokens(const FfnArgs& a, int tile) {
   const int ub = tile * a.units_per_block;
   const int ue = min(ub + a.units_per_block, a.rows_per_expert);
   if (ub >= ue) return;
   const int G = kWave / (LPR ? LPR : a.lpr);
-  const int wv = threadIdx.x >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (a.n_tokens <= kWavesPerBlock) {
     const int rg = kWavesPerBlock / a.n_tokens;
     const int t = wv / rg, q = wv - t * rg;
     const int ids1[1] = {t};
-    if (t < a.n_tokens) ffn_pass<FMT, CPL, 1, GATEUP, NSTD, false, LPR>(a, 0, ids1, ub + q * G, rg * G, ue);
+    if (t < a.n_tokens)
+      ffn_pass<FMT, CPL, 1, GATEUP, NSTD, false, LPR, XCOH>(a, 0, ids1, ub + q * G, rg * G, ue);
     return;
   }
   for (int t = wv; t < a.n_tokens; t += kWavesPerBlock) {
     const int ids1[1] = {t};
-    ffn_pass<FMT, CPL, 1, GATEUP, NSTD, false, LPR>(a, 0, ids1, ub, G, ue);
+    ffn_pass<FMT, CPL, 1, GATEUP, NSTD, false, LPR, XCOH>(a, 0, ids1, ub, G, ue);
   }
 }
 

@@ -25,7 +25,7 @@ inline int wpc_of(int dtype) {
 }
 inline int blk_of(int dtype) { return dtype == MOE_Q8_0 ? 32 : 256; }
 // Types of the shared expert, and of the routed experts (also Q2_K, Q3_K,
-// Q6_K, which have GEMV kernels only).
+// Q6_K).
 inline bool quant_type(int dtype) { return dtype == MOE_Q8_0 || dtype == MOE_Q4_K; }
 inline bool gemv_only_type(int dtype) {
   return dtype == MOE_Q2_K || dtype == MOE_Q3_K || dtype == MOE_Q6_K;

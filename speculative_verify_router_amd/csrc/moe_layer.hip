@@ -5,7 +5,7 @@
 // Two launch sequences:
 //  * staged (up to 16 tokens), three stages, each one launch where a fused
 //    instantiation exists:
-//      1 route_shared_gateup  router GEMV + shared gate/up; last router
+//      1 route_shared_gateup  router GEMV + shared gate/up; the grid's last
 //                             workgroup: top-k, weights, bucketing
 //      2 gateup               routed gate/up + SwiGLU, shared down
 //      3 down_combine         routed down; last workgroup per row tile
@@ -48,8 +48,8 @@ const char* const kStageNames[kNumStages] = {"route_shared_gateup", "gateup", "d
 
 struct Plan {
   int H, E, k, F, Fs, et, st, dt, M, flags;  // dt: routed down type
-  size_t ctr, logits, ids, w, counts, offsets, slots, active, nactive, h, hs, o, s, xs, tiles,
-      total;
+  size_t ctr, keys, logits, ids, w, counts, offsets, slots, active, nactive, h, hs, o, s, xs,
+      tiles, total;
   int tiles_cap;  // routed token tiles of the batched path, at most
 };
 
@@ -94,7 +94,11 @@ int make_plan(const moe_layer_desc* d, int M, Plan* p) {
     off = align256(off + bytes);
     return o;
   };
+  // Hand-off areas, zero between calls, at offsets that depend on E only
+  // (so that calls of any batch size agree on them): counters, then the
+  // routing keys of up to kFusedMaxTokens tokens.
   p->ctr = take(kCounterBytes);
+  p->keys = take((size_t)p->E * kFusedMaxTokens * 4);
   p->logits = take(Mz * p->E * 4);
   p->ids = take(P * 4);
   p->w = take(P * 4);
@@ -125,12 +129,14 @@ bool launch_phase1_nc(int skey, hipStream_t st, const RouteArgs& r, FfnArgs s, i
   case key(F, shape_code(C, L)): {                                                       \
     auto k = k_phase1<NC, F, shape_code(C, L)>;                                          \
     const int64_t cap = resident_blocks(k);                                              \
-    size_shared_tiles(s, sdtype, std::max<int64_t>(cap - r.n_router_blocks, cap / 4));  \
-    hipLaunchKernelGGL(k, dim3(r.n_router_blocks + tiles_of(s)), dim3(kBlock), 0, st, r, s); \
+    size_shared_tiles(s, sdtype, std::max<int64_t>(cap - r.n_router_blocks - 1, cap / 4)); \
+    hipLaunchKernelGGL(k, dim3(r.n_router_blocks + tiles_of(s) + 1), dim3(kBlock), 0, st, r, \
+                       s);                                                               \
     return true;                                                                         \
   }
     case 0:
-      hipLaunchKernelGGL((k_phase1<NC, 0, 1>), dim3(r.n_router_blocks), dim3(kBlock), 0, st, r, s);
+      hipLaunchKernelGGL((k_phase1<NC, 0, 1>), dim3(r.n_router_blocks + 1), dim3(kBlock), 0, st,
+                         r, s);
       return true;
     SVR_P1(kQ8_0, 4, 64)
     SVR_P1(kQ8_0, 1, 0) SVR_P1(kQ8_0, 2, 0) SVR_P1(kQ8_0, 4, 0) SVR_P1(kQ8_0, 5, 0)
@@ -168,6 +174,7 @@ inline void mark(hipEvent_t* ev, int i, hipStream_t st) {
 
 struct Buffers {
   Counters* ctr;
+  uint32_t* keys;
   float *logits, *w, *h, *hs, *o, *s;
   int32_t *ids, *counts, *offsets, *slots, *active, *nactive, *tiles, *ntiles;
   uint4* xs;
@@ -177,6 +184,7 @@ Buffers carve(const Plan& p, void* ws, int32_t* ids, float* w) {
   uint8_t* b = (uint8_t*)ws;
   Buffers r;
   r.ctr = (Counters*)(b + p.ctr);
+  r.keys = (uint32_t*)(b + p.keys);
   r.logits = (float*)(b + p.logits);
   r.ids = ids ? ids : (int32_t*)(b + p.ids);
   r.w = w ? w : (float*)(b + p.w);
@@ -477,7 +485,7 @@ int forward_impl(const moe_layer_desc* desc, const moe_layer_weights* wt, const 
   }
   bool fused1 = false;
   if (p.M <= kFusedMaxTokens) {
-    RouteArgs r{wt->router, x, b.logits, b.ids, b.w, bo, p.H, p.E, p.k, p.M, p.E, b.ctr, !pairs};
+    RouteArgs r{wt->router, x, b.keys, b.ids, b.w, bo, p.H, p.E, p.k, p.M, p.E, b.ctr, !pairs};
     fused1 = launch_phase1(p.H, shared, p.st, ss, st, r, sgu);
     if (!fused1 && shared) {
       // No fused instantiation for this shared shape: route alone, then the
@@ -547,16 +555,19 @@ int forward_impl(const moe_layer_desc* desc, const moe_layer_weights* wt, const 
 // device current, and is used everywhere the host needs the array.
 static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_MAX_WORKSPACE];
 
-// Fill kernel for the scratch counter page (no memset node, so that a
+// Fill kernel for the scratch hand-off areas (no memset node, so that a
 // caller may capture the first call in a graph).
 static __global__ __launch_bounds__(kBlock) void k_zero_words(uint32_t* p, int n) {
   for (int i = blockIdx.x * kBlock + threadIdx.x; i < n; i += gridDim.x * kBlock) p[i] = 0u;
 }
 
 constexpr int kMaxDevices = 64;
+// Hand-off areas at the start of any workspace: counters and the routing
+// keys of the largest layer.
+constexpr int kHandoffBytesMax = kCounterBytes + kMaxExperts * kFusedMaxTokens * 4;
 
 // Device address of `scratch` on the current device: looked up on the first
-// call on each device, when its counter page is also cleared on `st`.
+// call on each device, when its hand-off areas are also cleared on `st`.
 int scratch_address(hipStream_t st, void** out) {
   static std::mutex mu;
   static void* addr[kMaxDevices];
@@ -567,8 +578,8 @@ int scratch_address(hipStream_t st, void** out) {
     void* p = nullptr;
     if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_LAUNCH;
     (void)hipGetLastError();
-    hipLaunchKernelGGL(k_zero_words, dim3(kCounterBytes / 4 / kBlock), dim3(kBlock), 0, st,
-                       (uint32_t*)p, kCounterBytes / 4);
+    hipLaunchKernelGGL(k_zero_words, dim3(kHandoffBytesMax / 4 / kBlock), dim3(kBlock), 0, st,
+                       (uint32_t*)p, kHandoffBytesMax / 4);
     if (hipGetLastError() != hipSuccess) return MOE_ERR_LAUNCH;
     addr[dev] = p;
   }

@@ -1,8 +1,9 @@
 // Fused launches of the small-batch (decode / verify) path.
 //
-//   phase 1: router rows + shared-expert gate/up tiles; the last router
-//            workgroup to finish runs top-k for every token and the
-//            bucketing, so routing costs no launch of its own.
+//   phase 1: router rows + shared-expert gate/up tiles; the last workgroup
+//            of the grid waits for the router rows' keys, runs top-k for
+//            every token and the bucketing, so routing costs no launch of
+//            its own.
 //   phase 2: routed gate/up tiles + shared-expert down tiles.
 //   phase 3: routed down tiles; the last workgroup to finish a row tile
 //            (over all active experts) combines that tile of the output.
@@ -18,11 +19,6 @@
 namespace svr {
 
 constexpr int kMaxTiles = 1008;  // combine counters available in the workspace
-// Router workgroups arrive in groups (workgroup index mod kRouterGroups),
-// each group on its own 256-byte line; the last of a group arrives on
-// router_done.  One counter bumped by every router workgroup serialises
-// hundreds of atomics on one address.
-constexpr int kRouterGroups = 16;
 
 struct alignas(256) CounterLine {
   unsigned v;
@@ -30,17 +26,18 @@ struct alignas(256) CounterLine {
 };
 
 struct Counters {
-  unsigned router_done;
-  unsigned pad[15];
+  // Nonzero once the routing's wait for the router keys has given up;
+  // written, never read, by the kernels: a diagnostic word for the caller.
+  unsigned route_wait_err;
+  unsigned pad[63];
   unsigned tile_done[kMaxTiles];
-  CounterLine router_group[kRouterGroups];
 };
-static_assert(sizeof(Counters) == 8192 && sizeof(Counters) <= kCounterBytes, "counter pages");
+static_assert(sizeof(Counters) <= kCounterBytes, "counter page");
 
 struct RouteArgs {
   const float* router;
   const float* x;
-  float* logits;
+  uint32_t* keys;  // [M][E] routing keys, zero between calls
   int32_t* ids;
   float* w;
   BucketOut b;
@@ -50,44 +47,34 @@ struct RouteArgs {
   int bucket;  // 1: also build the per-expert lists (not needed with pair slots)
 };
 
+// Router workgroups: one expert row each, its M logits published as keys.
 template <int NC>
 __device__ __forceinline__ void router_part(const RouteArgs& r, int blk) {
-  __shared__ int s_last;
+  router_row_keys<NC>(r.router, r.x, r.keys, r.H, r.E, r.M, blk);
+}
+
+// The routing workgroup (dispatched after every router workgroup it waits
+// for): wave w takes tokens w, w + 4, ..., polls each token's keys,
+// selects its experts and clears the keys; then, if asked, the per-expert
+// lists.
+__device__ __forceinline__ void route_part(const RouteArgs& r) {
   const int wv = threadIdx.x >> 6;
-  router_row_block<NC>(r.router, r.x, r.logits, r.H, r.E, r.M, blk);
-  wait_stores();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int g = blk % kRouterGroups;
-    const int n_g = (r.n_router_blocks - g + kRouterGroups - 1) / kRouterGroups;
-    int last = 0;
-    if (arrive(&r.ctr->router_group[g].v) == (unsigned)(n_g - 1)) {
-      // Every workgroup of group g has arrived: reset its line for the next
-      // call, then arrive as the group on router_done.
-      __hip_atomic_store(&r.ctr->router_group[g].v, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const int n_groups = min(kRouterGroups, r.n_router_blocks);
-      last = arrive(&r.ctr->router_done) == (unsigned)(n_groups - 1);
-    }
-    s_last = last;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  // Logits of the other workgroups are read with load_shared (coherent).
   for (int t = wv; t < r.M; t += kWavesPerBlock)
-    topk_token<true>(r.logits + (int64_t)t * r.E, r.ids + (int64_t)t * r.k,
-                     r.w + (int64_t)t * r.k, r.E, r.k);
+    topk_keys_poll(r.keys + (int64_t)t * r.E, r.ids + (int64_t)t * r.k, r.w + (int64_t)t * r.k,
+                   r.E, r.k, &r.ctr->route_wait_err);
   if (r.bucket) {
     __syncthreads();
     bucket_block(r.ids, r.M * r.k, r.E, r.b);
   }
-  if (threadIdx.x == 0)
-    __hip_atomic_store(&r.ctr->router_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Phase 1.  SFMT == 0: no shared expert; SS: shared gate/up shape code.
+// Grid: router workgroups, shared gate/up tiles, then the routing workgroup.
 template <int NC, int SFMT, int SS>
 __global__ __launch_bounds__(kBlock) void k_phase1(RouteArgs r, FfnArgs s) {
-  if ((int)blockIdx.x < r.n_router_blocks) {
+  if (blockIdx.x == gridDim.x - 1) {
+    route_part(r);
+  } else if ((int)blockIdx.x < r.n_router_blocks) {
     router_part<NC>(r, blockIdx.x);
   } else if constexpr (SFMT != 0) {
     ffn_tile<SFMT, shape_cpl(SS), true, shape_lpr(SS)>(s, 0, blockIdx.x - r.n_router_blocks);

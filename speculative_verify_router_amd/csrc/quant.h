@@ -299,60 +299,47 @@ __device__ __forceinline__ void quantize_slice(XSlice<FMT>& xs, const float (&v)
   }
 }
 
-template <int FMT>
-__device__ __forceinline__ void load_x(XSlice<FMT>& xs, const float* row, int c) {
+// Every activation slice of a pass at once: slice (t, ci) is chunk
+// j + lpr * ci of activation row xrow[t] (K values per row).  All loads are
+// issued before the first slice is quantised, so the pass waits for one
+// memory round trip, not one per slice.  A chunk at or past `nchunks` reads
+// at an offset beyond the buffer resource, which returns zeros, and an
+// all-zero slice quantises to zero limbs, scale and sums.  XCOH: the
+// activations were written earlier in this launch by other workgroups (with
+// write-through stores), so the loads read past the per-XCD L2.
+template <int FMT, int NT, int CPL, bool XCOH = false>
+__device__ __forceinline__ void load_slices(XSlice<FMT> (&xs)[NT][CPL], const float* act,
+                                            const int (&xrow)[NT], int K, int j, int lpr,
+                                            int nchunks) {
   constexpr int W = QTraits<FMT>::kWpc;
-  const float* p = row + W * c;
-  float v[W];
+  constexpr uint32_t kOutside = 0x7FFFFFF0u;
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(act, kOutside);
+  f32x4 v[NT][CPL][W / 4];
 #pragma unroll
-  for (int i = 0; i < W / 4; ++i) {
-    const float4 a = ldf4(p + 4 * i);
-    v[4 * i + 0] = a.x;
-    v[4 * i + 1] = a.y;
-    v[4 * i + 2] = a.z;
-    v[4 * i + 3] = a.w;
-  }
-  quantize_slice<FMT, W>(xs, v);
-}
-
-// load_x for activations another workgroup of this launch wrote with
-// store_shared: 16-byte loads past the per-XCD L2.  `base` is the start of
-// the activation buffer, `row_off` the row's first element.
-template <int FMT>
-__device__ __forceinline__ void load_x_shared(XSlice<FMT>& xs, const float* base, int row_off,
-                                              int c) {
-  constexpr int W = QTraits<FMT>::kWpc;
-  const __amdgpu_buffer_rsrc_t r = make_rsrc(base, 0x7FFFFFF0u);
-  const uint32_t off = 4u * (uint32_t)(row_off + W * c);
-  float v[W];
+  for (int t = 0; t < NT; ++t)
 #pragma unroll
-  for (int i = 0; i < W / 4; ++i) {
-    const f32x4 a = bload16_shared(r, off + 16u * i);
-    v[4 * i + 0] = a.x;
-    v[4 * i + 1] = a.y;
-    v[4 * i + 2] = a.z;
-    v[4 * i + 3] = a.w;
-  }
-  quantize_slice<FMT, W>(xs, v);
-}
-
-template <int FMT>
-__device__ __forceinline__ void zero_x(XSlice<FMT>& xs) {
-  constexpr int D = (FMT == kQ2_K || FMT == kQ3_K) ? 16 : (FMT == kQ4_K || FMT == kQ6_K) ? 8 : 4;
+    for (int ci = 0; ci < CPL; ++ci) {
+      const int c = j + lpr * ci;
+      const uint32_t off = c < nchunks ? 4u * (uint32_t)(xrow[t] * K + W * c) : kOutside;
 #pragma unroll
-  for (int i = 0; i < D; ++i) xs.h[i] = xs.l[i] = 0u;
-  xs.s = 0.f;
-  if constexpr (FMT == kQ2_K) {
+      for (int i = 0; i < W / 4; ++i)
+        v[t][ci][i] = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16u * i, 0,
+                                                            XCOH ? kCpolSc1 : 0);
+    }
 #pragma unroll
-    for (int k = 0; k < 4; ++k) xs.sum[k] = 0.f;
-  } else if constexpr (FMT == kQ3_K) {
+  for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int k = 0; k < 4; ++k) xs.nsum4[k] = 0;
-  } else if constexpr (FMT == kQ6_K) {
-    xs.nsum32[0] = xs.nsum32[1] = 0;
-  } else {
-    xs.sum = 0.f;
-  }
+    for (int ci = 0; ci < CPL; ++ci) {
+      float f[W];
+#pragma unroll
+      for (int i = 0; i < W / 4; ++i) {
+        f[4 * i + 0] = v[t][ci][i].x;
+        f[4 * i + 1] = v[t][ci][i].y;
+        f[4 * i + 2] = v[t][ci][i].z;
+        f[4 * i + 3] = v[t][ci][i].w;
+      }
+      quantize_slice<FMT, W>(xs[t][ci], f);
+    }
 }
 
 // acc += a * dot - b * xs.sum for one chunk: the chunk's contribution,

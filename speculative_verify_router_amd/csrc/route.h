@@ -64,28 +64,30 @@ __device__ __forceinline__ void router_row_partials(const float* __restrict__ ro
   }
 }
 
-// Part 2, after a barrier: logit of token threadIdx.x < M (fixed order).
-__device__ __forceinline__ void router_row_finish(float* __restrict__ logits, int E, int M, int e,
-                                                  const RouterPart& s_part) {
+// Part 2 for the fused small-batch path: token threadIdx.x < M publishes
+// its logit as an order-preserving key (never 0) with a write-through store;
+// the routing workgroup of the same launch polls for it (topk_keys_poll).
+__device__ __forceinline__ void router_row_publish(uint32_t* __restrict__ keys, int E, int M,
+                                                   int e, const RouterPart& s_part) {
   if (threadIdx.x < M) {
     float acc = 0.f;
 #pragma unroll
     for (int w4 = 0; w4 < kWavesPerBlock; ++w4)
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc += s_part[w4][r][threadIdx.x];
-    store_shared(logits + (int64_t)threadIdx.x * E + e, acc);
+    store_shared(keys + (int64_t)threadIdx.x * E + e, order_key(acc));
   }
 }
 
 template <int NC>
-__device__ __forceinline__ void router_row_block(const float* __restrict__ router,
-                                                 const float* __restrict__ x,
-                                                 float* __restrict__ logits, int H, int E, int M,
-                                                 int e) {
+__device__ __forceinline__ void router_row_keys(const float* __restrict__ router,
+                                                const float* __restrict__ x,
+                                                uint32_t* __restrict__ keys, int H, int E, int M,
+                                                int e) {
   __shared__ RouterPart s_part;
   router_row_partials<NC>(router, x, H, M, e, s_part);
   __syncthreads();
-  router_row_finish(logits, E, M, e, s_part);
+  router_row_publish(keys, E, M, e, s_part);
 }
 
 // Router GEMV for any batch size (prefill): one wave per router row, tokens
@@ -134,19 +136,22 @@ static __global__ __launch_bounds__(kBlock) void k_router_logits(const float* __
 // w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0).
 // ---------------------------------------------------------------------------
 
-template <bool COHERENT, int NV>
-__device__ __forceinline__ void topk_token_nv(const float* __restrict__ row,
-                                              int32_t* __restrict__ ids, float* __restrict__ wts,
-                                              int E, int k) {
+// Selection of one token from its keys in registers: key[i] is the key of
+// expert lane + 64 i (0, below every real key, for lanes past E).  With
+// `poison` the weights are written as NaN (a routing wait gave up), so the
+// layer's outputs show it.
+struct TopkLane {
+  int e;    // lane j < k: the j-th selected expert
+  float w;  // its renormalised weight
+};
+
+template <int NV>
+__device__ __forceinline__ TopkLane topk_select(const uint32_t (&key)[NV], int E,
+                                                int32_t* __restrict__ ids,
+                                                float* __restrict__ wts, int k, bool coherent,
+                                                bool poison) {
   const int lane = threadIdx.x & (kWave - 1);
   const int nv = (E + kWave - 1) / kWave;
-  uint32_t key[NV];
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int e = lane + kWave * i;
-    key[i] = 0u;  // below every real key: never selected while k <= E
-    if (i < nv && e < E) key[i] = order_key(COHERENT ? load_shared(row + e) : row[e]);
-  }
   // Candidate: best untaken local key (bit i of `taken` marks key[i] taken).
   uint32_t taken = 0u;
   uint32_t ck = 0u;
@@ -190,15 +195,99 @@ __device__ __forceinline__ void topk_token_nv(const float* __restrict__ row,
   const float vmax = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_v), 0));
   const float ex = (lane < k) ? __expf(my_v - vmax) : 0.f;
   const float tot = wave_sum(ex);
-  if (lane < k) {
-    if (COHERENT) {  // read by other workgroups of the same launch
+  const float wj = poison ? __builtin_nanf("") : ex / tot;
+  if (lane < k && ids) {
+    if (coherent) {  // read by other workgroups of the same launch
       store_shared(ids + lane, (int32_t)my_e);
-      store_shared(wts + lane, ex / tot);
+      store_shared(wts + lane, wj);
     } else {
       ids[lane] = my_e;
-      wts[lane] = ex / tot;
+      wts[lane] = wj;
     }
   }
+  return TopkLane{my_e, wj};
+}
+
+template <bool COHERENT, int NV>
+__device__ __forceinline__ void topk_token_nv(const float* __restrict__ row,
+                                              int32_t* __restrict__ ids, float* __restrict__ wts,
+                                              int E, int k) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int nv = (E + kWave - 1) / kWave;
+  uint32_t key[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int e = lane + kWave * i;
+    key[i] = 0u;  // below every real key: never selected while k <= E
+    if (i < nv && e < E) key[i] = order_key(COHERENT ? load_shared(row + e) : row[e]);
+  }
+  (void)topk_select<NV>(key, E, ids, wts, k, COHERENT, false);
+}
+
+// Polls allowed for one token's keys (each a round trip past L2 and a short
+// sleep): far beyond any launch, only a bound so that no wave can wait
+// forever.
+constexpr int kKeyPollLimit = 1 << 20;
+
+// A wave reads one token's keys, published by other workgroups of this
+// launch with write-through stores, past L2 until none is 0 (a bounded
+// number of polls).  Returns false, and sets *err, if it gave up.
+template <int NV>
+__device__ __forceinline__ bool poll_keys(const uint32_t* __restrict__ row, int E,
+                                          uint32_t (&key)[NV], unsigned* err) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int nv = (E + kWave - 1) / kWave;
+  bool missing = true;
+  for (int n = 0; n < kKeyPollLimit; ++n) {
+    missing = false;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = lane + kWave * i;
+      key[i] = 0u;
+      if (i < nv && e < E) {
+        key[i] = load_shared(row + e);
+        missing |= key[i] == 0u;
+      }
+    }
+    if (__ballot(missing) == 0) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  const bool gave_up = __ballot(missing) != 0;
+  if (gave_up && lane == 0) store_shared(err, 1u);
+  return !gave_up;
+}
+
+// Top-k of one token whose keys other workgroups of this launch publish
+// with write-through stores (router_row_publish): poll, select, and clear
+// the row for the next call.  If the poll gave up the token's weights are
+// poisoned (NaN).
+template <int NV>
+__device__ __forceinline__ TopkLane topk_keys_poll_nv(uint32_t* __restrict__ row,
+                                                      int32_t* __restrict__ ids,
+                                                      float* __restrict__ wts, int E, int k,
+                                                      unsigned* err) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int nv = (E + kWave - 1) / kWave;
+  uint32_t key[NV];
+  const bool ok = poll_keys<NV>(row, E, key, err);
+  const TopkLane res = topk_select<NV>(key, E, ids, wts, k, true, !ok);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int e = lane + kWave * i;
+    if (i < nv && e < E) store_shared(row + e, 0u);
+  }
+  return res;
+}
+
+// Lane j < k of the result holds the token's j-th expert and weight.
+__device__ __forceinline__ TopkLane topk_keys_poll(uint32_t* __restrict__ row,
+                                                   int32_t* __restrict__ ids,
+                                                   float* __restrict__ wts, int E, int k,
+                                                   unsigned* err) {
+  if (E <= 5 * kWave) return topk_keys_poll_nv<5>(row, ids, wts, E, k, err);
+  if (E <= 6 * kWave) return topk_keys_poll_nv<6>(row, ids, wts, E, k, err);
+  if (E <= 8 * kWave) return topk_keys_poll_nv<8>(row, ids, wts, E, k, err);
+  return topk_keys_poll_nv<kMaxExperts / kWave>(row, ids, wts, E, k, err);
 }
 
 // NV keys per lane, the fewest that hold E: 5 for up to 320 experts (the

@@ -47,6 +47,8 @@ def test_stage_lists_follow_the_launch_path():
     d = svr.LayerDesc(4096, 288, 8, 1280, 1280, "q4_k", "q8_0")
     for M in (1, 2, 3, 4, 5, 16):
         assert _stage_names(d, M) == ["route_shared_gateup", "gateup", "down_combine"]
+        assert _stage_names(svr.LayerDesc(4096, 288, 8, 1280, 0, "q4_k", "q8_0"), M) == [
+            "route_shared_gateup", "gateup", "down_combine"]
     # Batches above 16 tokens: the grouped-GEMM path.
     for M in (17, 512):
         assert _stage_names(d, M) == ["route", "shared_gateup", "gateup", "shared_down",
@@ -150,7 +152,9 @@ def test_routed_down_type_selects_the_path():
     assert L.moe_stage_count(ctypes.byref(_desc(expert_type="q6_k").c()), 16) == 3
     assert L.moe_stage_count(ctypes.byref(_desc(down_type="q4_k").c()), 512) == 5
     assert L.moe_stage_count(ctypes.byref(_desc(down_type="q8_0").c()), 512) == 5
+    # verify batches: the staged path, gate/up and down types apart
     assert L.moe_stage_count(ctypes.byref(_desc(down_type="q8_0").c()), 4) == 3
+    assert L.moe_stage_count(ctypes.byref(mixed.c()), 4) == 3
     out = ctypes.c_size_t()
     bad = _desc().c()
     bad.down_type = 9

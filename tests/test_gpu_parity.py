@@ -250,3 +250,28 @@ def test_prepared_forward_matches_plain_call():
         torch.cuda.synchronize()
         assert np.array_equal(y.cpu().numpy(), y0)
         assert np.array_equal(ids.cpu().numpy(), ids0)
+
+
+@pytest.mark.parametrize("M", [1, 4, 9, 16])
+def test_handoff_areas_return_to_zero(M):
+    # The counters and the routing keys at the start of the workspace must
+    # be zero before a call and are zero after it, whatever the batch size
+    # (their offsets depend on the layer only); one workspace serves calls of
+    # different sizes in turn.  The routing wait's diagnostic word stays 0.
+    cfg = small_config(hidden=512, n_experts=40, top_k=4, ffn=256, shared_ffn=128,
+                       expert_type="q4_k", n_tokens=16, router_std=0.2, seed_index=560)
+    inp = synth.draw_layer(cfg)
+    x, _ = conditioned_tokens(inp)
+    w = upload(inp)
+    desc = desc_of(cfg)
+    ws = svr.workspace(desc, 16, "cuda")
+    handoff = 16384 + (cfg.n_experts * 64 + 255) // 256 * 256
+    for m in (M, 16, M):
+        y = torch.empty((m, 512), dtype=torch.float32, device="cuda")
+        ids = torch.empty((m, 4), dtype=torch.int32, device="cuda")
+        svr.moe_layer_forward(desc, w, dev(x[:m]), y, ids, None, ws=ws)
+        torch.cuda.synchronize()
+        assert int(ws[:handoff].count_nonzero().item()) == 0
+        ref = run_oracle(inp, x[:m])
+        assert np.array_equal(ids.cpu().numpy(), ref["ids"])
+        check_y(y.cpu().numpy(), ref["y"], f"M={m}")
