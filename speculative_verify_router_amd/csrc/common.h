@@ -13,6 +13,9 @@ constexpr int kBlock = 256;        // threads per workgroup (4 waves)
 constexpr int kWavesPerBlock = kBlock / kWave;
 constexpr int kMaxExperts = 1024;  // experts per layer
 constexpr int kMaxTopK = 64;       // selected experts per token
+// Batches up to this size give every (token, slot) pair its own workgroups
+// (equal work per workgroup) instead of grouping them by expert.
+constexpr int kPairTokens = 4;
 constexpr int kMaxChunksPerLane = 8;
 // Hand-off counters at the start of the workspace (zero between calls).
 constexpr int kCounterBytes = 16384;

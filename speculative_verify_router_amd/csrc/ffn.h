@@ -52,6 +52,10 @@ struct FfnArgs {
   int coherent_out;         // 1: outputs are read by other workgroups of this launch
   const int32_t* pair_expert;  // pair slots: slot p is pair p, expert pair_expert[p]
   int n_pairs;                 // number of pair slots (pair_expert != NULL)
+  // Pair slots, gate/up: NULL, or each pair's {expert, token word}
+  // (pair_infos_wave): the pairs of an expert share its rows and each
+  // serves all of the expert's tokens.
+  const uint2* pair_info;
   int max_rows;     // host side: cap on units_per_block (0: none)
 };
 
@@ -244,8 +248,17 @@ __device__ __forceinline__ void ffn_pass_nt(const FfnArgs& a, int expert, const 
 }
 
 // Pair slots: rows [tile * units_per_block, ...) of the expert of (token,
-// slot) pair `slot`, the four waves taking different rows.
-template <int FMT, int CPL, bool GATEUP, int NSTD = 0, bool LDSOUT = false, int LPR = 0>
+// slot) pair `slot`, the four waves taking different rows.  With token
+// words (gate/up), the n pairs of an expert selected by n tokens split the
+// tile's row steps n ways (the pair of the expert's r-th token takes steps
+// r, r + n, ...) and each runs one pass for all n tokens: the expert's rows
+// are streamed once, and every workgroup has the arithmetic of a one-token
+// tile.  Each output is computed as in a pass of its own token.  Passes of
+// three or four tokens keep a two-stage ring to stay within the registers.
+// SHARE: read the pairs' {expert, word} (else every pair runs its own
+// pass, which gives the same outputs).
+template <int FMT, int CPL, bool GATEUP, int NSTD = 0, bool LDSOUT = false, int LPR = 0,
+          bool SHARE = false>
 __device__ __forceinline__ void ffn_tile_pair(const FfnArgs& a, int slot, int tile,
                                               float* lds = nullptr) {
   if (slot >= a.n_pairs) return;
@@ -253,10 +266,45 @@ __device__ __forceinline__ void ffn_tile_pair(const FfnArgs& a, int slot, int ti
   const int ue = min(ub + a.units_per_block, a.rows_per_expert);
   if (ub >= ue) return;
   const int G = kWave / (LPR ? LPR : a.lpr);
+  const int first = ub + (int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * G;
+  const int step = kWavesPerBlock * G;
+  int e;
+  if constexpr (GATEUP && !LDSOUT && SHARE) {
+    if (a.pair_info) {
+      const uint2 info = a.pair_info[slot];  // one load: expert and word
+      e = __builtin_amdgcn_readfirstlane((int)info.x);
+      const uint32_t word = __builtin_amdgcn_readfirstlane(info.y);
+      const int t = slot / a.top_k;
+      int ids[kPairTokens];
+      int n = 0, r = 0;
+#pragma unroll
+      for (int u = 0; u < kPairTokens; ++u) {
+        const int b = (int)((word >> (8 * u)) & 255u);
+        if (b) {
+          if (u < t) ++r;
+          ids[n++] = u * a.top_k + b - 1;
+        }
+      }
+      if (n > 1) {
+        const int f = ub + (r * kWavesPerBlock + (int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * G;
+        const int s = n * step;
+        if (n == 2)
+          ffn_pass<FMT, CPL, 2, true, NSTD, false, LPR>(a, e, ids, f, s, ue);
+        else if (n == 3)
+          ffn_pass<FMT, CPL, 3, true, 2, false, LPR>(a, e, ids, f, s, ue);
+        else
+          ffn_pass<FMT, CPL, 4, true, 2, false, LPR>(a, e, ids, f, s, ue);
+        return;
+      }
+      // n == 1: this pair's own token, the pass below
+    } else {
+      e = __builtin_amdgcn_readfirstlane(a.pair_expert[slot]);
+    }
+  } else {
+    e = __builtin_amdgcn_readfirstlane(a.pair_expert[slot]);
+  }
   const int ids1[1] = {slot}, slot0[1] = {0};
-  const int e = a.pair_expert[slot];
-  ffn_pass<FMT, CPL, 1, GATEUP, NSTD, LDSOUT, LPR>(a, e, ids1, ub + (threadIdx.x >> 6) * G,
-                                                   kWavesPerBlock * G, ue,
+  ffn_pass<FMT, CPL, 1, GATEUP, NSTD, LDSOUT, LPR>(a, e, ids1, first, step, ue,
                                                    LdsOut{lds, ub, a.units_per_block}, slot0);
 }
 
@@ -288,14 +336,15 @@ __device__ __forceinline__ void ffn_tile_tokens(const FfnArgs& a, int tile) {
 }
 
 // Work of workgroup (tile, slot): rows [tile * units_per_block, ...) of the
-// expert in `slot`, for every token routed to it.
-template <int FMT, int CPL, bool GATEUP, int LPR = 0>
+// expert in `slot`, for every token routed to it.  SHARE: pair slots follow
+// the token words (ffn_tile_pair).
+template <int FMT, int CPL, bool GATEUP, int LPR = 0, bool SHARE = false>
 __device__ __forceinline__ void ffn_tile(const FfnArgs& a, int slot, int tile) {
   constexpr int TP = tp_for(FMT, CPL);
   const int ub = tile * a.units_per_block;
   if (a.pair_expert) {
     // One (token, slot) pair per slot: every workgroup does the same work.
-    ffn_tile_pair<FMT, CPL, GATEUP, 0, false, LPR>(a, slot, tile);
+    ffn_tile_pair<FMT, CPL, GATEUP, 0, false, LPR, SHARE>(a, slot, tile);
     return;
   }
   if (a.n_active && slot >= *a.n_active) return;

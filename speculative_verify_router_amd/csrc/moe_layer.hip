@@ -39,16 +39,13 @@ namespace {
 
 constexpr int kVersion = 400;  // 0.4.0
 constexpr int kFusedMaxTokens = 16;
-// Batches up to this size give every (token, slot) pair its own workgroups
-// (equal work per workgroup); larger ones go by expert with token passes.
-constexpr int kPairSlotTokens = 4;
 
 enum Stage { kStPhase1 = 0, kStPhase2, kStPhase3, kNumStages };
 const char* const kStageNames[kNumStages] = {"route_shared_gateup", "gateup", "down_combine"};
 
 struct Plan {
   int H, E, k, F, Fs, et, st, dt, M, flags;  // dt: routed down type
-  size_t ctr, keys, logits, ids, w, counts, offsets, slots, active, nactive, h, hs, o, s, xs,
+  size_t ctr, keys, logits, ids, w, ptok, counts, offsets, slots, active, nactive, h, hs, o, s, xs,
       tiles, total;
   int tiles_cap;  // routed token tiles of the batched path, at most
 };
@@ -102,6 +99,7 @@ int make_plan(const moe_layer_desc* d, int M, Plan* p) {
   p->logits = take(Mz * p->E * 4);
   p->ids = take(P * 4);
   p->w = take(P * 4);
+  p->ptok = take(P * 8);
   p->counts = take((size_t)p->E * 4);
   p->offsets = take((size_t)(p->E + 1) * 4);
   p->slots = take(P * 4);
@@ -175,6 +173,7 @@ inline void mark(hipEvent_t* ev, int i, hipStream_t st) {
 struct Buffers {
   Counters* ctr;
   uint32_t* keys;
+  uint2* ptok;
   float *logits, *w, *h, *hs, *o, *s;
   int32_t *ids, *counts, *offsets, *slots, *active, *nactive, *tiles, *ntiles;
   uint4* xs;
@@ -188,6 +187,7 @@ Buffers carve(const Plan& p, void* ws, int32_t* ids, float* w) {
   r.logits = (float*)(b + p.logits);
   r.ids = ids ? ids : (int32_t*)(b + p.ids);
   r.w = w ? w : (float*)(b + p.w);
+  r.ptok = (uint2*)(b + p.ptok);
   r.counts = (int32_t*)(b + p.counts);
   r.offsets = (int32_t*)(b + p.offsets);
   r.slots = (int32_t*)(b + p.slots);
@@ -266,6 +266,8 @@ FfnArgs routed_args(const Plan& p, const Buffers& b, bool gateup, const moe_laye
   if (pairs) {
     a.pair_expert = b.ids;
     a.n_pairs = p.M * p.k;
+    // gate/up: one pass per expert over all of its tokens
+    if (gateup) a.pair_info = b.ptok;
   } else {
     a.active = b.active;
     a.n_active = b.nactive;
@@ -470,7 +472,7 @@ int forward_impl(const moe_layer_desc* desc, const moe_layer_weights* wt, const 
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
   }
   const BucketOut bo{b.counts, b.offsets, b.slots, b.active, b.nactive};
-  const bool pairs = p.M <= kPairSlotTokens;
+  const bool pairs = p.M <= kPairTokens;
   const int slots_max = pairs ? p.M * p.k : ((p.M * p.k < p.E) ? p.M * p.k : p.E);
   const bool shared = p.Fs > 0;
   (void)hipGetLastError();  // clear a stale error from earlier, unrelated calls
@@ -485,7 +487,8 @@ int forward_impl(const moe_layer_desc* desc, const moe_layer_weights* wt, const 
   }
   bool fused1 = false;
   if (p.M <= kFusedMaxTokens) {
-    RouteArgs r{wt->router, x, b.keys, b.ids, b.w, bo, p.H, p.E, p.k, p.M, p.E, b.ctr, !pairs};
+    RouteArgs r{wt->router, x, b.keys, pairs ? b.ptok : nullptr, b.ids, b.w, bo, p.H, p.E, p.k,
+                p.M, p.E, b.ctr, !pairs};
     fused1 = launch_phase1(p.H, shared, p.st, ss, st, r, sgu);
     if (!fused1 && shared) {
       // No fused instantiation for this shared shape: route alone, then the
@@ -496,6 +499,8 @@ int forward_impl(const moe_layer_desc* desc, const moe_layer_weights* wt, const 
   }
   if (!fused1) {
     enqueue_route_plain(p, wt->router, x, b, bo, st);
+    if (pairs)
+      hipLaunchKernelGGL(k_pair_infos, dim3(1), dim3(kWave), 0, st, b.ids, b.ptok, p.M, p.k);
     if (shared && !launch_ffn(p.st, true, sgu, 1, st)) return MOE_ERR_SHAPE;
   }
 

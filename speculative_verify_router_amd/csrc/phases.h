@@ -38,6 +38,7 @@ struct RouteArgs {
   const float* router;
   const float* x;
   uint32_t* keys;  // [M][E] routing keys, zero between calls
+  uint2* pair_info;  // non-NULL (pair slots): each pair's {expert, token word}
   int32_t* ids;
   float* w;
   BucketOut b;
@@ -55,13 +56,22 @@ __device__ __forceinline__ void router_part(const RouteArgs& r, int blk) {
 
 // The routing workgroup (dispatched after every router workgroup it waits
 // for): wave w takes tokens w, w + 4, ..., polls each token's keys,
-// selects its experts and clears the keys; then, if asked, the per-expert
-// lists.
+// selects its experts and clears the keys; then, if asked, each pair's
+// expert and token word (pair slots) or the per-expert lists.
 __device__ __forceinline__ void route_part(const RouteArgs& r) {
-  const int wv = threadIdx.x >> 6;
-  for (int t = wv; t < r.M; t += kWavesPerBlock)
-    topk_keys_poll(r.keys + (int64_t)t * r.E, r.ids + (int64_t)t * r.k, r.w + (int64_t)t * r.k,
-                   r.E, r.k, &r.ctr->route_wait_err);
+  __shared__ int32_t s_ids[kPairTokens * kMaxTopK];
+  __shared__ uint32_t s_table[kMaxExperts];
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
+  for (int t = wv; t < r.M; t += kWavesPerBlock) {
+    const TopkLane tl =
+        topk_keys_poll(r.keys + (int64_t)t * r.E, r.ids + (int64_t)t * r.k,
+                       r.w + (int64_t)t * r.k, r.E, r.k, &r.ctr->route_wait_err);
+    if (r.pair_info && lane < r.k) s_ids[t * r.k + lane] = tl.e;
+  }
+  if (r.pair_info) {  // M <= kPairTokens
+    __syncthreads();
+    if (wv == 0) pair_infos_wave(s_ids, r.M, r.k, s_table, r.pair_info);
+  }
   if (r.bucket) {
     __syncthreads();
     bucket_block(r.ids, r.M * r.k, r.E, r.b);
@@ -83,12 +93,13 @@ __global__ __launch_bounds__(kBlock) void k_phase1(RouteArgs r, FfnArgs s) {
 
 // Two FFN roles in one grid: blocks [0, na) take tiles of role A (grid of
 // a_tiles x slots, tile fastest), the rest tiles of role B (one slot).
-// SA, SB: shape codes.
+// SA, SB: shape codes.  A gate/up role A with pair slots serves each
+// expert's tokens in one pass (token words).
 template <int FA, int SA, bool GA, int FB, int SB, bool GB>
 __global__ __launch_bounds__(kBlock) void k_dual(FfnArgs a, int a_tiles, int na, FfnArgs b) {
   const int blk = blockIdx.x;
   if (blk < na) {
-    ffn_tile<FA, shape_cpl(SA), GA, shape_lpr(SA)>(a, blk / a_tiles, blk % a_tiles);
+    ffn_tile<FA, shape_cpl(SA), GA, shape_lpr(SA), GA>(a, blk / a_tiles, blk % a_tiles);
   } else {
     ffn_tile<FB, shape_cpl(SB), GB, shape_lpr(SB)>(b, 0, blk - na);
   }

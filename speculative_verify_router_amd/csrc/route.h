@@ -314,6 +314,41 @@ static __global__ __launch_bounds__(kBlock) void k_topk(const float* __restrict_
 }
 
 // ---------------------------------------------------------------------------
+// Shared experts of a verify batch (up to kPairTokens tokens, pair slots).
+// Pair p = t*k + j gets {expert, word}, where byte u of the word is 1 + the
+// slot of token u's pair on the same expert (0: token u does not select
+// it): every pair of an expert gets the same word, and the expert's gate/up
+// pass serves all of its tokens at once, its rows split between those
+// pairs' workgroups.  One wave (every lane calls it) builds
+// the words in an LDS table of one word per expert (`table`, E words): each
+// pair clears its expert's word, ORs in its own byte (a token selects an
+// expert at most once, so no bytes collide), and reads the word back.  The
+// LDS operations of one wave complete in order, so no barrier is needed
+// between the steps.  ids: the M*k selected experts (global or LDS).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void pair_infos_wave(const int32_t* ids, int M, int k,
+                                                uint32_t* table, uint2* __restrict__ out) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int P = M * k;
+  // (an expert id outside [0, kMaxExperts) would only come from a routing
+  // that gave up; it still indexes inside the table)
+  auto slot_of = [&](int p) { return (uint32_t)ids[p] & (uint32_t)(kMaxExperts - 1); };
+  for (int p = lane; p < P; p += kWave) table[slot_of(p)] = 0u;
+  for (int p = lane; p < P; p += kWave) {
+    const int t = p / k;
+    atomicOr(&table[slot_of(p)], (uint32_t)(p - t * k + 1) << (8 * t));
+  }
+  for (int p = lane; p < P; p += kWave) out[p] = make_uint2((uint32_t)ids[p], table[slot_of(p)]);
+}
+
+static __global__ __launch_bounds__(kWave) void k_pair_infos(const int32_t* __restrict__ ids,
+                                                             uint2* __restrict__ out, int M,
+                                                             int k) {
+  __shared__ uint32_t table[kMaxExperts];
+  pair_infos_wave(ids, M, k, table, out);
+}
+
+// ---------------------------------------------------------------------------
 // Bucketing by one workgroup: counts[E], offsets[E+1] (exclusive scan),
 // active[] (experts with pairs, ascending, then -1), n_active, and slots[]:
 // the pair indices p = t*k + j of each expert in ascending p (so ascending

@@ -201,6 +201,27 @@ def test_rows_equal_single_token_calls_bitwise():
         assert np.array_equal(y1[0].view(np.uint32), y[t].view(np.uint32)), t
 
 
+@pytest.mark.parametrize("etype", ["q4_k", "q8_0", "q2_k"])
+@pytest.mark.parametrize("rows", [(0, 0, 0, 0), (0, 1, 0, 1), (0, 1, 1, 1), (0, 1, 2, 3)])
+def test_experts_shared_by_several_tokens(etype, rows):
+    # Verify batches whose tokens select the same experts (all four tokens,
+    # two pairs, three and one, partial overlaps): the gate/up pass of an
+    # expert serves all of its tokens at once.  Matches the oracle, and each
+    # row equals that token's single-token call bit for bit.
+    cfg = small_config(hidden=512, n_experts=16, top_k=4, ffn=256, shared_ffn=128,
+                       expert_type=etype, n_tokens=4, router_std=0.2, seed_index=570)
+    inp = synth.draw_layer(cfg)
+    x4, _ = conditioned_tokens(inp)
+    x = np.ascontiguousarray(x4[list(rows)])
+    inp, x, y, ref = _layer_case(cfg, x=x, inp=inp)
+    ids = np.asarray(ref["ids"])
+    assert len(np.unique(ids)) < ids.size  # some expert serves several tokens
+    w = upload(inp)
+    for t in range(4):
+        y1, _, _ = gpu_forward(cfg, w, x[t:t + 1])
+        assert np.array_equal(y1[0].view(np.uint32), y[t].view(np.uint32)), t
+
+
 def test_zero_tokens_is_a_no_op():
     cfg = small_config()
     inp = synth.draw_layer(cfg)
