@@ -80,3 +80,52 @@ def test_verify_batches_of_one_to_four_tokens_agree_bitwise(name):
             assert np.array_equal(y.view(np.uint32), y4[t0:t0 + M].view(np.uint32))
     del w, inp
     gc.collect()
+
+
+@pytest.mark.timeout(600)
+def test_soak_verify_calls_repeat_bit_for_bit():
+    # Repeated calls on one workspace: 2000 calls of the Step-3.5 verify
+    # layer, rotating four layer instances, each output (routing ids and
+    # weights, y) equal bit for bit to that instance's first output.  The
+    # calls exercise the in-launch hand-offs (router keys polled by the
+    # routing workgroup and cleared for the next call, the per-pair token
+    # words) under back-to-back reuse of the same hand-off areas.
+    import torch
+    import speculative_verify_router_amd as svr
+    from gpu_common import desc_of
+
+    cfg = synth.CONFIGS["step35_verify_m4"]
+    M, H, k = cfg.n_tokens, cfg.hidden, cfg.top_k
+    insts = []
+    for i in range(4):
+        log(f"[soak] drawing instance {i}")
+        inp = synth.draw_layer(cfg, instance=i)
+        x, _ = conditioned_tokens(inp, instance=i)
+        insts.append((upload(inp), dev(x)))
+        del inp
+        gc.collect()
+    desc = desc_of(cfg)
+    ws = svr.workspace(desc, M, "cuda")
+    y = torch.empty((M, H), dtype=torch.float32, device="cuda")
+    ids = torch.empty((M, k), dtype=torch.int32, device="cuda")
+    tw = torch.empty((M, k), dtype=torch.float32, device="cuda")
+    first = []
+    for w, x in insts:
+        svr.moe_layer_forward(desc, w, x, y, ids, tw, ws=ws)
+        first.append((y.clone(), ids.clone(), tw.clone()))
+    torch.cuda.synchronize()
+    n_calls, check_every = 2000, 50
+    bad = torch.zeros((), dtype=torch.int64, device="cuda")
+    for n in range(n_calls):
+        i = n % 4
+        w, x = insts[i]
+        svr.moe_layer_forward(desc, w, x, y, ids, tw, ws=ws)
+        y0, ids0, tw0 = first[i]
+        bad += (y.view(torch.int32) != y0.view(torch.int32)).sum()
+        bad += (ids != ids0).sum() + (tw.view(torch.int32) != tw0.view(torch.int32)).sum()
+        if (n + 1) % check_every == 0:
+            torch.cuda.synchronize()
+            assert int(bad.item()) == 0, f"mismatch by call {n}"
+            if (n + 1) % 500 == 0:
+                log(f"[soak] {n + 1} calls equal")
+    assert int(ws[:4].view(torch.int32).item()) == 0  # no routing wait gave up
