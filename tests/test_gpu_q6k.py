@@ -4,8 +4,8 @@ Q6_K is the recipes' type for the MTP heads' matrices ("Step-5 Preview
 GGUF", Tensor-type table); here it is a routed-expert type like the other
 K-quants.  Block decoding must be bit-exact; layers must match the oracle's
 ids exactly, routing weights within 1e-6 and outputs within 2e-3 x RMS on
-pair slots (1 to 4 tokens), expert lists (5 to 16) and the staged path
-beyond 16 tokens (no matrix-core decoder for this type).
+pair slots (1 to 4 tokens), expert lists (5 to 16) and the matrix-core
+grouped GEMMs beyond 16 tokens.
 """
 
 import numpy as np
