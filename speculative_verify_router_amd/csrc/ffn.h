@@ -253,8 +253,7 @@ __device__ __forceinline__ void ffn_pass_nt(const FfnArgs& a, int expert, const 
 // tile's row steps n ways (the pair of the expert's r-th token takes steps
 // r, r + n, ...) and each runs one pass for all n tokens: the expert's rows
 // are streamed once, and every workgroup has the arithmetic of a one-token
-// tile.  Each output is computed as in a pass of its own token.  Passes of
-// three or four tokens keep a two-stage ring to stay within the registers.
+// tile.  Each output is computed as in a pass of its own token.
 // SHARE: read the pairs' {expert, word} (else every pair runs its own
 // pass, which gives the same outputs).
 template <int FMT, int CPL, bool GATEUP, int NSTD = 0, bool LDSOUT = false, int LPR = 0,
@@ -288,12 +287,16 @@ __device__ __forceinline__ void ffn_tile_pair(const FfnArgs& a, int slot, int ti
       if (n > 1) {
         const int f = ub + (r * kWavesPerBlock + (int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * G;
         const int s = n * step;
-        if (n == 2)
-          ffn_pass<FMT, CPL, 2, true, NSTD, false, LPR>(a, e, ids, f, s, ue);
-        else if (n == 3)
-          ffn_pass<FMT, CPL, 3, true, 2, false, LPR>(a, e, ids, f, s, ue);
-        else
-          ffn_pass<FMT, CPL, 4, true, 2, false, LPR>(a, e, ids, f, s, ue);
+        // Passes of at most two tokens: a three- or four-token pass needs
+        // more registers than the one-token pass (spilling into AGPRs and
+        // halving the whole grid's occupancy); a second pass finds the
+        // rows in L2.
+        ffn_pass<FMT, CPL, 2, true, NSTD, false, LPR>(a, e, ids, f, s, ue);
+        if (n == 3) {
+          ffn_pass<FMT, CPL, 1, true, NSTD, false, LPR>(a, e, ids + 2, f, s, ue);
+        } else if (n == 4) {
+          ffn_pass<FMT, CPL, 2, true, NSTD, false, LPR>(a, e, ids + 2, f, s, ue);
+        }
         return;
       }
       // n == 1: this pair's own token, the pass below
