@@ -687,19 +687,24 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, int e, int pos0, i
 }
 
 // Grid: row_blocks x (token-tile capacity rounded up to 8).  Blocks go to
-// the eight XCDs round-robin; block b takes token tile 8 (b / 8 / row_blocks)
-// + b % 8 and row block (b / 8) % row_blocks, so the row blocks of one token
-// tile share an XCD (and its L2 copy of the tile's activations) and the
-// tiles spread over all XCDs.  Every wave of a workgroup passes the same
+// the eight XCDs round-robin; XCD x takes the x-th eighth of the live tile
+// list, in order: block b takes its ((b / 8) / row_blocks)-th tile and row
+// block (b / 8) % row_blocks.  So the row blocks of one token tile share an
+// XCD (and its L2 copy of the tile's activations), and the tiles of an
+// expert with more than 16 tokens run back to back on one XCD and find its
+// weight rows in that L2.  Every wave of a workgroup passes the same
 // slab barriers; waves whose rows lie past the expert compute zeros.
 template <int FMT, bool GATEUP, int RTR>
 __global__ __launch_bounds__(kBlock) void k_gemm(GemmArgs a) {
   __shared__ GemmLds<FMT, GATEUP, RTR> lds;
   const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
-  const int tile = (j / a.row_blocks) * 8 + xcd, rb = j % a.row_blocks;
+  const int n_tiles = a.tiles ? *a.n_tiles : (a.dense_tokens + 15) / 16;
+  const int per_xcd = (n_tiles + 7) / 8;
+  const int slot = j / a.row_blocks, rb = j % a.row_blocks;
+  const int tile = xcd * per_xcd + slot;
+  if (slot >= per_xcd || tile >= n_tiles) return;
   int e, pos0, cnt;
   if (a.tiles) {
-    if (tile >= *a.n_tiles) return;
     e = a.tiles[3 * tile];
     pos0 = a.tiles[3 * tile + 1];
     cnt = a.tiles[3 * tile + 2];
