@@ -222,6 +222,20 @@ def test_experts_shared_by_several_tokens(etype, rows):
         assert np.array_equal(y1[0].view(np.uint32), y[t].view(np.uint32)), t
 
 
+@pytest.mark.parametrize("E,k", [(128, 64), (64, 64), (100, 17)])
+def test_shared_experts_with_many_slots(E, k):
+    # Four tokens with up to 64 slots each (256 pairs: several pairs per lane
+    # when the routing builds the pairs' token words) on few experts, so most
+    # experts serve two to four tokens.
+    cfg = small_config(hidden=512, n_experts=E, top_k=k, ffn=256, shared_ffn=128,
+                       expert_type="q4_k", n_tokens=4, router_std=0.2, seed_index=580 + k)
+    inp, x, y, ref = _layer_case(cfg)
+    w = upload(inp)
+    for t in range(4):
+        y1, _, _ = gpu_forward(cfg, w, x[t:t + 1])
+        assert np.array_equal(y1[0].view(np.uint32), y[t].view(np.uint32)), t
+
+
 def test_zero_tokens_is_a_no_op():
     cfg = small_config()
     inp = synth.draw_layer(cfg)
