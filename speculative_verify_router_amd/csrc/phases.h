@@ -4,13 +4,18 @@
 //            of the grid waits for the router rows' keys, runs top-k for
 //            every token and the bucketing, so routing costs no launch of
 //            its own.
-//   phase 2: routed gate/up tiles + shared-expert down tiles.
-//   phase 3: routed down tiles; the last workgroup to finish a row tile
-//            (over all active experts) combines that tile of the output.
+//   phase 2: routed gate/up tiles + shared-expert down tiles (up to four
+//            tokens: per-pair tiles, the pairs of an expert that several
+//            tokens select sharing its rows).
+//   phase 3: routed down + combine: up to four tokens, one workgroup per
+//            (token, row tile) that adds its slots in LDS (k_down_tok);
+//            above, the last workgroup to finish a row tile (over all
+//            active experts) combines that tile of the output
+//            (k_down_combine).
 //
-// Hand-off counters live at the start of the workspace.  Each is returned
-// to zero by the workgroup that consumes it, so a workspace that starts
-// zero-filled stays valid from call to call.
+// The routing keys and the hand-off counters live at the start of the
+// workspace.  Each is returned to zero by the workgroup that consumes it,
+// so a workspace that starts zero-filled stays valid from call to call.
 #pragma once
 
 #include "ffn.h"

@@ -236,6 +236,21 @@ def test_shared_experts_with_many_slots(E, k):
         assert np.array_equal(y1[0].view(np.uint32), y[t].view(np.uint32)), t
 
 
+def test_wide_hidden_takes_the_unfused_routing():
+    # H = 9216 is past the fused phase-1 router (H <= 8192): the routing runs
+    # as separate launches, and for four tokens the pairs' token words come
+    # from their own one-wave launch.  Eight experts, two per token: tokens
+    # share experts.
+    cfg = small_config(hidden=9216, n_experts=8, top_k=2, ffn=256, shared_ffn=256,
+                       expert_type="q4_k", shared_type="q4_k", n_tokens=4, router_std=0.05,
+                       seed_index=590)
+    inp, x, y, ref = _layer_case(cfg)
+    w = upload(inp)
+    for t in range(4):
+        y1, _, _ = gpu_forward(cfg, w, x[t:t + 1])
+        assert np.array_equal(y1[0].view(np.uint32), y[t].view(np.uint32)), t
+
+
 def test_zero_tokens_is_a_no_op():
     cfg = small_config()
     inp = synth.draw_layer(cfg)
