@@ -266,8 +266,9 @@ FfnArgs routed_args(const Plan& p, const Buffers& b, bool gateup, const moe_laye
   if (pairs) {
     a.pair_expert = b.ids;
     a.n_pairs = p.M * p.k;
-    // gate/up: one pass per expert over all of its tokens
-    if (gateup) a.pair_info = b.ptok;
+    // gate/up of two or more tokens: one pass per expert over all of its
+    // tokens
+    if (gateup && p.M > 1) a.pair_info = b.ptok;
   } else {
     a.active = b.active;
     a.n_active = b.nactive;
@@ -473,6 +474,9 @@ int forward_impl(const moe_layer_desc* desc, const moe_layer_weights* wt, const 
   }
   const BucketOut bo{b.counts, b.offsets, b.slots, b.active, b.nactive};
   const bool pairs = p.M <= kPairTokens;
+  // Pairs of several tokens may share experts: the routing gives each pair
+  // its expert and token word (one token shares nothing).
+  const bool share = pairs && p.M > 1;
   const int slots_max = pairs ? p.M * p.k : ((p.M * p.k < p.E) ? p.M * p.k : p.E);
   const bool shared = p.Fs > 0;
   (void)hipGetLastError();  // clear a stale error from earlier, unrelated calls
@@ -487,7 +491,7 @@ int forward_impl(const moe_layer_desc* desc, const moe_layer_weights* wt, const 
   }
   bool fused1 = false;
   if (p.M <= kFusedMaxTokens) {
-    RouteArgs r{wt->router, x, b.keys, pairs ? b.ptok : nullptr, b.ids, b.w, bo, p.H, p.E, p.k,
+    RouteArgs r{wt->router, x, b.keys, share ? b.ptok : nullptr, b.ids, b.w, bo, p.H, p.E, p.k,
                 p.M, p.E, b.ctr, !pairs};
     fused1 = launch_phase1(p.H, shared, p.st, ss, st, r, sgu);
     if (!fused1 && shared) {
@@ -499,7 +503,7 @@ int forward_impl(const moe_layer_desc* desc, const moe_layer_weights* wt, const 
   }
   if (!fused1) {
     enqueue_route_plain(p, wt->router, x, b, bo, st);
-    if (pairs)
+    if (share)
       hipLaunchKernelGGL(k_pair_infos, dim3(1), dim3(kWave), 0, st, b.ids, b.ptok, p.M, p.k);
     if (shared && !launch_ffn(p.st, true, sgu, 1, st)) return MOE_ERR_SHAPE;
   }
