@@ -251,6 +251,16 @@ def test_wide_hidden_takes_the_unfused_routing():
         assert np.array_equal(y1[0].view(np.uint32), y[t].view(np.uint32)), t
 
 
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_largest_routing_shape(M):
+    # The layer at the routing limits: 1024 experts, 64 selected per token
+    # (256 pairs at four tokens; 1024 (token, slot) pairs over the expert
+    # lists at sixteen), with a shared expert.
+    cfg = small_config(hidden=512, n_experts=1024, top_k=64, ffn=256, shared_ffn=128,
+                       expert_type="q4_k", n_tokens=M, router_std=0.2, seed_index=600 + M)
+    _layer_case(cfg)
+
+
 def test_zero_tokens_is_a_no_op():
     cfg = small_config()
     inp = synth.draw_layer(cfg)
