@@ -216,10 +216,14 @@ __device__ __forceinline__ void ffn_pass(const FfnArgs& a, int expert, const int
   // The activations after the weights' first stages: both round trips
   // overlap, and the slices are quantised while the weights are in flight
   // (the scheduling barrier keeps the compiler from sinking the weight
-  // loads below the quantisation).
+  // loads below the quantisation).  With several lane groups per wave (all
+  // needing the same slices) each slice is quantised once per wave.
   __builtin_amdgcn_sched_barrier(0);
   XSlice<FMT> xs[NT][CPL];
-  load_slices<FMT, NT, CPL, XCOH>(xs, a.act, xrow, a.K, j, lpr, nchunks);
+  if constexpr (LPR > 0 && LPR < kWave)
+    load_slices_once<FMT, NT, CPL, LPR, XCOH>(xs, a.act, xrow, a.K, j, nchunks);
+  else
+    load_slices<FMT, NT, CPL, XCOH>(xs, a.act, xrow, a.K, j, lpr, nchunks);
   for (int base = first; base < ue; base += NST * step) {
 #pragma unroll
     for (int s = 0; s < NST; ++s) {

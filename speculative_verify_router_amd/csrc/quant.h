@@ -342,6 +342,38 @@ __device__ __forceinline__ void load_slices(XSlice<FMT> (&xs)[NT][CPL], const fl
     }
 }
 
+// The same slices for a wave of 64 / LPR lane groups, which all need the
+// same LPR * CPL chunk slices (lane j of every group: chunks j + LPR ci).
+// Each of those slices is quantised once, chunk c by lane c % 64 (in its
+// own slot c / 64), and every lane then gathers its CPL slices from the
+// lanes that made them, one ds_bpermute per dword.  The slices are the
+// ones load_slices gives, bit for bit: only the lane that computes them
+// differs.
+template <int FMT, int NT, int CPL, int LPR, bool XCOH = false>
+__device__ __forceinline__ void load_slices_once(XSlice<FMT> (&xs)[NT][CPL], const float* act,
+                                                 const int (&xrow)[NT], int K, int j,
+                                                 int nchunks) {
+  static_assert(LPR > 0 && LPR < kWave && kWave % LPR == 0, "lane groups of a wave");
+  constexpr int NQ = (LPR * CPL + kWave - 1) / kWave;  // slices each lane makes
+  constexpr int ND = (int)(sizeof(XSlice<FMT>) / 4);
+  const int lane = threadIdx.x & (kWave - 1);
+  XSlice<FMT> own[NT][NQ];
+  load_slices<FMT, NT, NQ, XCOH>(own, act, xrow, K, lane, kWave, nchunks);
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int ci = 0; ci < CPL; ++ci) {
+      // Chunk j + LPR ci: LPR ci % 64 is a multiple of LPR and j < LPR, so
+      // its slot (LPR ci) / 64 is the same for every lane.
+      const int src = ((j + LPR * ci) & (kWave - 1)) * 4;
+      uint32_t d[ND];
+      __builtin_memcpy(d, &own[t][(LPR * ci) / kWave], sizeof(d));
+#pragma unroll
+      for (int i = 0; i < ND; ++i) d[i] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)d[i]);
+      __builtin_memcpy(&xs[t][ci], d, sizeof(d));
+    }
+}
+
 // acc += a * dot - b * xs.sum for one chunk: the chunk's contribution,
 // with dot = sum_i q_i x16_i and a carrying the activation scale.
 struct ChunkScale {
