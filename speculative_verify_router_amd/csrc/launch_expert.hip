@@ -9,12 +9,19 @@ namespace host {
 // Phase 2: routed gate/up (A) + shared down (B) in one grid.  The resident
 // round is split in proportion to the bytes each side's waves stream: the
 // shared side's waves each take one token over the same rows.
-
-
+//
+// The round is one workgroup per CU for Q4_K gate/up over 32 or more
+// (token, slot) pairs (per-pair tiles, four tokens of top-8): a second
+// wave per SIMD buys it no bandwidth, and half as many tiles of twice the
+// rows spend less on per-tile start-up and activation quantisation (about
+// 1 us per layer at four tokens).  The other formats do more arithmetic
+// per byte and need the second wave to cover it (Q2_K: 4 us slower at one
+// workgroup per CU; Q8_0 at one token: 1 us slower).
 template <int FA, int SA, int FB, int SB>
 void launch_dual_t(hipStream_t st, FfnArgs a, FfnArgs b, const DualPlan& d) {
   auto k = k_dual<FA, SA, true, FB, SB, false>;
-  const int64_t cap = resident_blocks(k);
+  const bool one_per_cu = FA == kQ4_K && a.pair_expert && d.slots >= 32;
+  const int64_t cap = one_per_cu ? device_cus() : resident_blocks(k);
   int64_t bb = (int64_t)((double)cap * d.b_work / (double)(d.a_work + d.b_work) + 0.5);
   if (bb < 1) bb = 1;
   if (bb > cap / 2) bb = cap / 2;
