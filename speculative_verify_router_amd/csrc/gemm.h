@@ -720,59 +720,102 @@ __global__ __launch_bounds__(kBlock) void k_gemm(GemmArgs a) {
 // ---------------------------------------------------------------------------
 // Router logits for a batch: l[t][e] = sum_h Wr[e][h] x[t][h] on the fp32
 // matrix cores (v_mfma_f32_16x16x4_f32, lane 16 g + n: A row n column g, B
-// column n row g, D rows 4g..4g+3 of column n).  A workgroup computes one
-// 16-token x 16-expert tile; its four waves take quarters of H and their
-// partial tiles are added in LDS in a fixed order.
-
-static __global__ __launch_bounds__(kBlock) void k_router_mfma(const float* __restrict__ wr,
+// column n row g, D rows 4g..4g+3 of column n).  A workgroup computes a
+// 32-token x 32-expert tile as four 16 x 16 sub-tiles; its four waves take
+// quarters of H, each wave all four sub-tiles, so that every operand load
+// feeds two MFMAs (loads of 16 rows x 64 bytes are what bounds this kernel:
+// the address path, not the matrix cores).  The waves' partial tiles are
+// added in LDS in a fixed order.  Each sub-tile sums exactly as a
+// workgroup of its own would.
+// NG: groups of 16 columns per wave when known at compile time (H / 64),
+// else 0; a known count lets the whole ring be unrolled.
+template <int NG>
+__global__ __launch_bounds__(kBlock) void k_router_mfma(const float* __restrict__ wr,
                                                         const float* __restrict__ x,
                                                         float* __restrict__ logits, int H, int E,
                                                         int M) {
-  __shared__ f32x4 s_part[kWavesPerBlock - 1][kWave];
-  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x >> 6;
+  __shared__ f32x4 s_part[kWavesPerBlock - 1][2][2][kWave];
+  // The wave index is uniform; saying so keeps the loop bounds scalar.
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, g = lane >> 4;
-  const int t0 = 16 * blockIdx.x, e0 = 16 * blockIdx.y;
+  const int t0 = 32 * blockIdx.x, e0 = 32 * blockIdx.y;
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)M * (uint32_t)H * 4u);
   const __amdgpu_buffer_rsrc_t wrr = make_rsrc(wr, (uint32_t)E * (uint32_t)H * 4u);
   // Rows past M or E read as zero (offsets past the resources).
-  const uint32_t xo = (t0 + n < M) ? (uint32_t)(t0 + n) * H * 4u : 0xFFFFFFF0u;
-  const uint32_t wo = (e0 + n < E) ? (uint32_t)(e0 + n) * H * 4u : 0xFFFFFFF0u;
-  const int kq = H / kWavesPerBlock;  // H % 64 == 0: whole groups of 16 columns
-  const int kb = wv * kq, ke = kb + kq;
-  // Loads run kRing groups of 16 columns ahead of the MFMAs (the last
-  // groups re-read the wave's final group; those values are never used).
-  constexpr int kRing = 4;
-  auto load = [&](int k, f32x4& av, f32x4& bv) {
-    const uint32_t ko = 4u * (uint32_t)(min(k, ke - 16) + 4 * g);
-    av = __builtin_amdgcn_raw_buffer_load_b128(xr, xo == 0xFFFFFFF0u ? xo : xo + ko, 0, 0);
-    bv = __builtin_amdgcn_raw_buffer_load_b128(wrr, wo == 0xFFFFFFF0u ? wo : wo + ko, 0, 0);
-  };
-  f32x4 av[kRing], bv[kRing];
+  uint32_t xo[2], wo[2];
 #pragma unroll
-  for (int u = 0; u < kRing; ++u) load(kb + 16 * u, av[u], bv[u]);
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int k = kb; k < ke; k += 16 * kRing) {
+  for (int h = 0; h < 2; ++h) {
+    xo[h] = (t0 + 16 * h + n < M) ? (uint32_t)(t0 + 16 * h + n) * H * 4u : 0xFFFFFFF0u;
+    wo[h] = (e0 + 16 * h + n < E) ? (uint32_t)(e0 + 16 * h + n) * H * 4u : 0xFFFFFFF0u;
+  }
+  const int kq = H / kWavesPerBlock;  // H % 64 == 0: whole groups of 16 columns
+  const int kb = wv * kq, ng = NG ? NG : kq / 16;  // this wave's first column and groups
+  // Loads run kRing groups of 16 columns ahead of the MFMAs.  The loop is
+  // branch-free over whole rounds of kRing groups, so the wait before each
+  // group counts a fixed number of later loads: groups past the wave's last
+  // read offsets beyond the buffers, i.e. zeros, and add exactly nothing.
+  constexpr int kRing = 4;
+  constexpr uint32_t kOut = 0xFFFFFFF0u;
+  auto load = [&](int gi, f32x4 (&av)[2], f32x4 (&bv)[2]) {
+    const bool live = gi < ng;
+    const uint32_t ko = 4u * (uint32_t)(kb + 16 * gi + 4 * g);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      av[h] = __builtin_amdgcn_raw_buffer_load_b128(xr, live && xo[h] != kOut ? xo[h] + ko : kOut, 0, 0);
+      bv[h] = __builtin_amdgcn_raw_buffer_load_b128(wrr, live && wo[h] != kOut ? wo[h] + ko : kOut, 0, 0);
+    }
+  };
+  // Slot u holds group u mod kRing; each step first refills the slot the
+  // previous step used, then multiplies the slot loaded kRing - 1 steps ago.
+  f32x4 av[kRing][2], bv[kRing][2];
+#pragma unroll
+  for (int u = 0; u < kRing - 1; ++u) load(u, av[u], bv[u]);
+  f32x4 acc[2][2];  // [token half][expert half]
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) acc[i][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int r = 0; r < ng; r += kRing) {
 #pragma unroll
     for (int u = 0; u < kRing; ++u) {
-      if (k + 16 * u < ke) {
+      constexpr int kLead = kRing - 1;
+      load(r + u + kLead, av[(u + kLead) % kRing], bv[(u + kLead) % kRing]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u][j], bv[u][j], acc, 0, 0, 0);
-      }
-      load(k + 16 * (u + kRing), av[u], bv[u]);
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            acc[i][h] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u][i][j], bv[u][h][j], acc[i][h], 0, 0, 0);
+      // Keep each step's loads ahead of its products: scheduled together,
+      // the loads of a whole round sink to its end and every round waits
+      // for all of them.
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
-  if (wv > 0) s_part[wv - 1][lane] = acc;
+  if (wv > 0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) s_part[wv - 1][i][h][lane] = acc[i][h];
+  }
   __syncthreads();
   if (wv > 0) return;
 #pragma unroll
-  for (int w = 0; w < kWavesPerBlock - 1; ++w) acc += s_part[w][lane];
-  const int e = e0 + n;
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int t = t0 + 4 * g + j;
-    if (t < M && e < E) logits[(int64_t)t * E + e] = acc[j];
-  }
+    for (int h = 0; h < 2; ++h) {
+      f32x4 a = acc[i][h];
+#pragma unroll
+      for (int w = 0; w < kWavesPerBlock - 1; ++w) a += s_part[w][i][h][lane];
+      const int e = e0 + 16 * h + n;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = t0 + 16 * i + 4 * g + j;
+        if (t < M && e < E) logits[(int64_t)t * E + e] = a[j];
+      }
+    }
 }
 
 }  // namespace svr

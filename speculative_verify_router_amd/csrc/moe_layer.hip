@@ -208,8 +208,11 @@ Buffers carve(const Plan& p, void* ws, int32_t* ids, float* w) {
 void enqueue_logits(const Plan& p, const float* router, const float* x, float* logits,
                     hipStream_t st) {
   if (p.M > kFusedMaxTokens && p.H % 64 == 0) {
-    hipLaunchKernelGGL(k_router_mfma, dim3((p.M + 15) / 16, (p.E + 15) / 16), dim3(kBlock), 0, st,
-                       router, x, logits, p.H, p.E, p.M);
+    const dim3 grid((p.M + 31) / 32, (p.E + 31) / 32);
+    if (p.H == 4096)
+      hipLaunchKernelGGL(k_router_mfma<64>, grid, dim3(kBlock), 0, st, router, x, logits, p.H, p.E, p.M);
+    else
+      hipLaunchKernelGGL(k_router_mfma<0>, grid, dim3(kBlock), 0, st, router, x, logits, p.H, p.E, p.M);
     return;
   }
   hipLaunchKernelGGL(k_router_logits, dim3((p.E + kWavesPerBlock - 1) / kWavesPerBlock),
