@@ -277,9 +277,9 @@ constexpr int slab_loads() {
 template <int FMT>
 constexpr bool split_steps() { return FMT == kQ3_K || FMT == kQ6_K; }
 
-template <int FMT, int NM, int RTR>
+template <int FMT, int NM, int RTR, int TT = 1>
 struct Slab {
-  uint4 act[4];                             // this thread's part of the activation slab
+  uint4 act[TT][4];                         // this thread's part of each tile's activation slab
   uint4 q[NM][RTR][slab_loads<FMT>()];      // weight lines
 };
 
@@ -306,9 +306,17 @@ struct GemmLds {
 // waves of RTR row tiles of 16 rows (wave w: rows r0 + 16 RTR w ..), of NM
 // matrices (2: gate and up).  Outputs: gate/up -> h = silu(gate) * up,
 // split; down -> fp32.
-template <int FMT, bool GATEUP, int RTR>
+//
+// TT = 2 (Q8_0 only): two token tiles (pos0/cnt and pos1/cnt1; cnt1 may be
+// 0) share every weight operand, each tile's products going to its own
+// accumulators.  The two tiles' activation slabs take the two LDS
+// activation buffers, single-buffered: a barrier before each slab's stores
+// keeps them from overwriting what slower waves still read.
+template <int FMT, bool GATEUP, int RTR, int TT = 1>
 __device__ __forceinline__ void gemm_block(const GemmArgs& a, int e, int pos0, int cnt, int rb0,
-                                           GemmLds<FMT, GATEUP, RTR>& L) {
+                                           GemmLds<FMT, GATEUP, RTR>& L, int pos1 = 0,
+                                           int cnt1 = 0) {
+  static_assert(TT == 1 || (TT == 2 && FMT == kQ8_0), "two token tiles: Q8_0 only");
   constexpr int NM = GATEUP ? 2 : 1;
   constexpr int NQ = slab_loads<FMT>();
   // quant bytes per row and slab
@@ -325,15 +333,20 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, int e, int pos0, i
   // lanes of a wave write 1 KB of consecutive LDS.  Its source is unit
   // 8 step + 2 group + hi/lo of row n's 1 KB slab chunk.
   const int an = tid & 15, au = tid >> 4;
-  const int apos = pos0 + (an < cnt ? an : 0);  // rows past the tile repeat its first row
-  const int arow = a.act_gather ? a.slots[apos] / a.top_k : apos;
   const __amdgpu_buffer_rsrc_t ar = make_rsrc(a.act, (uint32_t)(a.act_rows * a.K * 4));
-  uint32_t aoff[4];
+  uint32_t aoff[TT][4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int u = au + 16 * j;  // (step u / 8, hi/lo (u / 4) % 2, group u % 4)
-    aoff[j] = (uint32_t)arow * (uint32_t)a.K * 4u +
-              16u * (uint32_t)(8 * (u >> 3) + 2 * (u & 3) + ((u >> 2) & 1));
+  for (int t = 0; t < TT; ++t) {
+    // rows past a tile repeat its first row (a missing second tile: the first's)
+    const int tp = (t == 1 && cnt1 > 0) ? pos1 : pos0, tc = (t == 1 && cnt1 > 0) ? cnt1 : cnt;
+    const int apos = tp + (an < tc ? an : 0);
+    const int arow = a.act_gather ? a.slots[apos] / a.top_k : apos;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int u = au + 16 * j;  // (step u / 8, hi/lo (u / 4) % 2, group u % 4)
+      aoff[t][j] = (uint32_t)arow * (uint32_t)a.K * 4u +
+                   16u * (uint32_t)(8 * (u >> 3) + 2 * (u & 3) + ((u >> 2) & 1));
+    }
   }
 
   QPlanes P[NM];
@@ -389,9 +402,11 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, int e, int pos0, i
           }
         }
   };
-  auto load_slab = [&](Slab<FMT, NM, RTR>& sl, int k) {
+  auto load_slab = [&](Slab<FMT, NM, RTR, TT>& sl, int k) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) sl.act[j] = bload16(ar, aoff[j] + 1024u * (uint32_t)k);
+    for (int t = 0; t < TT; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sl.act[t][j] = bload16(ar, aoff[t][j] + 1024u * (uint32_t)k);
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
@@ -411,11 +426,11 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, int e, int pos0, i
       }
   };
 
-  f32x4 acc[NM][RTR];
+  f32x4 acc[NM][RTR], acc1[NM][RTR];  // acc1: the second token tile (TT = 2)
 #pragma unroll
   for (int m = 0; m < NM; ++m)
 #pragma unroll
-    for (int rt = 0; rt < RTR; ++rt) acc[m][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int rt = 0; rt < RTR; ++rt) acc[m][rt] = acc1[m][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const uint32_t one = opaque_vgpr(0x3F803F80u);
   const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
   // Q2_K: all-ones B operands over the first / second 16 columns of a step
@@ -432,10 +447,18 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, int e, int pos0, i
 
   // Slab k: stage it in LDS, issue the loads of slab k + 1 into the
   // registers it leaves free, compute its eight steps.
-  auto consume = [&](Slab<FMT, NM, RTR>& sl, int k) {
-    uint4* const al = L.act[k & 1];
+  auto consume = [&](Slab<FMT, NM, RTR, TT>& sl, int k) {
+    uint4* const al = L.act[TT == 1 ? (k & 1) : 0];
+    if constexpr (TT == 2) {
+      if (k > 0) __syncthreads();  // every wave is done with the previous slab
 #pragma unroll
-    for (int j = 0; j < 4; ++j) al[tid + 256 * j] = sl.act[j];
+      for (int t = 0; t < TT; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) L.act[t][tid + 256 * j] = sl.act[t][j];
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) al[tid + 256 * j] = sl.act[0][j];
+    }
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
@@ -550,6 +573,69 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, int e, int pos0, i
             acc[m][rt][j] = v;
           }
     };
+    if constexpr (TT == 2) {
+      // Q8_0, two token tiles: acc += d P per step, the scale FMAs one step
+      // behind the products.
+      f32x4 q[TT][NM][RTR], qp[TT][NM][RTR];
+      auto apply2 = [&](const f32x4 (&pv)[TT][NM][RTR], const float2 (&acv)[NM][RTR]) {
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+          for (int rt = 0; rt < RTR; ++rt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              acc[m][rt][j] = fmaf(acv[m][rt].x, pv[0][m][rt][j], acc[m][rt][j]);
+              acc1[m][rt][j] = fmaf(acv[m][rt].x, pv[1][m][rt][j], acc1[m][rt][j]);
+            }
+      };
+#pragma unroll
+      for (int i = 0; i < kSlab; ++i) {
+        u32x4 ahi[TT], alo[TT];
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+          const uint4 h4 = L.act[t][((i * 2 + 0) * 4 + g) * 16 + n];
+          const uint4 l4 = L.act[t][((i * 2 + 1) * 4 + g) * 16 + n];
+          ahi[t] = u32x4{h4.x, h4.y, h4.z, h4.w};
+          alo[t] = u32x4{l4.x, l4.y, l4.z, l4.w};
+        }
+        u32x4 b[NM][RTR];
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+          for (int rt = 0; rt < RTR; ++rt) {
+            const int base = (m * RTR + rt) * NQ;
+            const int u = 2 * i + (g >> 1);
+            const uint2 w = reinterpret_cast<const uint2*>(wl)[((base + (i >> 1)) * 64 + (u & 3) * 16 + n) * 2 + (g & 1)];
+            b[m][rt] = q8_operand(w.x, w.y);
+          }
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+#pragma unroll
+          for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int rt = 0; rt < RTR; ++rt) q[t][m][rt] = mfma_bf16(ahi[t], b[m][rt], zero);
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+#pragma unroll
+          for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int rt = 0; rt < RTR; ++rt) q[t][m][rt] = mfma_bf16(alo[t], b[m][rt], q[t][m][rt]);
+        if (i > 0) apply2(qp, acp);
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+#pragma unroll
+          for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int rt = 0; rt < RTR; ++rt) qp[t][m][rt] = q[t][m][rt];
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+          for (int rt = 0; rt < RTR; ++rt)
+            acp[m][rt] = scl[(((m * RTR + rt) * 4 + (i >> 1)) * 16 + n) * 2 + (i & 1)];
+      }
+      apply2(qp, acp);
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < kSlab; ++i) {
       const uint4 h4 = al[((i * 2 + 0) * 4 + g) * 16 + n];
@@ -653,56 +739,65 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, int e, int pos0, i
     }
     apply(pp, pp1, Xp, Xp1, acp);
   };
-  Slab<FMT, NM, RTR> sl;
+  Slab<FMT, NM, RTR, TT> sl;
   load_group(0);
   load_slab(sl, 0);
   for (int k = 0; k < NS; ++k) consume(sl, k);
 
   // Epilogue: lane holds rows r0 + 16 rt + n for tokens 4g + j.
+  auto store_tile = [&](const f32x4 (&av)[NM][RTR], int tpos0, int tcnt) {
 #pragma unroll
-  for (int rt = 0; rt < RTR; ++rt) {
-    const int r = r0 + 16 * rt + n;
-    if (r >= a.rows) continue;
+    for (int rt = 0; rt < RTR; ++rt) {
+      const int r = r0 + 16 * rt + n;
+      if (r >= a.rows) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int t = 4 * g + j;
-      if (t >= cnt) continue;
-      const int pos = pos0 + t;
-      const int orow = a.out_scatter ? a.slots[pos] : pos;
-      if (GATEUP) {
-        const float h = silu(acc[0][rt][j]) * acc[NM - 1][rt][j];
-        uint32_t hi, lo;
-        split_bf16(h, hi, lo);
-        // Element r of the row: group r / 8, operand position of r % 8.
-        const int q = r & 7;
-        const int p = (q < 4) ? 2 * q : 2 * (q - 4) + 1;
-        uint16_t* row = reinterpret_cast<uint16_t*>(a.out) + (int64_t)orow * a.rows * 2;
-        row[(r >> 3) * 16 + p] = (uint16_t)hi;
-        row[(r >> 3) * 16 + 8 + p] = (uint16_t)lo;
-      } else {
-        reinterpret_cast<float*>(a.out)[(int64_t)orow * a.rows + r] = acc[0][rt][j];
+      for (int j = 0; j < 4; ++j) {
+        const int t = 4 * g + j;
+        if (t >= tcnt) continue;
+        const int pos = tpos0 + t;
+        const int orow = a.out_scatter ? a.slots[pos] : pos;
+        if (GATEUP) {
+          const float h = silu(av[0][rt][j]) * av[NM - 1][rt][j];
+          uint32_t hi, lo;
+          split_bf16(h, hi, lo);
+          // Element r of the row: group r / 8, operand position of r % 8.
+          const int q = r & 7;
+          const int p = (q < 4) ? 2 * q : 2 * (q - 4) + 1;
+          uint16_t* row = reinterpret_cast<uint16_t*>(a.out) + (int64_t)orow * a.rows * 2;
+          row[(r >> 3) * 16 + p] = (uint16_t)hi;
+          row[(r >> 3) * 16 + 8 + p] = (uint16_t)lo;
+        } else {
+          reinterpret_cast<float*>(a.out)[(int64_t)orow * a.rows + r] = av[0][rt][j];
+        }
       }
     }
-  }
+  };
+  store_tile(acc, pos0, cnt);
+  if (TT == 2 && cnt1 > 0) store_tile(acc1, pos1, cnt1);
 }
 
-// Grid: row_blocks x (token-tile capacity rounded up to 8).  Blocks go to
-// the eight XCDs round-robin; XCD x takes the x-th eighth of the live tile
-// list, in order: block b takes its ((b / 8) / row_blocks)-th tile and row
+// Grid: row_blocks x (capacity of work units rounded up to 8); a unit is
+// one token tile, or TT consecutive tiles of the dense list.  Blocks go to
+// the eight XCDs round-robin; XCD x takes the x-th eighth of the live unit
+// list, in order: block b takes its ((b / 8) / row_blocks)-th unit and row
 // block (b / 8) % row_blocks.  So the row blocks of one token tile share an
 // XCD (and its L2 copy of the tile's activations), and the tiles of an
 // expert with more than 16 tokens run back to back on one XCD and find its
 // weight rows in that L2.  Every wave of a workgroup passes the same
 // slab barriers; waves whose rows lie past the expert compute zeros.
-template <int FMT, bool GATEUP, int RTR>
+// TT = 2 (dense Q8_0, the shared expert): each workgroup takes two token
+// tiles, so every weight operand it builds serves 32 tokens.
+template <int FMT, bool GATEUP, int RTR, int TT = 1>
 __global__ __launch_bounds__(kBlock) void k_gemm(GemmArgs a) {
   __shared__ GemmLds<FMT, GATEUP, RTR> lds;
   const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
   const int n_tiles = a.tiles ? *a.n_tiles : (a.dense_tokens + 15) / 16;
-  const int per_xcd = (n_tiles + 7) / 8;
+  const int n_units = (n_tiles + TT - 1) / TT;
+  const int per_xcd = (n_units + 7) / 8;
   const int slot = j / a.row_blocks, rb = j % a.row_blocks;
-  const int tile = xcd * per_xcd + slot;
-  if (slot >= per_xcd || tile >= n_tiles) return;
+  const int unit = xcd * per_xcd + slot;
+  if (slot >= per_xcd || unit >= n_units) return;
+  const int tile = TT * unit;
   int e, pos0, cnt;
   if (a.tiles) {
     e = a.tiles[3 * tile];
@@ -714,7 +809,14 @@ __global__ __launch_bounds__(kBlock) void k_gemm(GemmArgs a) {
     cnt = min(16, a.dense_tokens - pos0);
     if (cnt <= 0) return;
   }
-  gemm_block<FMT, GATEUP, RTR>(a, e, pos0, cnt, rb * kWavesPerBlock * 16 * RTR, lds);
+  if constexpr (TT == 2) {
+    // the dense list only (the host launches TT = 2 for no other)
+    const int pos1 = pos0 + 16, cnt1 = max(0, min(16, a.dense_tokens - pos1));
+    gemm_block<FMT, GATEUP, RTR, 2>(a, e, pos0, cnt, rb * kWavesPerBlock * 16 * RTR, lds, pos1,
+                                    cnt1);
+  } else {
+    gemm_block<FMT, GATEUP, RTR>(a, e, pos0, cnt, rb * kWavesPerBlock * 16 * RTR, lds);
+  }
 }
 
 // ---------------------------------------------------------------------------

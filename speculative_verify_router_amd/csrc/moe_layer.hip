@@ -328,13 +328,13 @@ bool gemm_path(const Plan& p) {
   return true;
 }
 
-template <int FMT, bool GU, int RTR>
+template <int FMT, bool GU, int RTR, int TT = 1>
 void launch_gemm_t(GemmArgs a, int tiles_cap, hipStream_t st) {
   const int per = kWavesPerBlock * 16 * RTR;
   a.row_blocks = (a.rows + per - 1) / per;
-  const int t8 = (tiles_cap + 7) & ~7;
-  hipLaunchKernelGGL((k_gemm<FMT, GU, RTR>), dim3((unsigned)(t8 * a.row_blocks)), dim3(kBlock), 0,
-                     st, a);
+  const int t8 = ((tiles_cap + TT - 1) / TT + 7) & ~7;  // work units, rounded up to 8
+  hipLaunchKernelGGL((k_gemm<FMT, GU, RTR, TT>), dim3((unsigned)(t8 * a.row_blocks)),
+                     dim3(kBlock), 0, st, a);
 }
 
 void launch_gemm(int dtype, bool gateup, const GemmArgs& a, int tiles_cap, hipStream_t st) {
@@ -351,6 +351,11 @@ void launch_gemm(int dtype, bool gateup, const GemmArgs& a, int tiles_cap, hipSt
   } else if (dtype == MOE_Q4_K) {
     if (gateup) launch_gemm_t<kQ4_K, true, kGemmGateUpRtr>(a, tiles_cap, st);
     else launch_gemm_t<kQ4_K, false, kGemmDownRtr>(a, tiles_cap, st);
+  } else if (!a.tiles) {
+    // The dense token list (the shared expert): two token tiles per
+    // workgroup share each weight operand it builds.
+    if (gateup) launch_gemm_t<kQ8_0, true, kGemmQ8Rtr, 2>(a, tiles_cap, st);
+    else launch_gemm_t<kQ8_0, false, kGemmQ8Rtr, 2>(a, tiles_cap, st);
   } else {
     // Q8_0 weight slabs are twice as long: fewer row tiles per wave keep
     // two workgroups per CU.
