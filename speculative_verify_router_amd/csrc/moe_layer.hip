@@ -312,6 +312,7 @@ FfnArgs routed_args(const Plan& p, const Buffers& b, bool gateup, const moe_laye
 constexpr int kGemmGateUpRtr = 2;  // row tiles of 16 per wave and matrix
 constexpr int kGemmDownRtr = 4;
 constexpr int kGemmQ8Rtr = 1;
+constexpr int kGemmQ8DenseDownRtr = 2;  // the shared down: one round of two per CU
 // Stages of the batched path; the shared expert's GEMMs are stages of their
 // own (empty without one), so that "gateup" is the routed gate/up GEMM alone.
 constexpr int kGemmStages = 5;
@@ -353,9 +354,11 @@ void launch_gemm(int dtype, bool gateup, const GemmArgs& a, int tiles_cap, hipSt
     else launch_gemm_t<kQ4_K, false, kGemmDownRtr>(a, tiles_cap, st);
   } else if (!a.tiles) {
     // The dense token list (the shared expert): two token tiles per
-    // workgroup share each weight operand it builds.
+    // workgroup share each weight operand it builds.  The down GEMM's waves
+    // take two row tiles: at 512 tokens and H = 4096 its grid is then one
+    // resident round (38 us against 52 us with one row tile: 1.33 rounds).
     if (gateup) launch_gemm_t<kQ8_0, true, kGemmQ8Rtr, 2>(a, tiles_cap, st);
-    else launch_gemm_t<kQ8_0, false, kGemmQ8Rtr, 2>(a, tiles_cap, st);
+    else launch_gemm_t<kQ8_0, false, kGemmQ8DenseDownRtr, 2>(a, tiles_cap, st);
   } else {
     // Q8_0 weight slabs are twice as long: fewer row tiles per wave keep
     // two workgroups per CU.
